@@ -1,0 +1,285 @@
+/*
+ * mx.h -- C ABI of libmx, OCP-microscaling (MX) quantize-and-GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  BF16 tensors are packed into MX operands -- E2M1
+ * (MXFP4), E2M3 (MXFP6) or E4M3 (MXFP8) element codes with one E8M0
+ * exponent per block of 32 elements -- and packed operands are multiplied
+ * with the gfx950 block-scaled matrix cores.  Sources (pages, by title):
+ *   [P1] "feat(mxfp6): MXFP6 (E2M3) Flux linears, a fused MLP, and the MLPerf
+ *        recipe" (Primus pull request 1064)
+ *   [P3] "MXFP4 training for Flux models" (ROCm Primus technical guide)
+ *   [P4] "MXFP8 cudnn-fe Swiglu fused Grouped MLP fwd/bwd and wgrad group
+ *        gemm" (ao pull request 5)
+ * Element and scale encodings follow the OCP Microscaling Formats (MX) v1.0
+ * specification, which the pages name but do not spell out.
+ *
+ * Conventions for every entry point.
+ *  - Pointers named as tensors are DEVICE pointers, owned by the caller, who
+ *    also allocates every output and work buffer.  The library allocates no
+ *    memory and keeps no state beyond a per-device property cache.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously on it; the call returns once enqueued.
+ *  - bf16 tensors are row-major and dense.  Every device pointer must be
+ *    16-byte aligned.
+ *  - Packed operands are K-major ("rows x K"): codes [rows][K*bits/8] bytes
+ *    with bits = 4, 6 or 8, and scales [rows][K/32] E8M0 bytes.  Code layout
+ *    within a row: E2M1 element 2j in the low nibble of byte j and 2j+1 in
+ *    the high nibble; E2M3 a little-endian 6-bit stream, element j at bits
+ *    [6j, 6j+6); E4M3 one byte per element.  Every GEMM computes
+ *    C = A . B^T on two K-major operands (the NT layout of [P3],
+ *    Troubleshooting).
+ *  - Return value: MX_OK, or an mx_status error.  Arguments are validated on
+ *    the host before anything is enqueued; on error nothing is enqueued and
+ *    no output is touched.  There is no fallback path: a call the kernels
+ *    cannot serve fails with an error.
+ *  - Deterministic: no atomics; repeated calls give bitwise-identical results.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,           /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,          /* a size is negative, zero where it may not be, or not the multiple required */
+  MX_ERR_ALIGN = 3,          /* a device pointer is not 16-byte aligned */
+  MX_ERR_FORMAT = 4,         /* unknown format / scale mode / prologue / epilogue / mode, or a combination not served */
+  MX_ERR_OFFSETS = 5,        /* group offsets break their contract (checked only when asked to) */
+  MX_ERR_INDEX_OVERFLOW = 6, /* a tensor exceeds 2^31 bytes (the kernels use 32-bit offsets) */
+  MX_ERR_DEVICE = 7,         /* no current device, or the current device is not gfx950 */
+  MX_ERR_LAUNCH = 8          /* the HIP runtime reported an error when enqueuing */
+} mx_status;
+
+/* ---------------------------------------------------------------- enums */
+typedef enum { MX_E2M1 = 1, MX_E2M3 = 2, MX_E4M3 = 3 } mx_fmt;
+
+/* E8M0 exponent selection per block of 32 (amax = largest |value|):
+ *  FLOOR: X = floor(log2 amax) - 2 (emax of E2M1/E2M3), for MXFP4/MXFP6;
+ *  RCEIL: X = smallest integer with 448 * 2^X >= amax, for MXFP8 ([P4]:
+ *         the E8M0 conversion rounds upward).
+ * X is clamped to [-127, 127]; amax == 0 gives X = -127; a block holding a
+ * NaN or Inf gets the NaN scale 0xFF and all-zero codes. */
+typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_RCEIL = 1 } mx_scale_mode;
+
+/* Elementwise prologue applied before packing ([P1] description: the packer
+ * takes the activation epilogue as its prologue).  Each result is rounded to
+ * bf16 before rotation / amax.  With logical output v [R][C]:
+ *  IDENTITY: v = x                           x [R][C]
+ *  GELU:     v = gelu_tanh(x)                x = h [R][C]
+ *  DGELU:    v = da * gelu_tanh'(h)          x = da [R][C], aux = h [R][C]
+ *  SWIGLU:   v = silu(g) * u                 x = H [R][2C] = [gate | up]
+ *  DSWIGLU:  C = 2F, x = dz [R][F], aux = H [R][2F]:
+ *            v[:, :F] = dz * u * s * (1 + g*(1-s)),  v[:, F:] = dz * g * s,
+ *            s = 1/(1+exp(-g)) ([P4]: sigmoid formed as 1/(1+exp(-x))).
+ * exp and the tanh form are this library's own binary32 contract (Cody-Waite
+ * reduction + degree-7 polynomial), so results are reproducible to the bit. */
+typedef enum {
+  MX_PRO_IDENTITY = 0,
+  MX_PRO_GELU_TANH = 1,
+  MX_PRO_DGELU_TANH = 2,
+  MX_PRO_SWIGLU = 3,
+  MX_PRO_DSWIGLU = 4
+} mx_prologue;
+
+typedef enum { MX_BF16 = 0, MX_F32 = 1 } mx_dtype;
+
+typedef enum { MX_GROUPED_RAGGED_M = 0, MX_GROUPED_RAGGED_K = 1 } mx_grouped_mode;
+
+typedef enum { MX_EPI_NONE = 0, MX_EPI_SWIGLU = 1, MX_EPI_DSWIGLU = 2 } mx_epilogue;
+
+/* One packed operand: codes [rows][K*bits/8] bytes + scales [rows][K/32]. */
+typedef struct {
+  void* codes;
+  void* scales;
+} mx_packed;
+
+/* ---------------------------------------------------------------- quantize */
+/*
+ * mx_quantize -- pack a bf16 tensor into MX operands ([P1] Summary and
+ * commit messages: scale, optional Hadamard rotation, cast and bit-pack in
+ * one pass; [P4] first commit message: rowwise 1x32 and columnwise 32x1).
+ *
+ *  x, aux       bf16 inputs of the prologue (see mx_prologue); aux NULL
+ *               unless DGELU or DSWIGLU.  Shapes per batch entry.
+ *  batch        number of independent [R][C] problems stored back to back
+ *               (e.g. the G experts' weights); every pointer below advances by
+ *               one problem's size per batch entry.  >= 1.
+ *  R, C         logical size of the quantized tensor v; multiples of 32,
+ *               R = 0 or C = 0 enqueues nothing and returns MX_OK.
+ *  fmt          MX_E2M1, MX_E2M3 or MX_E4M3.
+ *  scale_mode   MX_SCALE_FLOOR or MX_SCALE_RCEIL.
+ *  hadamard     1: rotate every 32-block by the normalised 32-point
+ *               Walsh-Hadamard matrix (Sylvester order) before amax ([P1]
+ *               description: the rotation is folded into the packer).
+ *               Rotation order: radix-2 butterfly, strides 1,2,4,8,16, every
+ *               add rounded to binary32, one multiply by fl32(1/sqrt 32).
+ *               Only with MX_E2M3.
+ *  row_codes, row_scales   rowwise (1x32 along dim 1) operand, [R] x K=C.
+ *  col_codes, col_scales   columnwise (32x1 along dim 0) operand written
+ *                          transposed, i.e. K-major [C] x K=R.
+ *               Either pair may be NULL (both members of a pair alike), not
+ *               both.
+ *  colsum_partials  fp32 [R/32][C]: per-32-row-block column sums of v before
+ *               rotation, rows in increasing order from +0 ([P1] commit
+ *               messages: the bias gradient is finished from the packer's
+ *               per-column partials).  NULL for none.
+ *  colsum       fp32 [C]: sum of the partials in increasing block order
+ *               (one extra small launch).  Requires colsum_partials.  NULL
+ *               for none.
+ * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
+ * MX_ERR_INDEX_OVERFLOW, MX_ERR_DEVICE, MX_ERR_LAUNCH.
+ */
+int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt,
+                int scale_mode, int hadamard, int prologue, void* row_codes, void* row_scales,
+                void* col_codes, void* col_scales, float* colsum_partials, float* colsum,
+                void* stream);
+
+/* ---------------------------------------------------------------- GEMM */
+/*
+ * mx_gemm -- C[m][n] = sum_k A[m][k] * B[n][k] (+ bias[n]) on packed
+ * operands of one format, accumulated in binary32 by the scaled matrix
+ * cores.  The forward uses A = rows of X, B = rows of W; dgrad A = rows of
+ * dY, B = columns of W; wgrad A = columns of dY, B = columns of X, so K is
+ * the token count ([P1] description: M, N and K must be multiples of 256
+ * because the backward GEMMs use K as an output dimension).
+ *
+ *  a_codes, a_scales   A, [M] x K.      b_codes, b_scales   B, [N] x K.
+ *  M, N, K      multiples of 256; M = 0 or N = 0 enqueues nothing.
+ *  fmt          element format of both operands.
+ *  bias         optional [N] vector (NULL for none), dtype bias_dtype, added
+ *               to the binary32 accumulator before the single rounding of
+ *               the store ([P1] commit messages: the bias joins the GEMM's
+ *               store epilogue and the result is rounded once).
+ *  c            output [M][ldc] of dtype c_dtype (MX_BF16 rounds to nearest
+ *               even; MX_F32 stores the accumulator).  ldc >= N, a multiple
+ *               of 8.
+ * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
+ * MX_ERR_INDEX_OVERFLOW, MX_ERR_DEVICE, MX_ERR_LAUNCH.
+ */
+int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+            int64_t M, int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c,
+            int c_dtype, int64_t ldc, void* stream);
+
+/* ---------------------------------------------------------------- fused MLP */
+/*
+ * Fused MX MLP, Y = fc2(GELU_tanh(fc1(X) + b1)) ([P1] description and
+ * Summary: one function owns fc1 -> epilogue -> fc2, the packer takes the
+ * epilogue as a prologue in both directions, the activation is packed
+ * straight from on-chip memory and the pre-activation gradient is never
+ * assembled; the fc1 bias gradient comes back as a per-column sum).
+ * All packs use fmt / scale_mode / hadamard (MXFP6: MX_E2M3, FLOOR, 1).
+ * M, D, F multiples of 256.  Packed buffers: rows x K as named.
+ */
+typedef struct {
+  int64_t M, D, F;        /* tokens; fc1 in = fc2 out width; fc1 out = fc2 in width */
+  int32_t fmt, scale_mode, hadamard, reserved;
+  const void* X;          /* bf16 [M][D] */
+  const void* W1;         /* bf16 [F][D] */
+  const void* b1;         /* bf16 [F] or NULL */
+  const void* W2;         /* bf16 [D][F] */
+  void* h;                /* out bf16 [M][F]: fc1 + b1, kept for the backward */
+  void* Y;                /* out bf16 [M][D] */
+  mx_packed Xr;           /* work: X rows [M] x K=D */
+  mx_packed Xc;           /* out (kept): X columns [D] x K=M, for the fc1 weight gradient */
+  mx_packed W1r;          /* work: W1 rows [F] x K=D */
+  mx_packed W1c;          /* out (kept): W1 columns [D] x K=F, for the fc1 data gradient */
+  mx_packed W2r;          /* work: W2 rows [D] x K=F */
+  mx_packed W2c;          /* out (kept): W2 columns [F] x K=D, for the fc2 data gradient */
+  mx_packed ar;           /* work: a = GELU(h) rows [M] x K=F (a itself is never stored) */
+  mx_packed ac;           /* out (kept): a columns [F] x K=M, for the fc2 weight gradient */
+} mx_mlp_fwd_args;
+
+typedef struct {
+  int64_t M, D, F;
+  int32_t fmt, scale_mode, hadamard, reserved;
+  const void* dY;         /* bf16 [M][D] */
+  const void* h;          /* bf16 [M][F] from the forward */
+  mx_packed Xc, W1c, W2c, ac; /* from the forward */
+  void* da;               /* out bf16 [M][F]: fc2 data gradient (materialised) */
+  void* dX;               /* out bf16 [M][D] */
+  void* dW1;              /* out bf16 [F][D] */
+  void* dW2;              /* out bf16 [D][F] */
+  float* db1;             /* out fp32 [F], or NULL to skip the bias gradient */
+  float* db1_partials;    /* work fp32 [M/32][F]; required when db1 is set */
+  mx_packed dYr;          /* work: dY rows [M] x K=D */
+  mx_packed dYc;          /* work: dY columns [D] x K=M */
+  mx_packed dhr;          /* work: dh = dGELU(da, h) rows [M] x K=F (dh itself is never stored) */
+  mx_packed dhc;          /* work: dh columns [F] x K=M */
+} mx_mlp_bwd_args;
+
+int mx_fused_mlp_fwd(const mx_mlp_fwd_args* args, void* stream);
+int mx_fused_mlp_bwd(const mx_mlp_bwd_args* args, void* stream);
+
+/* ---------------------------------------------------------------- grouped */
+/*
+ * mx_grouped_gemm -- ragged grouped GEMM over G experts ([P4] commit
+ * messages).  offsets: device int32 [G], cumulative group ends: group g owns
+ * ragged indices [offsets[g-1], offsets[g]) (offsets[-1] := 0).  Contract
+ * (caller invariant): non-decreasing, multiples of 128 ([P4] first commit
+ * message: per-expert row counts are multiples of 128, so no tile straddles
+ * two experts), offsets[G-1] <= R.  Indices at or past offsets[G-1] are
+ * neither read nor written.  validate_offsets = 1 copies offsets to the
+ * host, synchronizing `stream`, and checks them (MX_ERR_OFFSETS).
+ *
+ * MX_GROUPED_RAGGED_M (forward and data gradients):
+ *   A [R] x K, B [G][N] x K (expert g's rows at B + g*N rows),
+ *   C[r][n] = sum_k A[r][k] * B_g(r)[n][k], bf16 [R][N].  N, K multiples of
+ *   256 (SWIGLU: N/2 a multiple of 128; DSWIGLU: N a multiple of 128).
+ *   epilogue MX_EPI_NONE:    C stored.
+ *   epilogue MX_EPI_SWIGLU:  N = 2F; C = H [R][2F] = [gate | up] stored
+ *     (the pre-activation kept for the backward); z = SwiGLU(H) is
+ *     quantized in the epilogue (fmt, scale_mode) into out_row = z rows [R]
+ *     x K=F and out_col = z columns [F] x K=R.  z itself is never stored.
+ *   epilogue MX_EPI_DSWIGLU: N = F; the GEMM result is dz; with H [R][2F]
+ *     (aux), dH = dSwiGLU(dz, H) is quantized into out_row = dH rows [R] x
+ *     K=2F and out_col = dH columns [2F] x K=R.  C (bf16 dz [R][F]) may be
+ *     NULL; dz and dH are otherwise never stored.
+ * MX_GROUPED_RAGGED_K (weight gradients):
+ *   A [M] x K=R, B [N] x K=R, C bf16 [G][M][N]:
+ *   C_g = sum over k in group g of A[:, k] B[:, k]^T; an empty group's C_g
+ *   is written as zeros.  M, N multiples of 256.
+ * Errors: as mx_gemm, plus MX_ERR_OFFSETS; G <= 0 is MX_ERR_SHAPE; R == 0
+ * enqueues nothing except, in RAGGED_K mode, the zero fill of C.
+ */
+typedef struct {
+  int32_t mode;            /* mx_grouped_mode */
+  int32_t epilogue;        /* mx_epilogue (RAGGED_M only) */
+  int32_t fmt;             /* element format of A, B and the epilogue's outputs */
+  int32_t scale_mode;      /* scale selection of the epilogue's quantization */
+  int32_t G;               /* number of groups, >= 1 */
+  int32_t validate_offsets;
+  int64_t R;               /* ragged extent: rows (RAGGED_M) or K (RAGGED_K) allocated */
+  int64_t M, N, K;         /* RAGGED_M: N, K used (M ignored); RAGGED_K: M, N used (K ignored) */
+  const int32_t* offsets;  /* device int32 [G] */
+  mx_packed A, B;
+  void* C;                 /* bf16 output, see mode */
+  const void* aux;         /* DSWIGLU: H bf16 [R][2F] */
+  mx_packed out_row, out_col; /* epilogue quantization outputs */
+} mx_grouped_args;
+
+int mx_grouped_gemm(const mx_grouped_args* args, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+/* Human-readable name of a status code (static string). */
+const char* mx_status_str(int status);
+/* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0. */
+int mx_device_supported(int device);
+/* Bytes of one packed operand's codes / scales for rows x K in fmt (0 on bad input). */
+int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K);
+int64_t mx_scales_bytes(int64_t rows, int64_t K);
+/* Library version string. */
+const char* mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H */

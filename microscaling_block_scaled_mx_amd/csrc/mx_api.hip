@@ -1,0 +1,377 @@
+// C ABI of libmx: host-side argument validation and launch composition.
+// Declarations and the contract of every entry point are in include/mx.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+#include <vector>
+
+#include "mx.h"
+#include "mx_kernels.h"
+
+namespace {
+
+using mx::GemmParams;
+using mx::PackParams;
+
+// ---------------------------------------------------------------- helpers
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int bits_of(int fmt) { return fmt == MX_E2M1 ? 4 : fmt == MX_E2M3 ? 6 : fmt == MX_E4M3 ? 8 : 0; }
+
+// Formats, scale modes and rotation the kernels serve: FLOOR for every
+// format (E4M3 with FLOOR takes emax 8), RCEIL only with E4M3 (its 448 is
+// E4M3's largest value), the rotation only with E2M3.
+bool combo_ok(int fmt, int mode, int had) {
+  if (bits_of(fmt) == 0) return false;
+  if (mode != MX_SCALE_FLOOR && mode != MX_SCALE_RCEIL) return false;
+  if (had != 0 && had != 1) return false;
+  if (mode == MX_SCALE_RCEIL && fmt != MX_E4M3) return false;
+  if (had && fmt != MX_E2M3) return false;
+  return true;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int device_state(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 2;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 2;
+    g_dev_state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  return g_dev_state[dev];
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MX_ERR_DEVICE;
+  }
+  return device_state(dev) == 1 ? MX_OK : MX_ERR_DEVICE;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MX_ERR_LAUNCH;
+  }
+  return MX_OK;
+}
+
+// grid dimensions the launches need must fit
+bool grid_fits(int64_t x, int64_t y, int64_t z) {
+  return x >= 0 && y >= 0 && z >= 0 && x < (1ll << 31) && y <= 65535 * 1024ll && z <= 65535;
+}
+
+// ---------------------------------------------------------------- quantize
+int validate_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt, int mode,
+                      int had, int pro, const void* rc, const void* rs, const void* cc, const void* cs,
+                      const float* part, const float* sum) {
+  if (!x) return MX_ERR_NULL;
+  if ((rc == nullptr) != (rs == nullptr) || (cc == nullptr) != (cs == nullptr)) return MX_ERR_NULL;
+  if (!rc && !cc && !part) return MX_ERR_NULL;
+  if (sum && !part) return MX_ERR_NULL;
+  if (pro < MX_PRO_IDENTITY || pro > MX_PRO_DSWIGLU) return MX_ERR_FORMAT;
+  const bool need_aux = (pro == MX_PRO_DGELU_TANH || pro == MX_PRO_DSWIGLU);
+  if (need_aux && !aux) return MX_ERR_NULL;
+  if (!combo_ok(fmt, mode, had)) return MX_ERR_FORMAT;
+  if (batch < 1 || R < 0 || C < 0 || R % 32 || C % 32) return MX_ERR_SHAPE;
+  if (pro == MX_PRO_DSWIGLU && C % 64) return MX_ERR_SHAPE;
+  const void* ptrs[] = {x, aux, rc, rs, cc, cs, part, sum};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MX_ERR_ALIGN;
+  if (!grid_fits((C + 127) / 128, (R + 63) / 64, batch)) return MX_ERR_INDEX_OVERFLOW;
+  return MX_OK;
+}
+
+int quantize_launch(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt, int mode,
+                    int had, int pro, void* rc, void* rs, void* cc, void* cs, float* part, float* sum,
+                    hipStream_t s) {
+  if (R == 0 || C == 0) return MX_OK;
+  PackParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.aux = static_cast<const uint16_t*>(aux);
+  p.R = R;
+  p.C = C;
+  p.row_codes = static_cast<uint8_t*>(rc);
+  p.row_scales = static_cast<uint8_t*>(rs);
+  p.col_codes = static_cast<uint8_t*>(cc);
+  p.col_scales = static_cast<uint8_t*>(cs);
+  p.partials = part;
+  int st = launched(mx::launch_pack(p, fmt, mode, had, pro, batch, s));
+  if (st != MX_OK) return st;
+  if (sum) st = launched(mx::launch_colsum_finish(part, R / 32, C, sum, batch, s));
+  return st;
+}
+
+// ---------------------------------------------------------------- GEMM
+int validate_gemm(const void* ac, const void* as, const void* bc, const void* bs, int64_t M, int64_t N,
+                  int64_t K, int fmt, const void* bias, int bias_dtype, const void* c, int c_dtype, int64_t ldc) {
+  if (!ac || !as || !bc || !bs || !c) return MX_ERR_NULL;
+  if (bits_of(fmt) == 0) return MX_ERR_FORMAT;
+  if ((bias_dtype != MX_BF16 && bias_dtype != MX_F32) || (c_dtype != MX_BF16 && c_dtype != MX_F32))
+    return MX_ERR_FORMAT;
+  if (M < 0 || N < 0 || K < 0 || M % 256 || N % 256 || K % 256) return MX_ERR_SHAPE;
+  if (ldc < N || ldc % 8) return MX_ERR_SHAPE;
+  const void* ptrs[] = {ac, as, bc, bs, bias, c};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MX_ERR_ALIGN;
+  if (!grid_fits(N / 256, M / 128, 1)) return MX_ERR_INDEX_OVERFLOW;
+  return MX_OK;
+}
+
+int gemm_launch(const void* ac, const void* as, const void* bc, const void* bs, int64_t M, int64_t N, int64_t K,
+                int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc, hipStream_t s) {
+  if (M == 0 || N == 0) return MX_OK;
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  p.a_codes = static_cast<const uint8_t*>(ac);
+  p.a_scales = static_cast<const uint8_t*>(as);
+  p.b_codes = static_cast<const uint8_t*>(bc);
+  p.b_scales = static_cast<const uint8_t*>(bs);
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ktot = K;
+  p.bias = bias;
+  p.bias_f32 = bias_dtype == MX_F32;
+  p.c = c;
+  p.ldc = ldc;
+  p.c_f32 = c_dtype == MX_F32;
+  return launched(mx::launch_gemm(p, fmt, mx::kDense, mx::kEpiStore, s));
+}
+
+bool packed_ok(const mx_packed& q) { return q.codes && q.scales; }
+bool packed_aligned(const mx_packed& q) { return aligned16(q.codes) && aligned16(q.scales); }
+
+}  // namespace
+
+extern "C" {
+
+int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt, int scale_mode,
+                int hadamard, int prologue, void* row_codes, void* row_scales, void* col_codes, void* col_scales,
+                float* colsum_partials, float* colsum, void* stream) {
+  int st = validate_quantize(x, aux, batch, R, C, fmt, scale_mode, hadamard, prologue, row_codes, row_scales,
+                             col_codes, col_scales, colsum_partials, colsum);
+  if (st != MX_OK) return st;
+  if ((st = check_device()) != MX_OK) return st;
+  return quantize_launch(x, aux, batch, R, C, fmt, scale_mode, hadamard, prologue, row_codes, row_scales,
+                         col_codes, col_scales, colsum_partials, colsum, static_cast<hipStream_t>(stream));
+}
+
+int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
+            int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
+            void* stream) {
+  int st = validate_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc);
+  if (st != MX_OK) return st;
+  if ((st = check_device()) != MX_OK) return st;
+  return gemm_launch(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc,
+                     static_cast<hipStream_t>(stream));
+}
+
+int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
+  if (!a) return MX_ERR_NULL;
+  if (!a->X || !a->W1 || !a->W2 || !a->h || !a->Y) return MX_ERR_NULL;
+  const mx_packed* packs[] = {&a->Xr, &a->Xc, &a->W1r, &a->W1c, &a->W2r, &a->W2c, &a->ar, &a->ac};
+  for (const mx_packed* q : packs)
+    if (!packed_ok(*q)) return MX_ERR_NULL;
+  if (!combo_ok(a->fmt, a->scale_mode, a->hadamard)) return MX_ERR_FORMAT;
+  const int64_t M = a->M, D = a->D, F = a->F;
+  if (M < 0 || D < 0 || F < 0 || M % 256 || D % 256 || F % 256) return MX_ERR_SHAPE;
+  const void* ptrs[] = {a->X, a->W1, a->b1, a->W2, a->h, a->Y};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MX_ERR_ALIGN;
+  for (const mx_packed* q : packs)
+    if (!packed_aligned(*q)) return MX_ERR_ALIGN;
+  if (!grid_fits(F / 128 + D / 128, M / 64, 1)) return MX_ERR_INDEX_OVERFLOW;
+  int st = check_device();
+  if (st != MX_OK) return st;
+  if (M == 0 || D == 0 || F == 0) return MX_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
+  // packs of X, W1, W2: rows for the forward, columns kept for the backward
+  if ((st = quantize_launch(a->X, nullptr, 1, M, D, fmt, mode, had, MX_PRO_IDENTITY, a->Xr.codes, a->Xr.scales,
+                            a->Xc.codes, a->Xc.scales, nullptr, nullptr, s)))
+    return st;
+  if ((st = quantize_launch(a->W1, nullptr, 1, F, D, fmt, mode, had, MX_PRO_IDENTITY, a->W1r.codes,
+                            a->W1r.scales, a->W1c.codes, a->W1c.scales, nullptr, nullptr, s)))
+    return st;
+  if ((st = quantize_launch(a->W2, nullptr, 1, D, F, fmt, mode, had, MX_PRO_IDENTITY, a->W2r.codes,
+                            a->W2r.scales, a->W2c.codes, a->W2c.scales, nullptr, nullptr, s)))
+    return st;
+  // fc1: h = X W1^T + b1 (bias in the fp32 accumulator, one rounding)
+  if ((st = gemm_launch(a->Xr.codes, a->Xr.scales, a->W1r.codes, a->W1r.scales, M, F, D, fmt, a->b1, MX_BF16,
+                        a->h, MX_BF16, F, s)))
+    return st;
+  // a = GELU(h) exists only inside the packer: packed rows for fc2, columns for dW2
+  if ((st = quantize_launch(a->h, nullptr, 1, M, F, fmt, mode, had, MX_PRO_GELU_TANH, a->ar.codes, a->ar.scales,
+                            a->ac.codes, a->ac.scales, nullptr, nullptr, s)))
+    return st;
+  // fc2: Y = a W2^T
+  return gemm_launch(a->ar.codes, a->ar.scales, a->W2r.codes, a->W2r.scales, M, D, F, fmt, nullptr, MX_BF16, a->Y,
+                     MX_BF16, D, s);
+}
+
+int mx_fused_mlp_bwd(const mx_mlp_bwd_args* a, void* stream) {
+  if (!a) return MX_ERR_NULL;
+  if (!a->dY || !a->h || !a->da || !a->dX || !a->dW1 || !a->dW2) return MX_ERR_NULL;
+  if (a->db1 && !a->db1_partials) return MX_ERR_NULL;
+  const mx_packed* packs[] = {&a->Xc, &a->W1c, &a->W2c, &a->ac, &a->dYr, &a->dYc, &a->dhr, &a->dhc};
+  for (const mx_packed* q : packs)
+    if (!packed_ok(*q)) return MX_ERR_NULL;
+  if (!combo_ok(a->fmt, a->scale_mode, a->hadamard)) return MX_ERR_FORMAT;
+  const int64_t M = a->M, D = a->D, F = a->F;
+  if (M < 0 || D < 0 || F < 0 || M % 256 || D % 256 || F % 256) return MX_ERR_SHAPE;
+  const void* ptrs[] = {a->dY, a->h, a->da, a->dX, a->dW1, a->dW2, a->db1, a->db1_partials};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MX_ERR_ALIGN;
+  for (const mx_packed* q : packs)
+    if (!packed_aligned(*q)) return MX_ERR_ALIGN;
+  if (!grid_fits(F / 128 + D / 128, M / 64 + F / 64, 1)) return MX_ERR_INDEX_OVERFLOW;
+  int st = check_device();
+  if (st != MX_OK) return st;
+  if (M == 0 || D == 0 || F == 0) return MX_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
+  if ((st = quantize_launch(a->dY, nullptr, 1, M, D, fmt, mode, had, MX_PRO_IDENTITY, a->dYr.codes, a->dYr.scales,
+                            a->dYc.codes, a->dYc.scales, nullptr, nullptr, s)))
+    return st;
+  // fc2 dgrad: da = dY W2 (K = D), materialised
+  if ((st = gemm_launch(a->dYr.codes, a->dYr.scales, a->W2c.codes, a->W2c.scales, M, F, D, fmt, nullptr, MX_BF16,
+                        a->da, MX_BF16, F, s)))
+    return st;
+  // dh = dGELU(da, h) exists only inside the packer; bias gradient from its column sums
+  if ((st = quantize_launch(a->da, a->h, 1, M, F, fmt, mode, had, MX_PRO_DGELU_TANH, a->dhr.codes, a->dhr.scales,
+                            a->dhc.codes, a->dhc.scales, a->db1 ? a->db1_partials : nullptr, a->db1, s)))
+    return st;
+  // fc1 dgrad: dX = dh W1 (K = F)
+  if ((st = gemm_launch(a->dhr.codes, a->dhr.scales, a->W1c.codes, a->W1c.scales, M, D, F, fmt, nullptr, MX_BF16,
+                        a->dX, MX_BF16, D, s)))
+    return st;
+  // fc1 wgrad: dW1 = dh^T X (K = M)
+  if ((st = gemm_launch(a->dhc.codes, a->dhc.scales, a->Xc.codes, a->Xc.scales, F, D, M, fmt, nullptr, MX_BF16,
+                        a->dW1, MX_BF16, D, s)))
+    return st;
+  // fc2 wgrad: dW2 = dY^T a (K = M)
+  return gemm_launch(a->dYc.codes, a->dYc.scales, a->ac.codes, a->ac.scales, D, F, M, fmt, nullptr, MX_BF16,
+                     a->dW2, MX_BF16, F, s);
+}
+
+int mx_grouped_gemm(const mx_grouped_args* a, void* stream) {
+  if (!a) return MX_ERR_NULL;
+  if (!a->offsets || !packed_ok(a->A) || !packed_ok(a->B)) return MX_ERR_NULL;
+  if (bits_of(a->fmt) == 0) return MX_ERR_FORMAT;
+  if (a->mode != MX_GROUPED_RAGGED_M && a->mode != MX_GROUPED_RAGGED_K) return MX_ERR_FORMAT;
+  if (a->epilogue < MX_EPI_NONE || a->epilogue > MX_EPI_DSWIGLU) return MX_ERR_FORMAT;
+  if (a->mode == MX_GROUPED_RAGGED_K && a->epilogue != MX_EPI_NONE) return MX_ERR_FORMAT;
+  const bool quant = a->epilogue != MX_EPI_NONE;
+  if (quant) {
+    if (!combo_ok(a->fmt, a->scale_mode, 0)) return MX_ERR_FORMAT;
+    if (!packed_ok(a->out_row) || !packed_ok(a->out_col)) return MX_ERR_NULL;
+    if (a->epilogue == MX_EPI_DSWIGLU && !a->aux) return MX_ERR_NULL;
+  }
+  if (a->epilogue != MX_EPI_DSWIGLU && !a->C) return MX_ERR_NULL;
+  if (a->G < 1 || a->G > 65535 || a->R < 0 || a->R % 128) return MX_ERR_SHAPE;
+  if (a->mode == MX_GROUPED_RAGGED_M) {
+    if (a->N <= 0 || a->K < 0 || a->N % 256 || a->K % 128) return MX_ERR_SHAPE;
+  } else {
+    if (a->M < 0 || a->N < 0 || a->M % 256 || a->N % 256) return MX_ERR_SHAPE;
+  }
+  const void* ptrs[] = {a->offsets, a->A.codes, a->A.scales, a->B.codes, a->B.scales, a->C, a->aux,
+                        a->out_row.codes, a->out_row.scales, a->out_col.codes, a->out_col.scales};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MX_ERR_ALIGN;
+  if (!grid_fits(a->N / 128 + 1, a->R / 128 + a->M / 128, a->G)) return MX_ERR_INDEX_OVERFLOW;
+  int st = check_device();
+  if (st != MX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->validate_offsets) {
+    std::vector<int32_t> off(a->G);
+    if (hipMemcpyAsync(off.data(), a->offsets, sizeof(int32_t) * a->G, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+      (void)hipGetLastError();
+      return MX_ERR_LAUNCH;
+    }
+    int32_t prev = 0;
+    for (int i = 0; i < a->G; ++i) {
+      if (off[i] < prev || off[i] % 128 || off[i] > a->R) return MX_ERR_OFFSETS;
+      prev = off[i];
+    }
+  }
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  p.a_codes = static_cast<const uint8_t*>(a->A.codes);
+  p.a_scales = static_cast<const uint8_t*>(a->A.scales);
+  p.b_codes = static_cast<const uint8_t*>(a->B.codes);
+  p.b_scales = static_cast<const uint8_t*>(a->B.scales);
+  p.offsets = a->offsets;
+  p.G = a->G;
+  p.R = a->R;
+  p.c = a->C;
+  p.c_f32 = 0;
+  p.q_mode = a->scale_mode;
+  if (a->mode == MX_GROUPED_RAGGED_M) {
+    if (a->R == 0) return MX_OK;
+    p.M = a->R;
+    p.N = a->N;
+    p.K = a->K;
+    p.ktot = a->K;
+    p.ldc = a->N;
+    p.b_group_rows = a->N;
+    p.F = a->epilogue == MX_EPI_SWIGLU ? a->N / 2 : a->N;
+    p.aux = static_cast<const uint16_t*>(a->aux);
+    p.q_row_codes = static_cast<uint8_t*>(a->out_row.codes);
+    p.q_row_scales = static_cast<uint8_t*>(a->out_row.scales);
+    p.q_col_codes = static_cast<uint8_t*>(a->out_col.codes);
+    p.q_col_scales = static_cast<uint8_t*>(a->out_col.scales);
+    const int epi = a->epilogue == MX_EPI_SWIGLU ? mx::kEpiSwiglu
+                    : a->epilogue == MX_EPI_DSWIGLU ? mx::kEpiDSwiglu
+                                                     : mx::kEpiStore;
+    if (epi == mx::kEpiSwiglu && (a->N / 2) % 128) return MX_ERR_SHAPE;
+    return launched(mx::launch_gemm(p, a->fmt, mx::kRaggedM, epi, s));
+  }
+  if (a->M == 0 || a->N == 0) return MX_OK;
+  p.M = a->M;
+  p.N = a->N;
+  p.K = 0;
+  p.ktot = a->R;
+  p.ldc = a->N;
+  return launched(mx::launch_gemm(p, a->fmt, mx::kRaggedK, mx::kEpiStore, s));
+}
+
+const char* mx_status_str(int status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: a size is out of range or not the required multiple";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case MX_ERR_FORMAT: return "MX_ERR_FORMAT: unsupported format / scale mode / prologue / epilogue combination";
+    case MX_ERR_OFFSETS: return "MX_ERR_OFFSETS: group offsets break their contract";
+    case MX_ERR_INDEX_OVERFLOW: return "MX_ERR_INDEX_OVERFLOW: a size exceeds what one launch can index";
+    case MX_ERR_DEVICE: return "MX_ERR_DEVICE: no gfx950 device is current";
+    case MX_ERR_LAUNCH: return "MX_ERR_LAUNCH: the HIP runtime failed to enqueue";
+    default: return "unknown mx status";
+  }
+}
+
+int mx_device_supported(int device) { return device_state(device) == 1 ? 1 : 0; }
+
+int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K) {
+  const int b = bits_of(fmt);
+  if (!b || rows < 0 || K < 0 || K % 32) return 0;
+  return rows * (K * b / 8);
+}
+
+int64_t mx_scales_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || K % 32) return 0;
+  return rows * (K / 32);
+}
+
+const char* mx_version(void) { return "libmx 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,301 @@
+// Device-side building blocks of libmx (gfx950): bf16 conversion, E8M0 scale
+// selection, E2M1/E2M3/E4M3 encoding, bit packing, the 32-point Hadamard
+// butterfly and the activation prologues.  Compiled with -ffp-contract=off:
+// every float operation below is one binary32 operation, rounded to nearest
+// even, so the results are reproducible to the bit.
+//
+// Page references (by title):
+//   [P1] "feat(mxfp6): MXFP6 (E2M3) Flux linears, a fused MLP, and the MLPerf
+//        recipe" (Primus pull request 1064)
+//   [P3] "MXFP4 training for Flux models" (ROCm Primus technical guide)
+//   [P4] "MXFP8 cudnn-fe Swiglu fused Grouped MLP fwd/bwd and wgrad group
+//        gemm" (ao pull request 5)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+enum Fmt { kE2M1 = 1, kE2M3 = 2, kE4M3 = 3 };
+enum ScaleMode { kFloor = 0, kRceil = 1 };
+enum Prologue { kIdentity = 0, kGelu = 1, kDGelu = 2, kSwiglu = 3, kDSwiglu = 4 };
+
+template <int FMT> struct FmtTraits;
+// E2M1: s|e2|m1, bias 1, largest 6.0 (code 7), sign bit 3.
+template <> struct FmtTraits<kE2M1> {
+  static constexpr int kBits = 4, kMant = 1, kEmin = 0, kEmaxElem = 2;
+  static constexpr uint32_t kMaxCode = 7, kSign = 0x8;
+};
+// E2M3: s|e2|m3, bias 1, largest 7.5 (code 31), sign bit 5.
+template <> struct FmtTraits<kE2M3> {
+  static constexpr int kBits = 6, kMant = 3, kEmin = 0, kEmaxElem = 2;
+  static constexpr uint32_t kMaxCode = 31, kSign = 0x20;
+};
+// E4M3 ("fn"): s|e4|m3, bias 7, largest 448 (code 0x7e), no infinities.
+template <> struct FmtTraits<kE4M3> {
+  static constexpr int kBits = 8, kMant = 3, kEmin = -6, kEmaxElem = 8;
+  static constexpr uint32_t kMaxCode = 0x7e, kSign = 0x80;
+};
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// binary32 -> bf16 bits, nearest-even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
+}
+// Round through bf16 and back.
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16(f) << 16); }
+
+// ------------------------------------------------------------------ E8M0
+// Scale byte from the block's amax, given as the bit pattern of |amax| in
+// binary32.  For non-negative floats integer order is value order and every
+// NaN pattern sorts above +Inf, so a plain unsigned max over |x| bits is a
+// NaN-propagating amax ([P4] commit messages).
+//   NaN/Inf block     -> 0xff.
+//   FLOOR: X = floor(log2 amax) - emax_elem  (exponent field; a subnormal
+//          or zero amax falls under the low clamp anyway).
+//   RCEIL: X = smallest integer with 448 * 2^X >= amax.  With amax = m*2^E,
+//          m in [1,2): 448*2^(E-8) = 1.75*2^E, so X = E - 8 + (m > 1.75);
+//          exact, no division ([P4]: the scale's E8M0 conversion rounds up).
+//   X clamped to [-127, 127]; byte = X + 127.
+template <int FMT, int MODE>
+__device__ __forceinline__ uint32_t scale_byte(uint32_t amax_bits) {
+  int ef = (int)(amax_bits >> 23);
+  int X;
+  if (MODE == kRceil) {
+    X = ef - 127 - 8 + ((amax_bits & 0x7fffffu) > 0x600000u ? 1 : 0);
+  } else {
+    X = ef - 127 - FmtTraits<FMT>::kEmaxElem;
+  }
+  X = X < -127 ? -127 : (X > 127 ? 127 : X);
+  return amax_bits >= 0x7f800000u ? 0xffu : (uint32_t)(X + 127);
+}
+
+// 2^-X as a binary32 (X in [-127, 125] from the selection above, so the
+// result is always a normal number).
+__device__ __forceinline__ float inv_scale(uint32_t byte) {
+  return __uint_as_float((254u - byte) << 23);
+}
+
+// ------------------------------------------------------------------ encode
+// Encode a scaled value v (|v| within the format's range up to saturation):
+// round to the nearest code, ties to the even code, saturate at the largest
+// finite magnitude, keep the sign (negative values rounding to zero give the
+// negative-zero code).  With E = max(floor(log2 |v|), emin) the code is
+// rint(|v| * 2^(mant - E)) + ((E - emin) << mant): inside one binade the
+// codes are evenly spaced, and a round-up across a binade edge lands on the
+// next binade's first code.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode(float v) {
+  using T = FmtTraits<FMT>;
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 31) ? T::kSign : 0u;
+  uint32_t a = u & 0x7fffffffu;
+  int E = (int)(a >> 23) - 127;
+  E = E < T::kEmin ? T::kEmin : E;
+  E = E > 8 ? 8 : E;  // |v| <= 512 by construction; keeps the factor normal
+  float f = __uint_as_float((uint32_t)(127 + T::kMant - E) << 23);
+  float t = __uint_as_float(a) * f;
+  uint32_t code = (uint32_t)(int)__builtin_rintf(t) + ((uint32_t)(E - T::kEmin) << T::kMant);
+  code = code > T::kMaxCode ? T::kMaxCode : code;
+  return code | sign;
+}
+
+// ------------------------------------------------------------------ packing
+// Pack 32 codes of one block into the in-memory layout (dwords, little
+// endian): E2M1 4 dwords, E2M3 6 dwords, E4M3 8 dwords.
+template <int FMT>
+__device__ __forceinline__ void pack32(const uint32_t (&c)[32], uint32_t (&w)[FmtTraits<FMT>::kBits]) {
+  constexpr int B = FmtTraits<FMT>::kBits;
+#pragma unroll
+  for (int i = 0; i < B; ++i) w[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int bit = j * B, wd = bit >> 5, off = bit & 31;
+    w[wd] |= c[j] << off;
+    if (off + B > 32) w[wd + 1] |= c[j] >> (32 - off);
+  }
+}
+
+// ------------------------------------------------------------------ Hadamard
+// Normalised 32-point Walsh-Hadamard rotation in Sylvester order ([P1]
+// description: mandatory for MXFP6, folded into the packer).  Radix-2
+// butterfly, strides 1, 2, 4, 8, 16 (a+b, a-b), then one multiply by
+// fl32(1/sqrt(32)) = 0x3e3504f3.
+__device__ __forceinline__ void hadamard32(float (&y)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+  const float c = __uint_as_float(0x3e3504f3u);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) y[i] = y[i] * c;
+}
+
+// ------------------------------------------------------------------ quantize one block
+// v: 32 values (prologue applied, bf16-rounded, rotated if asked).
+// Returns the scale byte; fills the packed words.
+template <int FMT, int MODE>
+__device__ __forceinline__ uint32_t quant_block(const float (&v)[32], uint32_t (&w)[FmtTraits<FMT>::kBits]) {
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+    amax = amax > b ? amax : b;
+  }
+  const uint32_t s = scale_byte<FMT, MODE>(amax);
+  const float f = inv_scale(s == 0xffu ? 127u : s);
+  uint32_t c[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) c[i] = (s == 0xffu) ? 0u : encode<FMT>(v[i] * f);
+  pack32<FMT>(c, w);
+  return s;
+}
+
+// ------------------------------------------------------------------ LDS tiles
+// A bf16 tile in LDS, row-major with `pitch` bytes per row.
+// Row block: 32 consecutive bf16 of one row (16-byte aligned start).
+__device__ __forceinline__ void lds_row_block(const uint8_t* tile, int pitch, int row, int col0, float (&v)[32]) {
+  const uint4* src = reinterpret_cast<const uint4*>(tile + row * pitch + col0 * 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 q = src[j];
+    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * j + 2 * k] = bf16_lo(ws[k]);
+      v[8 * j + 2 * k + 1] = bf16_hi(ws[k]);
+    }
+  }
+}
+// Column block: rows row0..row0+31 of one column.
+__device__ __forceinline__ void lds_col_block(const uint8_t* tile, int pitch, int row0, int col, float (&v)[32]) {
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(tile + row0 * pitch) + col;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(src[i * (pitch / 2)]);
+}
+
+// Store one block's packed codes (E2M1 16 B, E2M3 24 B at 8-byte alignment,
+// E4M3 32 B).
+template <int FMT>
+__device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t (&w)[FmtTraits<FMT>::kBits]) {
+  if constexpr (FMT == kE2M1) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (FMT == kE2M3) {
+    uint2* d = reinterpret_cast<uint2*>(dst);
+    d[0] = make_uint2(w[0], w[1]);
+    d[1] = make_uint2(w[2], w[3]);
+    d[2] = make_uint2(w[4], w[5]);
+  } else {
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// Quantize 32 values and write codes + scale byte.
+template <int FMT, int MODE, int HAD>
+__device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* codes, uint8_t* scale) {
+  if constexpr (HAD) hadamard32(v);
+  uint32_t w[FmtTraits<FMT>::kBits];
+  const uint32_t s = quant_block<FMT, MODE>(v, w);
+  store_block<FMT>(codes, w);
+  *scale = (uint8_t)s;
+}
+
+// ------------------------------------------------------------------ prologue math
+// Own exp (binary32), the library's contract: Cody-Waite reduction
+// n = rint(x * LOG2E), r = (x - n*LN2_HI) - n*LN2_LO with LN2_HI = ln 2 cut
+// to 16 significant bits, then the degree-7 Taylor polynomial (1/k! rounded
+// to binary32) in Horner order, scaled by 2^n.  x < -87 -> +0 (results stay
+// normal), x > 89 -> +inf, NaN -> NaN.
+__device__ __forceinline__ float mx_exp(float x) {
+  const float LOG2E = 0x1.715476p+0f;   // fl32(1/ln 2)
+  const float LN2_HI = 0x1.62e4p-1f;     // 0.693145751953125
+  const float LN2_LO = 0x1.7f7d1cp-20f;  // fl32(ln 2 - LN2_HI)
+  const float P2 = 0x1.0p-1f, P3 = 0x1.555556p-3f, P4 = 0x1.555556p-5f;
+  const float P5 = 0x1.111112p-7f, P6 = 0x1.6c16c2p-10f, P7 = 0x1.a01a02p-13f;
+  float n = __builtin_rintf(x * LOG2E);
+  float r = x - n * LN2_HI;
+  r = r - n * LN2_LO;
+  float p = P7;
+  p = P6 + r * p;
+  p = P5 + r * p;
+  p = P4 + r * p;
+  p = P3 + r * p;
+  p = P2 + r * p;
+  p = 1.0f + r * p;
+  p = 1.0f + r * p;
+  float res = __builtin_ldexpf(p, (int)n);
+  res = (x > 89.0f) ? __builtin_inff() : res;
+  res = (x < -87.0f) ? 0.0f : res;
+  return (x != x) ? x : res;
+}
+
+// tanh-GELU pieces.  u = K0*(x + K1*((x*x)*x)); q = 2/(exp(2|u|)+1);
+// 1 + tanh(u) = q (u < 0) or 2 - q (u >= 0); 1 - tanh(u)^2 = q*(2-q).
+// K0 = fl32(sqrt(2/pi)), K1 = fl32(0.044715).
+__device__ __forceinline__ float gelu_u(float x) {
+  const float K0 = 0x1.988454p-1f, K1 = 0x1.6e4e26p-5f;
+  float x3 = (x * x) * x;
+  float inner = x + K1 * x3;
+  return K0 * inner;
+}
+__device__ __forceinline__ float gelu_q(float u) {
+  float e = mx_exp(2.0f * __builtin_fabsf(u));
+  return 2.0f / (e + 1.0f);
+}
+
+// a = bf16((0.5*x) * (1 + tanh u))
+__device__ __forceinline__ float gelu_bf16(float x) {
+  float u = gelu_u(x);
+  float q = gelu_q(u);
+  float opt = (u < 0.0f) ? q : (2.0f - q);
+  return round_bf16((0.5f * x) * opt);
+}
+
+// dh = bf16(da * (0.5*(1+tanh u) + (0.5*x) * ((q*(2-q)) * (K0*(1 + (3*K1)*(x*x))))))
+// with the second term taken as 0 when q*(2-q) == 0.
+__device__ __forceinline__ float dgelu_bf16(float da, float x) {
+  const float K0 = 0x1.988454p-1f, K1x3 = 0x1.12ba9cp-3f;  // fl32(3 * fl32(0.044715))
+  float u = gelu_u(x);
+  float q = gelu_q(u);
+  float opt = (u < 0.0f) ? q : (2.0f - q);
+  float w = q * (2.0f - q);
+  float first = 0.5f * opt;
+  float second = (0.5f * x) * (w * (K0 * (1.0f + K1x3 * (x * x))));
+  second = (w == 0.0f) ? 0.0f : second;
+  return round_bf16(da * (first + second));
+}
+
+// SwiGLU on [gate | up] ([P4] commit messages: sigmoid as 1/(1+exp(-x))).
+__device__ __forceinline__ float sigmoid_mx(float g) { return 1.0f / (1.0f + mx_exp(-g)); }
+__device__ __forceinline__ float swiglu_bf16(float g, float u) {
+  float s = sigmoid_mx(g);
+  return round_bf16((g * s) * u);
+}
+// d_gate = bf16((dz*u) * (s*(1 + g*(1-s)))),  d_up = bf16(dz*(g*s)).
+__device__ __forceinline__ float dswiglu_gate_bf16(float dz, float g, float u) {
+  float s = sigmoid_mx(g);
+  return round_bf16((dz * u) * (s * (1.0f + g * (1.0f - s))));
+}
+__device__ __forceinline__ float dswiglu_up_bf16(float dz, float g) {
+  float s = sigmoid_mx(g);
+  return round_bf16(dz * (g * s));
+}
+
+}  // namespace mx

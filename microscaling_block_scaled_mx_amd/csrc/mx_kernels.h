@@ -1,0 +1,59 @@
+// Internal launch interface between the C ABI (mx_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+struct PackParams {
+  const uint16_t* x;    // prologue input (bf16 bits)
+  const uint16_t* aux;  // second prologue input or nullptr
+  int64_t R, C;         // logical quantized tensor [R][C] per batch entry
+  uint8_t* row_codes;   // [R][C*bits/8] or nullptr
+  uint8_t* row_scales;  // [R][C/32]
+  uint8_t* col_codes;   // [C][R*bits/8] or nullptr
+  uint8_t* col_scales;  // [C][R/32]
+  float* partials;      // [R/32][C] or nullptr
+};
+
+bool pack_supported(int fmt, int mode, int had, int pro);
+hipError_t launch_pack(const PackParams& p, int fmt, int mode, int had, int pro, int64_t batch,
+                       hipStream_t stream);
+hipError_t launch_colsum_finish(const float* partials, int64_t nb, int64_t C, float* out, int64_t batch,
+                                hipStream_t stream);
+
+enum GemmMode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
+enum Epilogue { kEpiStore = 0, kEpiSwiglu = 1, kEpiDSwiglu = 2 };
+
+struct GemmParams {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int64_t M, N;          // output extent (per group for ragged-K)
+  int64_t K;             // reduction length (dense, ragged-M)
+  int64_t ktot;          // row length of A/B in elements (K, or R for ragged-K)
+  const void* bias;      // [N] or nullptr
+  int bias_f32;          // bias dtype: 0 bf16, 1 f32
+  void* c;               // output
+  int64_t ldc;           // output row pitch in elements
+  int c_f32;             // output dtype: 0 bf16, 1 f32
+  // grouped
+  const int32_t* offsets;
+  int G;
+  int64_t b_group_rows;  // ragged-M: rows of B per group (N)
+  // epilogue quantization (SwiGLU / dSwiGLU)
+  int64_t R;             // ragged extent allocated (rows of H / out_row, K of out_col)
+  int64_t F;             // SwiGLU hidden width
+  const uint16_t* aux;   // dSwiGLU: H [R][2F]
+  uint8_t* q_row_codes;
+  uint8_t* q_row_scales;
+  uint8_t* q_col_codes;
+  uint8_t* q_col_scales;
+  int q_mode;            // scale mode for the epilogue's quantization
+};
+
+hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,189 @@
+"""Thin ctypes binding of libmx (include/mx.h).  Argument marshalling only:
+every step of the path runs in the HIP kernels behind the C ABI.  torch is
+used for device memory (tensors) and the current stream.  There is no
+fallback: if libmx.so is missing or a call fails, an exception is raised."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmx.so")
+
+# mx_fmt / mx_scale_mode / mx_prologue / mx_dtype / grouped enums (include/mx.h)
+E2M1, E2M3, E4M3 = 1, 2, 3
+FLOOR, RCEIL = 0, 1
+PRO_IDENTITY, PRO_GELU_TANH, PRO_DGELU_TANH, PRO_SWIGLU, PRO_DSWIGLU = 0, 1, 2, 3, 4
+BF16, F32 = 0, 1
+RAGGED_M, RAGGED_K = 0, 1
+EPI_NONE, EPI_SWIGLU, EPI_DSWIGLU = 0, 1, 2
+BITS = {E2M1: 4, E2M3: 6, E4M3: 8}
+
+STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_FORMAT",
+          5: "MX_ERR_OFFSETS", 6: "MX_ERR_INDEX_OVERFLOW", 7: "MX_ERR_DEVICE", 8: "MX_ERR_LAUNCH"}
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class Packed(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class MlpFwdArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("D", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("fmt", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("hadamard", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("X", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("h", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("Xr", Packed), ("Xc", Packed), ("W1r", Packed), ("W1c", Packed), ("W2r", Packed),
+                ("W2c", Packed), ("ar", Packed), ("ac", Packed)]
+
+
+class MlpBwdArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("D", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("fmt", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("hadamard", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("dY", ctypes.c_void_p), ("h", ctypes.c_void_p),
+                ("Xc", Packed), ("W1c", Packed), ("W2c", Packed), ("ac", Packed),
+                ("da", ctypes.c_void_p), ("dX", ctypes.c_void_p), ("dW1", ctypes.c_void_p),
+                ("dW2", ctypes.c_void_p), ("db1", ctypes.c_void_p), ("db1_partials", ctypes.c_void_p),
+                ("dYr", Packed), ("dYc", Packed), ("dhr", Packed), ("dhc", Packed)]
+
+
+class GroupedArgs(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("scale_mode", ctypes.c_int32), ("G", ctypes.c_int32), ("validate_offsets", ctypes.c_int32),
+                ("R", ctypes.c_int64), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("offsets", ctypes.c_void_p), ("A", Packed), ("B", Packed), ("C", ctypes.c_void_p),
+                ("aux", ctypes.c_void_p), ("out_row", Packed), ("out_col", Packed)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmx.so (built in-tree by microscaling_block_scaled_mx_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m microscaling_block_scaled_mx_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mx_quantize.restype = ci
+        L.mx_quantize.argtypes = [vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.mx_gemm.restype = ci
+        L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
+        L.mx_fused_mlp_fwd.restype = ci
+        L.mx_fused_mlp_fwd.argtypes = [ctypes.POINTER(MlpFwdArgs), vp]
+        L.mx_fused_mlp_bwd.restype = ci
+        L.mx_fused_mlp_bwd.argtypes = [ctypes.POINTER(MlpBwdArgs), vp]
+        L.mx_grouped_gemm.restype = ci
+        L.mx_grouped_gemm.argtypes = [ctypes.POINTER(GroupedArgs), vp]
+        L.mx_status_str.restype = ctypes.c_char_p
+        L.mx_status_str.argtypes = [ci]
+        L.mx_device_supported.restype = ci
+        L.mx_device_supported.argtypes = [ci]
+        L.mx_codes_bytes.restype = i64
+        L.mx_codes_bytes.argtypes = [ci, i64, i64]
+        L.mx_scales_bytes.restype = i64
+        L.mx_scales_bytes.argtypes = [i64, i64]
+        L.mx_version.restype = ctypes.c_char_p
+        L.mx_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise MXError(st, what)
+
+
+# ---------------------------------------------------------------- buffers
+def alloc_packed(rows: int, K: int, fmt: int, device="cuda", batch: int | None = None):
+    """(codes, scales) uint8 tensors for a packed operand [rows] x K."""
+    shape = (rows, K * BITS[fmt] // 8) if batch is None else (batch, rows, K * BITS[fmt] // 8)
+    sshape = (rows, K // 32) if batch is None else (batch, rows, K // 32)
+    return (torch.empty(shape, dtype=torch.uint8, device=device),
+            torch.empty(sshape, dtype=torch.uint8, device=device))
+
+
+def _packed(p):
+    return Packed(_ptr(p[0]), _ptr(p[1])) if p is not None else Packed(None, None)
+
+
+# ---------------------------------------------------------------- entry points
+def quantize(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = False,
+             prologue: int = PRO_IDENTITY, aux=None, row=None, col=None, colsum_partials=None, colsum=None,
+             batch: int = 1, stream=None):
+    """mx_quantize: row=(codes, scales) [R] x K=C, col=(codes, scales) [C] x K=R."""
+    st = lib().mx_quantize(_ptr(x), _ptr(aux), batch, R, C, fmt, scale_mode, int(hadamard), prologue,
+                           _ptr(row[0]) if row else None, _ptr(row[1]) if row else None,
+                           _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
+                           _ptr(colsum_partials), _ptr(colsum), _stream(stream))
+    _check(st, "mx_quantize")
+
+
+def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16, c_dtype: int = BF16,
+         ldc: int | None = None, stream=None):
+    """mx_gemm: c [M][ldc] = A . B^T (+ bias); a, b = (codes, scales)."""
+    st = lib().mx_gemm(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
+                       _ptr(c), c_dtype, N if ldc is None else ldc, _stream(stream))
+    _check(st, "mx_gemm")
+
+
+def fused_mlp_fwd(M, D, F, X, W1, b1, W2, h, Y, Xr, Xc, W1r, W1c, W2r, W2c, ar, ac, fmt=E2M3,
+                  scale_mode=FLOOR, hadamard=True, stream=None):
+    a = MlpFwdArgs(M, D, F, fmt, scale_mode, int(hadamard), 0, _ptr(X), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(h),
+                   _ptr(Y), _packed(Xr), _packed(Xc), _packed(W1r), _packed(W1c), _packed(W2r), _packed(W2c),
+                   _packed(ar), _packed(ac))
+    _check(lib().mx_fused_mlp_fwd(ctypes.byref(a), _stream(stream)), "mx_fused_mlp_fwd")
+
+
+def fused_mlp_bwd(M, D, F, dY, h, Xc, W1c, W2c, ac, da, dX, dW1, dW2, db1, db1_partials, dYr, dYc, dhr, dhc,
+                  fmt=E2M3, scale_mode=FLOOR, hadamard=True, stream=None):
+    a = MlpBwdArgs(M, D, F, fmt, scale_mode, int(hadamard), 0, _ptr(dY), _ptr(h), _packed(Xc), _packed(W1c),
+                   _packed(W2c), _packed(ac), _ptr(da), _ptr(dX), _ptr(dW1), _ptr(dW2), _ptr(db1),
+                   _ptr(db1_partials), _packed(dYr), _packed(dYc), _packed(dhr), _packed(dhc))
+    _check(lib().mx_fused_mlp_bwd(ctypes.byref(a), _stream(stream)), "mx_fused_mlp_bwd")
+
+
+def grouped_gemm(mode, G, R, offsets, A, B, C, fmt=E4M3, epilogue=EPI_NONE, scale_mode=RCEIL, M=0, N=0, K=0,
+                 aux=None, out_row=None, out_col=None, validate_offsets=False, stream=None):
+    a = GroupedArgs(mode, epilogue, fmt, scale_mode, G, int(validate_offsets), R, M, N, K, _ptr(offsets),
+                    _packed(A), _packed(B), _ptr(C), _ptr(aux), _packed(out_row), _packed(out_col))
+    _check(lib().mx_grouped_gemm(ctypes.byref(a), _stream(stream)), "mx_grouped_gemm")
+
+
+def device_supported(device: int = 0) -> bool:
+    return bool(lib().mx_device_supported(device))
+
+
+def status_str(st: int) -> str:
+    return lib().mx_status_str(st).decode()
+
+
+def version() -> str:
+    return lib().mx_version().decode()

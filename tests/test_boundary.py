@@ -1,0 +1,175 @@
+"""C-ABI boundary checks that need no GPU: libmx.so loads, exports every
+function include/mx.h declares, and rejects malformed arguments on the host
+with the documented status before touching a device.  With well-formed
+arguments and no gfx950 device present the call must answer MX_ERR_DEVICE
+(never a silent success or a CPU fallback)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from microscaling_block_scaled_mx_amd import mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+OK, NULL, SHAPE, ALIGN, FORMAT, OFFSETS, OVERFLOW, DEVICE = 0, 1, 2, 3, 4, 5, 6, 7
+P = 0x10000  # a 16-byte aligned fake device address; never dereferenced on these paths
+P2, P3, P4, P5, P6, P7, P8 = (P * i for i in range(2, 9))
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mx_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mx.lib()
+    names = header_functions()
+    assert {"mx_quantize", "mx_gemm", "mx_fused_mlp_fwd", "mx_fused_mlp_bwd", "mx_grouped_gemm"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_sizes():
+    assert mx.status_str(0) == "MX_OK"
+    for st in range(1, 9):
+        assert mx.status_str(st).startswith(mx.STATUS[st])
+    L = mx.lib()
+    assert L.mx_codes_bytes(mx.E2M1, 256, 256) == 256 * 128
+    assert L.mx_codes_bytes(mx.E2M3, 256, 256) == 256 * 192
+    assert L.mx_codes_bytes(mx.E4M3, 256, 256) == 256 * 256
+    assert L.mx_codes_bytes(9, 256, 256) == 0 and L.mx_codes_bytes(mx.E2M1, 1, 33) == 0
+    assert L.mx_scales_bytes(256, 512) == 256 * 16
+    assert "gfx950" in mx.version()
+
+
+def q(**kw):
+    a = dict(x=P, aux=None, batch=1, R=64, C=128, fmt=mx.E2M1, mode=mx.FLOOR, had=0, pro=mx.PRO_IDENTITY,
+             rc=P2, rs=P3, cc=P4, cs=P5, part=None, sum=None)
+    a.update(kw)
+    return mx.lib().mx_quantize(a["x"], a["aux"], a["batch"], a["R"], a["C"], a["fmt"], a["mode"], a["had"],
+                                a["pro"], a["rc"], a["rs"], a["cc"], a["cs"], a["part"], a["sum"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL),
+    (dict(rc=None), NULL),                       # codes without scales
+    (dict(cs=None), NULL),
+    (dict(rc=None, rs=None, cc=None, cs=None), NULL),  # nothing requested
+    (dict(sum=P6), NULL),                        # colsum without partials
+    (dict(pro=mx.PRO_DGELU_TANH), NULL),         # aux required
+    (dict(pro=mx.PRO_DSWIGLU), NULL),
+    (dict(fmt=0), FORMAT), (dict(fmt=4), FORMAT),
+    (dict(mode=2), FORMAT),
+    (dict(fmt=mx.E2M1, mode=mx.RCEIL), FORMAT),  # RCEIL is E4M3's
+    (dict(fmt=mx.E2M1, had=1), FORMAT),          # rotation is E2M3's
+    (dict(fmt=mx.E4M3, mode=mx.RCEIL, had=1), FORMAT),
+    (dict(pro=7), FORMAT),
+    (dict(R=48), SHAPE), (dict(C=40), SHAPE), (dict(R=-32), SHAPE), (dict(batch=0), SHAPE),
+    (dict(pro=mx.PRO_DSWIGLU, aux=P6, C=96), SHAPE),  # F = C/2 must be a multiple of 32
+    (dict(x=P + 8), ALIGN), (dict(rs=P3 + 4), ALIGN), (dict(part=P6 + 2), ALIGN),
+    (dict(batch=70000), OVERFLOW),
+])
+def test_quantize_rejections(kw, want):
+    assert q(**kw) == want
+
+
+def test_quantize_valid_args_need_the_device():
+    # valid on the host; no gfx950 device here, so the library refuses
+    for kw in (dict(), dict(fmt=mx.E2M3, had=1), dict(fmt=mx.E4M3, mode=mx.RCEIL),
+               dict(fmt=mx.E4M3, mode=mx.FLOOR), dict(pro=mx.PRO_DGELU_TANH, aux=P6, part=P7, sum=P8),
+               dict(R=0), dict(cc=None, cs=None), dict(rc=None, rs=None, part=P7)):
+        st = q(**kw)
+        assert st in (OK, DEVICE), (kw, st)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def g(**kw):
+    a = dict(ac=P, as_=P2, bc=P3, bs=P4, M=256, N=512, K=768, fmt=mx.E2M3, bias=None, bt=mx.BF16, c=P5,
+             ct=mx.BF16, ldc=512)
+    a.update(kw)
+    return mx.lib().mx_gemm(a["ac"], a["as_"], a["bc"], a["bs"], a["M"], a["N"], a["K"], a["fmt"], a["bias"],
+                            a["bt"], a["c"], a["ct"], a["ldc"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(ac=None), NULL), (dict(bs=None), NULL), (dict(c=None), NULL),
+    (dict(fmt=5), FORMAT), (dict(bt=2), FORMAT), (dict(ct=3), FORMAT),
+    (dict(M=128), SHAPE), (dict(N=300), SHAPE), (dict(K=384), SHAPE), (dict(M=-256), SHAPE),
+    (dict(ldc=256), SHAPE), (dict(ldc=516), SHAPE),
+    (dict(ac=P + 4), ALIGN), (dict(c=P5 + 2), ALIGN), (dict(bias=P6 + 8), ALIGN),
+])
+def test_gemm_rejections(kw, want):
+    assert g(**kw) == want
+
+
+def test_gemm_valid_args_need_the_device():
+    for kw in (dict(), dict(bias=P6, bt=mx.F32, ct=mx.F32, ldc=1024), dict(M=0), dict(K=0)):
+        st = g(**kw)
+        assert st in (OK, DEVICE)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def grouped(**kw):
+    a = dict(mode=mx.RAGGED_M, epilogue=mx.EPI_NONE, fmt=mx.E4M3, scale_mode=mx.RCEIL, G=8,
+             validate_offsets=0, R=32768, M=0, N=2048, K=768, offsets=P, A=(P2, P3), B=(P4, P5), C=P6, aux=None,
+             out_row=(None, None), out_col=(None, None))
+    a.update(kw)
+    args = mx.GroupedArgs(a["mode"], a["epilogue"], a["fmt"], a["scale_mode"], a["G"], a["validate_offsets"],
+                          a["R"], a["M"], a["N"], a["K"], a["offsets"], mx.Packed(*a["A"]), mx.Packed(*a["B"]),
+                          a["C"], a["aux"], mx.Packed(*a["out_row"]), mx.Packed(*a["out_col"]))
+    return mx.lib().mx_grouped_gemm(ctypes.byref(args), None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(offsets=None), NULL), (dict(A=(P2, None)), NULL), (dict(C=None), NULL),
+    (dict(epilogue=mx.EPI_SWIGLU), NULL),                          # quantization outputs missing
+    (dict(epilogue=mx.EPI_DSWIGLU, C=None, out_row=(P7, P8), out_col=(P7, P8)), NULL),  # H missing
+    (dict(mode=2), FORMAT), (dict(epilogue=3), FORMAT), (dict(fmt=0), FORMAT),
+    (dict(mode=mx.RAGGED_K, epilogue=mx.EPI_SWIGLU, out_row=(P7, P8), out_col=(P7, P8)), FORMAT),
+    (dict(epilogue=mx.EPI_SWIGLU, fmt=mx.E2M1, scale_mode=mx.RCEIL, out_row=(P7, P8), out_col=(P7, P8)), FORMAT),
+    (dict(G=0), SHAPE), (dict(G=-1), SHAPE), (dict(R=1000), SHAPE), (dict(N=1000), SHAPE), (dict(K=100), SHAPE),
+    (dict(mode=mx.RAGGED_K, M=100, N=256), SHAPE),
+    (dict(offsets=P + 4), ALIGN), (dict(C=P6 + 2), ALIGN),
+])
+def test_grouped_rejections(kw, want):
+    assert grouped(**kw) == want
+
+
+def test_grouped_valid_args_need_the_device():
+    for kw in (dict(), dict(mode=mx.RAGGED_K, M=2048, N=768), dict(R=0),
+               dict(epilogue=mx.EPI_SWIGLU, N=1536, K=2048, out_row=(P7, P8), out_col=(P7, P8))):
+        st = grouped(**kw)
+        assert st in (OK, DEVICE)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def mlp_fwd_args(**kw):
+    base = dict(M=256, D=256, F=512, fmt=mx.E2M3, mode=mx.FLOOR, had=1)
+    base.update(kw)
+    packs = [mx.Packed(P * (10 + 2 * i), P * (11 + 2 * i)) for i in range(8)]
+    return mx.MlpFwdArgs(base["M"], base["D"], base["F"], base["fmt"], base["mode"], base["had"], 0,
+                         P, P2, None, P3, P4, P5, *packs)
+
+
+def test_fused_mlp_rejections():
+    L = mx.lib()
+    assert L.mx_fused_mlp_fwd(None, None) == NULL
+    assert L.mx_fused_mlp_fwd(ctypes.byref(mlp_fwd_args(M=100)), None) == SHAPE
+    assert L.mx_fused_mlp_fwd(ctypes.byref(mlp_fwd_args(fmt=mx.E2M1, had=1)), None) == FORMAT
+    a = mlp_fwd_args()
+    a.Xr = mx.Packed(None, None)
+    assert L.mx_fused_mlp_fwd(ctypes.byref(a), None) == NULL
+    a = mlp_fwd_args()
+    a.Y = P5 + 2
+    assert L.mx_fused_mlp_fwd(ctypes.byref(a), None) == ALIGN
+    st = L.mx_fused_mlp_fwd(ctypes.byref(mlp_fwd_args()), None)
+    assert st in (OK, DEVICE)
+    b = mx.MlpBwdArgs()
+    assert L.mx_fused_mlp_bwd(ctypes.byref(b), None) == NULL

@@ -1,0 +1,386 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: packed codes, scales and column sums bit-exact; GEMM outputs within
+max|gpu - ref| <= 2e-3 * max|ref| (ref = the oracle's unrounded binary64
+result; infinity-norm relative error, since elementwise relative error is
+ill-posed under cancellation), bf16 stores equal to nearest-even bf16 of
+the same kernel's fp32 store, and bitwise equality on exact-product
+constructions where every fp32 partial sum is exact.  Intermediate bf16
+tensors the fused paths keep (h, da, H) are fed to the oracle's packers so
+the packs can be compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from microscaling_block_scaled_mx_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+REL = 2e-3
+FMT_CASES = [(1, 0, False), (2, 0, True), (2, 0, False), (3, 1, False), (3, 0, False)]
+
+
+@pytest.fixture(scope="module")
+def mxl():
+    from microscaling_block_scaled_mx_amd import mx
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert mx.device_supported(0), "GPU tests need a gfx950 device"
+    return mx
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor, dtype=None) -> np.ndarray:
+    torch.cuda.synchronize()
+    a = t.cpu().numpy()
+    if t.dtype == torch.int16:
+        a = a.view(np.uint16)
+    return a if dtype is None else a.view(dtype)
+
+
+def bf16_empty(*shape):
+    return torch.empty(shape, dtype=torch.int16, device="cuda")
+
+
+def with_specials(x: np.ndarray, rng) -> np.ndarray:
+    """Inject NaN / Inf / zero / subnormal / huge blocks and values (bf16 bits)."""
+    x = x.copy()
+    R, C = x.shape
+    x[0, 0:32] = 0                      # all-zero block
+    x[0, 33] = 0x8000                   # a -0.0
+    x[1, 5] = 0x7FC0                    # NaN
+    x[2, 40] = 0x7F80                   # +Inf
+    x[3, 64:96] = 0x0001 + np.arange(32, dtype=np.uint16)  # subnormals only
+    x[4, 7] = 0x7F7F                    # largest finite
+    x[5, 96:128] = 0x0080               # smallest normal
+    x[35, 3] = 0xFF80                   # -Inf (second row block for the col pass)
+    return x
+
+
+def assert_packs_equal(got: dict, want: dict, fmt, keys):
+    for k in keys:
+        g, w = got[k], want[k]
+        assert g.shape == w.shape, (k, g.shape, w.shape)
+        if not np.array_equal(g, w):
+            bad = np.argwhere(g != w)
+            raise AssertionError(f"{k}: {len(bad)} mismatching bytes, first at {bad[:5].tolist()}")
+
+
+def assert_f32_bitwise(got: np.ndarray, want: np.ndarray):
+    """Bit-for-bit binary32 equality; NaN matches NaN (payload and sign of a
+    NaN carry no meaning)."""
+    g, w = got.view(np.uint32), want.view(np.uint32)
+    gn, wn = np.isnan(got), np.isnan(want)
+    np.testing.assert_array_equal(gn, wn)
+    np.testing.assert_array_equal(g[~gn], w[~wn])
+
+
+def gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, row=True, col=True, colsum=False, in_cols=None,
+                 batch=1):
+    xd = dev(x)
+    ad = dev(aux) if aux is not None else None
+    shp = (lambda r, k: (r, k) if batch == 1 else (batch, r, k))
+    rowp = colp = None
+    if row:
+        rowp = (torch.zeros(shp(R, C * mxl.BITS[fmt] // 8), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp(R, C // 32), dtype=torch.uint8, device="cuda"))
+    if col:
+        colp = (torch.zeros(shp(C, R * mxl.BITS[fmt] // 8), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp(C, R // 32), dtype=torch.uint8, device="cuda"))
+    part = sums = None
+    if colsum:
+        part = torch.zeros(shp(R // 32, C), dtype=torch.float32, device="cuda")
+        sums = torch.zeros((C,) if batch == 1 else (batch, C), dtype=torch.float32, device="cuda")
+    mxl.quantize(xd, R, C, fmt, mode, had, pro, aux=ad, row=rowp, col=colp, colsum_partials=part, colsum=sums,
+                 batch=batch)
+    out = {}
+    if row:
+        out["row_codes"], out["row_scales"] = host(rowp[0]), host(rowp[1])
+    if col:
+        out["col_codes"], out["col_scales"] = host(colp[0]), host(colp[1])
+    if colsum:
+        out["colsum_partials"], out["colsum"] = host(part), host(sums)
+    return out
+
+
+# ------------------------------------------------------------------ packer
+@pytest.mark.parametrize("fmt,mode,had", FMT_CASES)
+@pytest.mark.parametrize("pro", [0, 1, 2])
+def test_quantize_parity_identity_gelu_dgelu(mxl, orc, fmt, mode, had, pro):
+    rng = np.random.default_rng(100 + 10 * fmt + pro)
+    R, C = 96, 160  # ragged against the 64 x 128 tile
+    x = with_specials(I.bf16_normal(rng, (R, C), 2.0), rng)
+    aux = I.bf16_normal(rng, (R, C), 3.0) if pro == 2 else None
+    got = gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, colsum=True)
+    want = orc.quantize(x, R, C, fmt, mode, had, pro=pro, aux=aux, row=True, col=True, colsum=True)
+    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
+    assert_f32_bitwise(got["colsum"], want["colsum"])
+
+
+@pytest.mark.parametrize("fmt,mode", [(3, 1), (1, 0), (2, 0)])
+def test_quantize_parity_swiglu_dswiglu(mxl, orc, fmt, mode):
+    rng = np.random.default_rng(7 + fmt)
+    R, F = 160, 96
+    H = I.bf16_normal(rng, (R, 2 * F), 2.0)
+    H[0, 0] = 0x7FC0
+    got = gpu_quantize(mxl, H, None, R, F, fmt, mode, False, 3)
+    want = orc.quantize(H, R, F, fmt, mode, False, pro=3, row=True, col=True)
+    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    dz = I.bf16_normal(rng, (R, F), 1.0)
+    got = gpu_quantize(mxl, dz, H, R, 2 * F, fmt, mode, False, 4, colsum=True)
+    want = orc.quantize(dz, R, 2 * F, fmt, mode, False, pro=4, aux=H, row=True, col=True, colsum=True)
+    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_f32_bitwise(got["colsum"], want["colsum"])
+
+
+def test_quantize_batched(mxl, orc):
+    rng = np.random.default_rng(21)
+    B, R, C = 3, 64, 128
+    x = I.bf16_normal(rng, (B, R, C), 0.02)
+    got = gpu_quantize(mxl, x, None, R, C, 3, 1, False, 0, batch=B)
+    for b in range(B):
+        want = orc.quantize(x[b], R, C, 3, 1, row=True, col=True)
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+            assert np.array_equal(got[k][b], want[k]), (b, k)
+
+
+def test_quantize_zero_size_is_a_noop(mxl):
+    x = torch.zeros(1, dtype=torch.int16, device="cuda")
+    rc = torch.full((4,), 7, dtype=torch.uint8, device="cuda")
+    mxl.quantize(x, 0, 64, 1, 0, row=(rc, rc))
+    assert host(rc).tolist() == [7, 7, 7, 7]
+
+
+# ------------------------------------------------------------------ GEMM
+def gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed, bias=False):
+    rng = np.random.default_rng(seed)
+    A = I.bf16_normal(rng, (M, K), 1.0)
+    B = I.bf16_normal(rng, (N, K), 0.02)
+    b = I.bf16_normal(rng, (N,), 0.01) if bias else None
+    pa = orc.quantize(A, M, K, fmt, mode, had)
+    pb = orc.quantize(B, N, K, fmt, mode, had)
+    ref = orc.gemm(pa["row_codes"], pa["row_scales"], pb["row_codes"], pb["row_scales"], M, N, K, fmt, bias=b)
+    a = (dev(pa["row_codes"]), dev(pa["row_scales"]))
+    bb = (dev(pb["row_codes"]), dev(pb["row_scales"]))
+    c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    c16 = bf16_empty(M, N)
+    bd = dev(b) if b is not None else None
+    mxl.gemm(a, bb, M, N, K, fmt, c32, bias=bd, c_dtype=mxl.F32)
+    mxl.gemm(a, bb, M, N, K, fmt, c16, bias=bd, c_dtype=mxl.BF16)
+    return ref, host(c32), host(c16)
+
+
+@pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
+@pytest.mark.parametrize("shape", [(256, 256, 256), (384, 512, 768), (128 * 5, 256 * 3, 256 * 5)])
+def test_gemm_parity(mxl, orc, fmt, mode, had, shape):
+    M, N, K = shape
+    if M % 256:
+        M = 256 * ((M + 255) // 256)
+    ref, c32, c16 = gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed=M + N + K + fmt, bias=(K == 768))
+    err = np.max(np.abs(c32.astype(np.float64) - ref)) / np.max(np.abs(ref))
+    assert err <= REL, err
+    want16 = I.f32_to_bf16_bits(c32)
+    assert np.array_equal(c16, want16)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_gemm_exact_products_bitwise(mxl, orc, fmt):
+    # one shared scale per operand and codes whose products are multiples of
+    # a common unit well inside 2^24 units per dot product: every binary32
+    # partial sum is exact, so the GPU must equal the oracle to the bit.
+    rng = np.random.default_rng(50 + fmt)
+    M, N, K = 256, 256, 512
+    bits = {1: 4, 2: 6, 3: 8}[fmt]
+    vals = np.array([orc.decode(fmt, c) for c in range(1 << bits)])
+    ok = np.isfinite(vals) & (np.abs(vals) <= 8) & (np.abs(vals) >= (0.125 if fmt == 3 else 0))
+    if fmt == 3:
+        ok &= (np.abs(vals) * 8 == np.round(np.abs(vals) * 8))
+    allowed = np.nonzero(ok)[0]
+
+    def packed(rows):
+        codes = rng.choice(allowed, size=(rows, K))
+        raw = np.zeros((rows, K * bits // 8), np.uint8)
+        for r in range(rows):
+            acc = 0
+            for j, c in enumerate(codes[r]):
+                acc |= int(c) << (bits * j)
+            raw[r] = np.frombuffer(acc.to_bytes(K * bits // 8, "little"), np.uint8)
+        return raw, np.full((rows, K // 32), 127 + int(rng.integers(-3, 4)), np.uint8)
+    ac, asc = packed(M)
+    bc, bsc = packed(N)
+    ref = orc.gemm(ac, asc, bc, bsc, M, N, K, fmt)
+    c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mxl.gemm((dev(ac), dev(asc)), (dev(bc), dev(bsc)), M, N, K, fmt, c32, c_dtype=mxl.F32)
+    assert np.array_equal(host(c32).astype(np.float64), ref)
+
+
+def test_gemm_determinism(mxl, orc):
+    rng = np.random.default_rng(3)
+    M, N, K = 512, 512, 1024
+    A = I.bf16_normal(rng, (M, K))
+    B = I.bf16_normal(rng, (N, K), 0.02)
+    pa = (torch.empty((M, K * 3 // 4), dtype=torch.uint8, device="cuda"),
+          torch.empty((M, K // 32), dtype=torch.uint8, device="cuda"))
+    pb = (torch.empty((N, K * 3 // 4), dtype=torch.uint8, device="cuda"),
+          torch.empty((N, K // 32), dtype=torch.uint8, device="cuda"))
+    mxl.quantize(dev(A), M, K, 2, 0, True, row=pa)
+    mxl.quantize(dev(B), N, K, 2, 0, True, row=pb)
+    c1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    c2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mxl.gemm(pa, pb, M, N, K, 2, c1, c_dtype=mxl.F32)
+    mxl.gemm(pa, pb, M, N, K, 2, c2, c_dtype=mxl.F32)
+    assert np.array_equal(host(c1).view(np.uint32), host(c2).view(np.uint32))
+
+
+# ------------------------------------------------------------------ fused MLP
+def run_mlp(mxl, X, W1, b1, W2, dY, M, D, F, fmt=2, mode=0, had=True):
+    P = lambda r, k: mxl.alloc_packed(r, k, fmt)
+    t = dict(X=dev(X), W1=dev(W1), b1=dev(b1) if b1 is not None else None, W2=dev(W2), dY=dev(dY),
+             h=bf16_empty(M, F), Y=bf16_empty(M, D), Xr=P(M, D), Xc=P(D, M), W1r=P(F, D), W1c=P(D, F),
+             W2r=P(D, F), W2c=P(F, D), ar=P(M, F), ac=P(F, M), da=bf16_empty(M, F), dX=bf16_empty(M, D),
+             dW1=bf16_empty(F, D), dW2=bf16_empty(D, F), db1=torch.empty(F, dtype=torch.float32, device="cuda"),
+             part=torch.empty((M // 32, F), dtype=torch.float32, device="cuda"), dYr=P(M, D), dYc=P(D, M),
+             dhr=P(M, F), dhc=P(F, M))
+    mxl.fused_mlp_fwd(M, D, F, t["X"], t["W1"], t["b1"], t["W2"], t["h"], t["Y"], t["Xr"], t["Xc"], t["W1r"],
+                      t["W1c"], t["W2r"], t["W2c"], t["ar"], t["ac"], fmt=fmt, scale_mode=mode, hadamard=had)
+    mxl.fused_mlp_bwd(M, D, F, t["dY"], t["h"], t["Xc"], t["W1c"], t["W2c"], t["ac"], t["da"], t["dX"], t["dW1"],
+                      t["dW2"], t["db1"], t["part"], t["dYr"], t["dYc"], t["dhr"], t["dhc"], fmt=fmt,
+                      scale_mode=mode, hadamard=had)
+    return t
+
+
+def rel_err(got_bf16, ref64):
+    g = I.bf16_bits_to_f32(got_bf16).astype(np.float64)
+    return np.max(np.abs(g - ref64)) / max(np.max(np.abs(ref64)), 1e-300)
+
+
+def bf16_close(got_bf16, ref64):
+    """|gpu - ref| <= 2e-3 max|ref| + half a bf16 ulp of ref (one rounding of the store)."""
+    g = I.bf16_bits_to_f32(got_bf16).astype(np.float64)
+    half_ulp = np.abs(ref64) * 2.0 ** -8
+    return np.all(np.abs(g - ref64) <= REL * np.max(np.abs(ref64)) + half_ulp)
+
+
+def test_fused_mlp_parity_small(mxl, orc):
+    M, D, F = 256, 256, 512
+    X, W1, b1, W2, dY = I.mlp(302, M, D, F)
+    t = run_mlp(mxl, X, W1, b1, W2, dY, M, D, F)
+    h = host(t["h"])
+    fwd = orc.mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=h)
+    for name, key in (("Xr", "X"), ("W1r", "W1"), ("W2r", "W2")):
+        assert np.array_equal(host(t[name][0]), fwd[key]["row_codes"]), name
+        assert np.array_equal(host(t[name][1]), fwd[key]["row_scales"]), name
+    for name, key in (("Xc", "X"), ("W1c", "W1"), ("W2c", "W2")):
+        assert np.array_equal(host(t[name][0]), fwd[key]["col_codes"]), name
+        assert np.array_equal(host(t[name][1]), fwd[key]["col_scales"]), name
+    assert bf16_close(h, fwd["h64"])
+    # activation packs, bit-exact given the GPU's h
+    assert np.array_equal(host(t["ar"][0]), fwd["a"]["row_codes"])
+    assert np.array_equal(host(t["ar"][1]), fwd["a"]["row_scales"])
+    assert np.array_equal(host(t["ac"][0]), fwd["a"]["col_codes"])
+    assert np.array_equal(host(t["ac"][1]), fwd["a"]["col_scales"])
+    assert bf16_close(host(t["Y"]), fwd["Y64"])
+    da = host(t["da"])
+    bwd = orc.mlp_bwd_ref(dY, fwd, M, D, F, da_in=da, h_in=h)
+    assert bf16_close(da, bwd["da64"])
+    assert np.array_equal(host(t["dhr"][0]), bwd["dh"]["row_codes"])
+    assert np.array_equal(host(t["dhc"][0]), bwd["dh"]["col_codes"])
+    assert np.array_equal(host(t["dhc"][1]), bwd["dh"]["col_scales"])
+    assert np.array_equal(host(t["db1"]).view(np.uint32), bwd["db1"].view(np.uint32))
+    assert bf16_close(host(t["dX"]), bwd["dX64"])
+    assert bf16_close(host(t["dW1"]), bwd["dW1_64"])
+    assert bf16_close(host(t["dW2"]), bwd["dW2_64"])
+
+
+def test_fused_mlp_zero_output_projection(mxl):
+    M, D, F = 256, 256, 256
+    X, W1, b1, W2, dY = I.mlp(303, M, D, F)
+    W2 = np.zeros_like(W2)
+    t = run_mlp(mxl, X, W1, b1, W2, dY, M, D, F)
+    for k in ("Y", "da", "dX", "dW1"):
+        assert not np.any(host(t[k]) & 0x7FFF), k
+    assert not np.any(host(t["db1"]))
+    assert np.any(host(t["dW2"]) & 0x7FFF)
+
+
+# ------------------------------------------------------------------ grouped
+def run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G):
+    fmt, mode = 3, 1
+    P = lambda r, k, b=None: mxl.alloc_packed(r, k, fmt, batch=b)
+    off = dev(offsets.astype(np.int32))
+    t = dict(Xr=P(R, D), Xc=P(D, R), W1r=P(2 * F, D, G), W1c=P(D, 2 * F, G), W2r=P(D, F, G), W2c=P(F, D, G),
+             H=bf16_empty(R, 2 * F), zr=P(R, F), zc=P(F, R), Y=bf16_empty(R, D), dYr=P(R, D), dYc=P(D, R),
+             dz=bf16_empty(R, F), dHr=P(R, 2 * F), dHc=P(2 * F, R), dX=bf16_empty(R, D),
+             dW1=bf16_empty(G, 2 * F, D), dW2=bf16_empty(G, D, F))
+    Xd, W1d, W2d, dYd = dev(X), dev(W1), dev(W2), dev(dY)
+    mxl.quantize(Xd, R, D, fmt, mode, row=t["Xr"], col=t["Xc"])
+    mxl.quantize(W1d, 2 * F, D, fmt, mode, row=t["W1r"], col=t["W1c"], batch=G)
+    mxl.quantize(W2d, D, F, fmt, mode, row=t["W2r"], col=t["W2c"], batch=G)
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["Xr"], t["W1r"], t["H"], epilogue=mxl.EPI_SWIGLU, N=2 * F, K=D,
+                     out_row=t["zr"], out_col=t["zc"], validate_offsets=True)
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["zr"], t["W2r"], t["Y"], N=D, K=F)
+    mxl.quantize(dYd, R, D, fmt, mode, row=t["dYr"], col=t["dYc"])
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["dYr"], t["W2c"], t["dz"], epilogue=mxl.EPI_DSWIGLU, N=F, K=D,
+                     aux=t["H"], out_row=t["dHr"], out_col=t["dHc"])
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["dHr"], t["W1c"], t["dX"], N=D, K=2 * F)
+    mxl.grouped_gemm(mxl.RAGGED_K, G, R, off, t["dYc"], t["zc"], t["dW2"], M=D, N=F)
+    mxl.grouped_gemm(mxl.RAGGED_K, G, R, off, t["dHc"], t["Xc"], t["dW1"], M=2 * F, N=D)
+    return t
+
+
+def test_grouped_parity_small(mxl, orc):
+    R, D, F, G = 1024, 256, 256, 4
+    counts, offsets, X, W1, W2, dY = I.grouped_mlp(502, R, D, F, G, zero_expert=2)
+    t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G)
+    H = host(t["H"])
+    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H)
+    assert bf16_close(H, fwd["H64"])
+    assert np.array_equal(host(t["zr"][0]), fwd["z"]["row_codes"])
+    assert np.array_equal(host(t["zr"][1]), fwd["z"]["row_scales"])
+    assert np.array_equal(host(t["zc"][0]), fwd["z"]["col_codes"])
+    assert np.array_equal(host(t["zc"][1]), fwd["z"]["col_scales"])
+    assert bf16_close(host(t["Y"]), fwd["Y64"])
+    dz = host(t["dz"])
+    bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=dz, H_in=H)
+    assert bf16_close(dz, bwd["dz64"])
+    assert np.array_equal(host(t["dHr"][0]), bwd["dH"]["row_codes"])
+    assert np.array_equal(host(t["dHr"][1]), bwd["dH"]["row_scales"])
+    assert np.array_equal(host(t["dHc"][0]), bwd["dH"]["col_codes"])
+    assert np.array_equal(host(t["dHc"][1]), bwd["dH"]["col_scales"])
+    assert bf16_close(host(t["dX"]), bwd["dX64"])
+    dW1, dW2 = host(t["dW1"]), host(t["dW2"])
+    assert not np.any(dW1[2]) and not np.any(dW2[2])  # zero-token expert: zeros written
+    assert bf16_close(dW1, bwd["dW1_64"])
+    assert bf16_close(dW2, bwd["dW2_64"])
+
+
+def test_grouped_inactive_tail_untouched(mxl, orc):
+    # offsets[-1] < R: rows past the last group end are neither read nor written
+    R, D, F, G = 1024, 256, 128, 2
+    rng = np.random.default_rng(9)
+    offsets = np.array([256, 640], np.int32)
+    X = I.bf16_normal(rng, (R, D))
+    X[640:] = 0x7FC0  # NaN-poisoned tail: must never be read
+    W1 = I.bf16_normal(rng, (G, 2 * F, D), 0.02)
+    fmt = 3
+    xr = mxl.alloc_packed(R, D, fmt)
+    mxl.quantize(dev(X), R, D, fmt, 1, row=xr)
+    w1r = mxl.alloc_packed(2 * F, D, fmt, batch=G)
+    mxl.quantize(dev(W1), 2 * F, D, fmt, 1, row=w1r, batch=G)
+    H = torch.full((R, 2 * F), 0x1234, dtype=torch.int16, device="cuda")
+    zr = (torch.full((R, F), 0xAB, dtype=torch.uint8, device="cuda"),
+          torch.full((R, F // 32), 0xAB, dtype=torch.uint8, device="cuda"))
+    zc = (torch.full((F, R), 0xAB, dtype=torch.uint8, device="cuda"),
+          torch.full((F, R // 32), 0xAB, dtype=torch.uint8, device="cuda"))
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, dev(offsets), xr, w1r, H, epilogue=mxl.EPI_SWIGLU, N=2 * F, K=D,
+                     out_row=zr, out_col=zc)
+    Hh = host(H)
+    assert np.all(Hh[640:] == 0x1234) and not np.any(Hh[:640] == 0x1234)
+    assert np.all(host(zr[0])[640:] == 0xAB) and np.all(host(zc[0])[:, 640:] == 0xAB)
+    assert not np.any(np.isnan(I.bf16_bits_to_f32(Hh[:640])))
