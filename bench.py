@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the MX quantize-and-GEMM hot path on one MI355X.
+
+Headline step (the workload the metric is quoted on): the MXFP6 (E2M3,
+FLOOR scales, Hadamard-32 along K) linear at the Flux-12B attention
+projection shape -- X [4096, 3072] ~N(0,1), W [3072, 3072] ~N(0,0.02),
+dY [4096, 3072] ~N(0,1), bf16 -- one step = dual (row + column) packs of X,
+W and dY, then forward Y = X W^T, dgrad dX = dY W and wgrad dW = dY^T X
+(K = 4096 tokens), bf16 outputs.  value = 3 * 2*M*N*K / step time
+(TFLOP/s), inputs resident in HBM; four copies of the inputs are rotated so
+that a step does not find its inputs in the 256 MB Infinity Cache.
+
+The same JSON line carries the per-kernel times (HIP events on the stream
+the kernels run on), the roofline of the dominant kernel (the GEMM), the
+CPU oracle timed on a bounded sample, and -- unless --extra none -- the
+other workloads of the metric: the 256^3 MXFP4 parity GEMM, the fused
+MXFP6 MLP at M=8192 (3072 -> 12288 -> 3072), the MXFP4 sweep over the five
+Flux-12B block linears at M=16384 and the MXFP8 grouped SwiGLU MLP
+(G=8, D=2048, F=768, R=32768).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--extra all|none] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quantizer GB/s"
+PEAK_TFLOPS = {"fp4": 10100.0, "fp6": 10100.0, "fp8": 5000.0}  # MI355X dense MFMA
+HBM_GBS = 8000.0
+# algorithmic bytes per element of a pack: 2 B bf16 in + (bits/8 + 1/32) per output axis
+PACK_OUT = {4: 0.5 + 1 / 32, 6: 0.75 + 1 / 32, 8: 1.0 + 1 / 32}
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+class Timer:
+    """Per-launch HIP events on the current stream, aggregated by name."""
+
+    def __init__(self):
+        self.rec = []
+        self.on = False
+
+    def run(self, name, fn, *a, **kw):
+        import torch
+        if not self.on:
+            return fn(*a, **kw)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn(*a, **kw)
+        e.record()
+        self.rec.append((name, s, e))
+        return out
+
+    def summary(self):
+        import torch
+        torch.cuda.synchronize()
+        agg = {}
+        for name, s, e in self.rec:
+            agg.setdefault(name, []).append(s.elapsed_time(e) * 1e3)  # us
+        self.rec = []
+        return {k: float(np.mean(v)) for k, v in agg.items()}
+
+
+# ------------------------------------------------------------------ headline: MX linear
+class LinearStep:
+    def __init__(self, mx, M, N, K, fmt, mode, had, seed, copies=4, rng_inputs=None):
+        from microscaling_block_scaled_mx_amd import inputs as I
+        import torch
+        self.mx, self.M, self.N, self.K, self.fmt, self.mode, self.had = mx, M, N, K, fmt, mode, had
+        X, W, dY = rng_inputs if rng_inputs is not None else I.linear(seed, M, N, K)
+        self.host = (X, W, dY)
+        self.inp = [(dev(X), dev(W), dev(dY)) for _ in range(copies)]
+        P = lambda r, k: mx.alloc_packed(r, k, fmt)
+        self.Xr, self.Xc, self.Wr, self.Wc, self.dYr, self.dYc = P(M, K), P(K, M), P(N, K), P(K, N), P(M, N), P(N, M)
+        e16 = lambda *s: torch.empty(s, dtype=torch.int16, device="cuda")
+        self.Y, self.dX, self.dW = e16(M, N), e16(M, K), e16(N, K)
+
+    def run(self, i, T):
+        mx, M, N, K, f, m, h = self.mx, self.M, self.N, self.K, self.fmt, self.mode, self.had
+        X, W, dY = self.inp[i % len(self.inp)]
+        T.run("pack_X", mx.quantize, X, M, K, f, m, h, row=self.Xr, col=self.Xc)
+        T.run("pack_W", mx.quantize, W, N, K, f, m, h, row=self.Wr, col=self.Wc)
+        T.run("pack_dY", mx.quantize, dY, M, N, f, m, h, row=self.dYr, col=self.dYc)
+        T.run("gemm_fwd", mx.gemm, self.Xr, self.Wr, M, N, K, f, self.Y)
+        T.run("gemm_dgrad", mx.gemm, self.dYr, self.Wc, M, K, N, f, self.dX)
+        T.run("gemm_wgrad", mx.gemm, self.dYc, self.Xc, N, K, M, f, self.dW)
+
+    def flops(self):
+        return 3 * 2.0 * self.M * self.N * self.K
+
+
+def time_steps(fn, steps, warmup, T):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    T.on = True
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    T.on = False
+    return dt / steps
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(step: LinearStep, rows=1024):
+    """The oracle (never tuned for this) on the host cores: full dual packs of
+    X, W, dY plus `rows` output rows of each GEMM; the full-step time is
+    extrapolated from the sampled rows."""
+    from oracle import oracle as orc
+    X, W, dY = step.host
+    M, N, K, f, m, h = step.M, step.N, step.K, step.fmt, step.mode, step.had
+    t0 = time.perf_counter()
+    px = orc.quantize(X, M, K, f, m, h, row=True, col=True)
+    pw = orc.quantize(W, N, K, f, m, h, row=True, col=True)
+    pd = orc.quantize(dY, M, N, f, m, h, row=True, col=True)
+    t_pack = time.perf_counter() - t0
+    t_gemm = 0.0
+    # (A operand, B operand, M, N, K) of the fwd, dgrad and wgrad GEMMs
+    gemms = ((px, "row", pw, "row", M, N, K), (pd, "row", pw, "col", M, K, N), (pd, "col", px, "col", N, K, M))
+    for pa, sa, pb, sb, MM, NN, KK in gemms:
+        r = min(rows, MM)
+        t1 = time.perf_counter()
+        orc.gemm(pa[sa + "_codes"], pa[sa + "_scales"], pb[sb + "_codes"], pb[sb + "_scales"], MM, NN, KK, f,
+                 rows=np.arange(r))
+        t_gemm += (time.perf_counter() - t1) * (MM / r)
+    total = t_pack + t_gemm
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": step.flops() / total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"full dual packs of X, W, dY ({t_pack:.1f} s) + {rows} output rows of each of the 3 GEMMs, "
+                      f"GEMM time scaled to all rows; step estimate {total:.1f} s",
+            "seconds_measured": round(time.perf_counter() - t0, 2)}
+
+
+# ------------------------------------------------------------------ other workloads
+def bench_cfg1(mx, T, iters=20):
+    import torch
+    from microscaling_block_scaled_mx_amd import inputs as I
+    A, B = I.gemm_pair(101, 256, 256, 256)
+    Ad, Bd = dev(A), dev(B)
+    pa, pb = mx.alloc_packed(256, 256, mx.E2M1), mx.alloc_packed(256, 256, mx.E2M1)
+    C = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+
+    def one(i):
+        T.run("c1_pack", mx.quantize, Ad, 256, 256, mx.E2M1, mx.FLOOR, row=pa)
+        T.run("c1_pack", mx.quantize, Bd, 256, 256, mx.E2M1, mx.FLOOR, row=pb)
+        T.run("c1_gemm", mx.gemm, pa, pb, 256, 256, 256, mx.E2M1, C, c_dtype=mx.F32)
+    sec = time_steps(one, iters, 5, T)
+    k = T.summary()
+    return {"workload": "MXFP4 quantize + GEMM 256^3, fp32 C", "us_per_step": sec * 1e6,
+            "gemm_us": k["c1_gemm"], "pack_us": k["c1_pack"]}
+
+
+def bench_cfg3(mx, T, iters=5):
+    import torch
+    from microscaling_block_scaled_mx_amd import inputs as I
+    M, D, F = 8192, 3072, 12288
+    X, W1, b1, W2, dY = I.mlp(301, M, D, F)
+    P = lambda r, k: mx.alloc_packed(r, k, mx.E2M3)
+    e16 = lambda *s: torch.empty(s, dtype=torch.int16, device="cuda")
+    t = dict(X=dev(X), W1=dev(W1), b1=dev(b1), W2=dev(W2), dY=dev(dY), h=e16(M, F), Y=e16(M, D), Xr=P(M, D),
+             Xc=P(D, M), W1r=P(F, D), W1c=P(D, F), W2r=P(D, F), W2c=P(F, D), ar=P(M, F), ac=P(F, M),
+             da=e16(M, F), dX=e16(M, D), dW1=e16(F, D), dW2=e16(D, F),
+             db1=torch.empty(F, dtype=torch.float32, device="cuda"),
+             part=torch.empty((M // 32, F), dtype=torch.float32, device="cuda"), dYr=P(M, D), dYc=P(D, M),
+             dhr=P(M, F), dhc=P(F, M))
+
+    def one(i):
+        T.run("c3_fwd", mx.fused_mlp_fwd, M, D, F, t["X"], t["W1"], t["b1"], t["W2"], t["h"], t["Y"], t["Xr"],
+              t["Xc"], t["W1r"], t["W1c"], t["W2r"], t["W2c"], t["ar"], t["ac"])
+        T.run("c3_bwd", mx.fused_mlp_bwd, M, D, F, t["dY"], t["h"], t["Xc"], t["W1c"], t["W2c"], t["ac"], t["da"],
+              t["dX"], t["dW1"], t["dW2"], t["db1"], t["part"], t["dYr"], t["dYc"], t["dhr"], t["dhc"])
+    sec = time_steps(one, iters, 2, T)
+    k = T.summary()
+    fl = 6 * 2.0 * M * D * F
+    return {"workload": "fused MXFP6 MLP M=8192 3072->12288->3072 tanh-GELU fwd+bwd (+db1)",
+            "ms_per_step": sec * 1e3, "fwd_ms": k["c3_fwd"] / 1e3, "bwd_ms": k["c3_bwd"] / 1e3,
+            "tflops": fl / sec / 1e12, "frac_of_fp6_peak": fl / sec / 1e12 / PEAK_TFLOPS["fp6"]}
+
+
+def bench_cfg4(mx, T, iters=3):
+    import torch
+    from microscaling_block_scaled_mx_amd import inputs as I
+    out = {"workload": "MXFP4 Flux-12B block linears at M=16384, fwd+dgrad+wgrad", "linears": {}}
+    tot_fl = tot_gemm_us = tot_us = 0.0
+    for i, (name, K, N) in enumerate(I.FLUX_LINEARS):
+        st = LinearStep(mx, 16384, N, K, mx.E2M1, mx.FLOOR, False, 401 + i, copies=1)
+        sec = time_steps(lambda j: st.run(j, T), iters, 1, T)
+        k = T.summary()
+        g = k["gemm_fwd"] + k["gemm_dgrad"] + k["gemm_wgrad"]
+        fl = st.flops()
+        out["linears"][name] = {"K": K, "N": N, "gemm_us": g, "step_us": sec * 1e6,
+                                "gemm_tflops": fl / (g * 1e-6) / 1e12}
+        tot_fl += fl
+        tot_gemm_us += g
+        tot_us += sec * 1e6
+        del st
+        torch.cuda.empty_cache()
+    out["gemm_tflops"] = tot_fl / (tot_gemm_us * 1e-6) / 1e12
+    out["frac_of_fp4_peak"] = out["gemm_tflops"] / PEAK_TFLOPS["fp4"]
+    out["step_tflops"] = tot_fl / (tot_us * 1e-6) / 1e12
+    return out
+
+
+def bench_cfg5(mx, T, iters=5):
+    import torch
+    from microscaling_block_scaled_mx_amd import inputs as I
+    R, D, F, G = 32768, 2048, 768, 8
+    counts, offsets, X, W1, W2, dY = I.grouped_mlp(501, R, D, F, G)
+    fmt, mode = mx.E4M3, mx.RCEIL
+    P = lambda r, k, b=None: mx.alloc_packed(r, k, fmt, batch=b)
+    e16 = lambda *s: torch.empty(s, dtype=torch.int16, device="cuda")
+    t = dict(X=dev(X), W1=dev(W1), W2=dev(W2), dY=dev(dY), off=dev(offsets.astype(np.int32)), Xr=P(R, D),
+             Xc=P(D, R), W1r=P(2 * F, D, G), W1c=P(D, 2 * F, G), W2r=P(D, F, G), W2c=P(F, D, G), H=e16(R, 2 * F),
+             zr=P(R, F), zc=P(F, R), Y=e16(R, D), dYr=P(R, D), dYc=P(D, R), dHr=P(R, 2 * F), dHc=P(2 * F, R),
+             dX=e16(R, D), dW1=e16(G, 2 * F, D), dW2=e16(G, D, F))
+
+    def one(i):
+        T.run("c5_pack", mx.quantize, t["X"], R, D, fmt, mode, row=t["Xr"], col=t["Xc"])
+        T.run("c5_pack", mx.quantize, t["W1"], 2 * F, D, fmt, mode, row=t["W1r"], col=t["W1c"], batch=G)
+        T.run("c5_pack", mx.quantize, t["W2"], D, F, fmt, mode, row=t["W2r"], col=t["W2c"], batch=G)
+        T.run("c5_fc1_swiglu", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["Xr"], t["W1r"], t["H"],
+              epilogue=mx.EPI_SWIGLU, N=2 * F, K=D, out_row=t["zr"], out_col=t["zc"])
+        T.run("c5_fc2", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["zr"], t["W2r"], t["Y"], N=D, K=F)
+        T.run("c5_pack", mx.quantize, t["dY"], R, D, fmt, mode, row=t["dYr"], col=t["dYc"])
+        T.run("c5_fc2_dgrad_dswiglu", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["dYr"], t["W2c"], None,
+              epilogue=mx.EPI_DSWIGLU, N=F, K=D, aux=t["H"], out_row=t["dHr"], out_col=t["dHc"])
+        T.run("c5_fc1_dgrad", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["dHr"], t["W1c"], t["dX"], N=D,
+              K=2 * F)
+        T.run("c5_wgrad2", mx.grouped_gemm, mx.RAGGED_K, G, R, t["off"], t["dYc"], t["zc"], t["dW2"], M=D, N=F)
+        T.run("c5_wgrad1", mx.grouped_gemm, mx.RAGGED_K, G, R, t["off"], t["dHc"], t["Xc"], t["dW1"], M=2 * F, N=D)
+    sec = time_steps(one, iters, 2, T)
+    k = T.summary()
+    fl = 2.0 * R * D * F * (2 + 1 + 1 + 2 + 1 + 2)
+    gemm_us = sum(v for n, v in k.items() if n != "c5_pack")
+    out = {"workload": "MXFP8 grouped SwiGLU MLP G=8 D=2048 F=768 R=32768 (one empty expert), fwd+bwd",
+           "counts": [int(c) for c in counts], "ms_per_step": sec * 1e3, "step_tflops": fl / sec / 1e12,
+           "gemm_tflops": fl / (gemm_us * 1e-6) / 1e12, "kernels_us": k}
+    out["frac_of_fp8_peak"] = out["gemm_tflops"] / PEAK_TFLOPS["fp8"]
+    return out
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extra", choices=["all", "none"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
+              "kernels on its own shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from microscaling_block_scaled_mx_amd import mx
+    if not torch.cuda.is_available() or not mx.device_supported(0):
+        print("bench.py needs a gfx950 GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    T = Timer()
+    M, N, K = 4096, 3072, 3072
+    step = LinearStep(mx, M, N, K, mx.E2M3, mx.FLOOR, True, 201)
+    print(f"[bench] linear MXFP6 {M}x{N}x{K}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    sec = time_steps(lambda i: step.run(i, T), args.steps, args.warmup, T)
+    k = T.summary()
+    value = step.flops() / sec / 1e12
+    gemm_us = float(np.mean([k["gemm_fwd"], k["gemm_dgrad"], k["gemm_wgrad"]]))
+    gemm_flops = 2.0 * M * N * K
+    achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
+    pack_bytes = M * K * (2 + 2 * PACK_OUT[6])
+    kernels = {n: {"us": round(v, 2)} for n, v in k.items()}
+    for n in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
+        kernels[n]["tflops"] = round(gemm_flops / (k[n] * 1e-6) / 1e12, 1)
+    for n, (r, c) in (("pack_X", (M, K)), ("pack_W", (N, K)), ("pack_dY", (M, N))):
+        kernels[n]["gbs"] = round(r * c * (2 + 2 * PACK_OUT[6]) / (k[n] * 1e-6) / 1e9, 1)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp6 (e2m3 x e2m3, fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "MXFP6 linear (E2M3, FLOOR, Hadamard-32) X[4096,3072] W[3072,3072]: dual packs "
+                               "of X, W, dY + fwd, dgrad, wgrad GEMMs, bf16 out",
+                   "M": M, "N": N, "K": K, "format": "mxfp6", "gemm_flops_per_step": step.flops()},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<E2M3> (fwd/dgrad/wgrad launches, 77.3 GFLOP each)",
+                     "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp6"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": None},
+        "quantizer": {"kernel": "pack_kernel<E2M3, Hadamard> dual pack of X", "achieved_gbs":
+                      round(pack_bytes / (k["pack_X"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
+                      "frac": round(pack_bytes / (k["pack_X"] * 1e-6) / 1e9 / HBM_GBS, 4)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(step)
+    if args.extra == "all":
+        extra = {}
+        for name, fn in (("mxfp4_256", bench_cfg1), ("fused_mlp_mxfp6", bench_cfg3), ("mxfp4_flux_sweep", bench_cfg4),
+                         ("grouped_mxfp8", bench_cfg5)):
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            extra[name] = fn(mx, T)
+            torch.cuda.empty_cache()
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
