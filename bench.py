@@ -257,6 +257,38 @@ def bench_cfg5(mx, T, iters=5):
     return out
 
 
+def only(mx, spec, steps, warmup, T):
+    """One kernel configuration, for profilers: gemm:FMT:M:N:K or pack:FMT:R:C
+    (dual pack).  Prints one JSON line with its average time."""
+    import torch
+    from microscaling_block_scaled_mx_amd import inputs as I
+    kind, fbits, *dims = spec.split(":")
+    fmt = {"4": mx.E2M1, "6": mx.E2M3, "8": mx.E4M3}[fbits]
+    mode = mx.RCEIL if fmt == mx.E4M3 else mx.FLOOR
+    had = fmt == mx.E2M3
+    if kind == "gemm":
+        M, N, K = (int(v) for v in dims)
+        A, B = I.gemm_pair(7, M, N, K, 1.0, 0.02)
+        pa, pb = mx.alloc_packed(M, K, fmt), mx.alloc_packed(N, K, fmt)
+        mx.quantize(dev(A), M, K, fmt, mode, had, row=pa)
+        mx.quantize(dev(B), N, K, fmt, mode, had, row=pb)
+        C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        sec = time_steps(lambda i: T.run("gemm", mx.gemm, pa, pb, M, N, K, fmt, C), steps, warmup, T)
+        us = T.summary()["gemm"]
+        print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12,
+                          "ms_per_iter": sec * 1e3}), flush=True)
+    else:
+        R, C = (int(v) for v in dims)
+        X = dev(I.bf16_normal(np.random.default_rng(7), (R, C)))
+        row, col = mx.alloc_packed(R, C, fmt), mx.alloc_packed(C, R, fmt)
+        sec = time_steps(lambda i: T.run("pack", mx.quantize, X, R, C, fmt, mode, had, row=row, col=col),
+                         steps, warmup, T)
+        us = T.summary()["pack"]
+        b = R * C * (2 + 2 * PACK_OUT[int(fbits)])
+        print(json.dumps({"only": spec, "us": us, "gbs": b / (us * 1e-6) / 1e9, "ms_per_iter": sec * 1e3}),
+              flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -265,6 +297,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extra", choices=["all", "none"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="profile one kernel config instead: gemm:FMT:M:N:K or pack:FMT:R:C (FMT = 4, 6 or 8)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
@@ -278,6 +312,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     T = Timer()
+    if args.only:
+        only(mx, args.only, args.steps, args.warmup, T)
+        return
     M, N, K = 4096, 3072, 3072
     step = LinearStep(mx, M, N, K, mx.E2M3, mx.FLOOR, True, 201)
     print(f"[bench] linear MXFP6 {M}x{N}x{K}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,

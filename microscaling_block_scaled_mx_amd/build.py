@@ -50,6 +50,11 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # every kernel launched from host code must have its host stub in the library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    missing = [ln for ln in nm.splitlines() if "mx" in ln and "device_stub" in ln]
+    if missing:
+        raise RuntimeError("libmx.so has unresolved kernel stubs:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

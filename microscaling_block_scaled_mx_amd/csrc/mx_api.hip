@@ -68,6 +68,12 @@ bool grid_fits(int64_t x, int64_t y, int64_t z) {
   return x >= 0 && y >= 0 && z >= 0 && x < (1ll << 31) && y <= 65535 * 1024ll && z <= 65535;
 }
 
+// the GEMM kernels address an operand with 32-bit byte offsets
+constexpr int64_t kMaxOperandBytes = (1ll << 31) - 1;
+bool operand_fits(int fmt, int64_t rows, int64_t k) {
+  return rows * (k * bits_of(fmt) / 8) <= kMaxOperandBytes;
+}
+
 // ---------------------------------------------------------------- quantize
 int validate_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt, int mode,
                       int had, int pro, const void* rc, const void* rs, const void* cc, const void* cs,
@@ -122,6 +128,7 @@ int validate_gemm(const void* ac, const void* as, const void* bc, const void* bs
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MX_ERR_ALIGN;
   if (!grid_fits(N / 256, M / 128, 1)) return MX_ERR_INDEX_OVERFLOW;
+  if (!operand_fits(fmt, M, K) || !operand_fits(fmt, N, K)) return MX_ERR_INDEX_OVERFLOW;
   return MX_OK;
 }
 
@@ -287,6 +294,10 @@ int mx_grouped_gemm(const mx_grouped_args* a, void* stream) {
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MX_ERR_ALIGN;
   if (!grid_fits(a->N / 128 + 1, a->R / 128 + a->M / 128, a->G)) return MX_ERR_INDEX_OVERFLOW;
+  if (a->mode == MX_GROUPED_RAGGED_M
+          ? (!operand_fits(a->fmt, a->R, a->K) || !operand_fits(a->fmt, (int64_t)a->G * a->N, a->K))
+          : (!operand_fits(a->fmt, a->M, a->R) || !operand_fits(a->fmt, a->N, a->R)))
+    return MX_ERR_INDEX_OVERFLOW;
   int st = check_device();
   if (st != MX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -167,19 +167,17 @@ __device__ __forceinline__ uint32_t quant_block(const float (&v)[32], uint32_t (
 }
 
 // ------------------------------------------------------------------ LDS tiles
-// A bf16 tile in LDS, row-major with `pitch` bytes per row.
-// Row block: 32 consecutive bf16 of one row (16-byte aligned start).
+// A bf16 tile in LDS, row-major with `pitch` bytes per row (a multiple of 8).
+// Row block: 32 consecutive bf16 of one row (8-byte aligned start).
 __device__ __forceinline__ void lds_row_block(const uint8_t* tile, int pitch, int row, int col0, float (&v)[32]) {
-  const uint4* src = reinterpret_cast<const uint4*>(tile + row * pitch + col0 * 2);
+  const uint2* src = reinterpret_cast<const uint2*>(tile + row * pitch + col0 * 2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint4 q = src[j];
-    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[8 * j + 2 * k] = bf16_lo(ws[k]);
-      v[8 * j + 2 * k + 1] = bf16_hi(ws[k]);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const uint2 q = src[j];
+    v[4 * j + 0] = bf16_lo(q.x);
+    v[4 * j + 1] = bf16_hi(q.x);
+    v[4 * j + 2] = bf16_lo(q.y);
+    v[4 * j + 3] = bf16_hi(q.y);
   }
 }
 // Column block: rows row0..row0+31 of one column.

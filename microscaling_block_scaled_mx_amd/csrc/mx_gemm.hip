@@ -7,7 +7,7 @@
 //      store epilogue into the fp32 accumulator (description, commit
 //      messages).
 // [P3] "MXFP4 training for Flux models": MXFP4 GEMM, NT layout
-//      (Troubleshooting).
+//      (Troubleshooting); 256x256 tiles at the Flux QKV shape (Tuned GEMMs).
 // [P4] "MXFP8 cudnn-fe Swiglu fused Grouped MLP fwd/bwd and wgrad group
 //      gemm": ragged grouped GEMM with the expert picked from the tile
 //      coordinate (counts are multiples of 128, so no tile straddles two
@@ -15,20 +15,35 @@
 //      columnwise 32x1 in the same launch, ragged-K weight gradient writing
 //      zeros for empty experts (commit messages).
 //
-// Tiling.  512 threads = 8 wavefronts in a 2 (M) x 4 (N) grid over a
-// BM x 256 output tile (BM = 256 or 128); each wavefront owns a
-// (BM/2) x 64 sub-tile = (BM/64) x 2 MFMA tiles of 32 x 32.  K advances 128
-// elements per stage; A and B stages sit in LDS (row pitch = stage bytes +
-// 16, which spreads consecutive rows over distinct LDS banks for the 16-byte
-// operand reads), double-buffered, with the next stage's global loads in
-// flight while the current one is multiplied.
+// Tiling.  256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN output
+// tile; a wavefront owns (BM/2) x (BN/2) = (BM/64) x (BN/64) MFMA tiles of
+// 32 x 32, whose accumulators live in AGPRs (one wavefront per SIMD).  K
+// advances BK elements per stage (128 for E2M1/E2M3, 64 for E4M3).  Stages
+// form a ring of S buffers in LDS filled by direct global -> LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane), so
+// S - 1 stages are in flight while one is multiplied and no registers are
+// spent on staging.  A stage's rows are stored densely; the 16-byte chunks
+// of each row are permuted (XOR for E2M1 / E4M3, a rotation for E2M3's six
+// chunks) so that the 32 rows one operand read touches spread over all LDS
+// banks.  The loads of a stage are awaited with an explicit vmcnt, then one
+// barrier per stage publishes it to all wavefronts and frees the buffer that
+// the next issue overwrites.
+//
+// Dense tiles are ordered for cache reuse: workgroups are dealt round-robin
+// to the 8 XCDs (each with its own L2), so consecutive workgroup ids are
+// remapped to give every XCD a contiguous range of tiles, and each range is
+// walked in groups of 8 tile rows so that concurrent tiles share A and B
+// panels.
 //
 // MFMA operand layout (measured): lane l holds row l%32 of A (of B) and the
 // 32-element K block g = l/32 of the 64-element step.  E2M1 / E2M3 take the
 // block's 32 codes contiguously (16 / 24 bytes); E4M3 takes K [16g, 16g+16)
 // in bytes 0-15 and [32+16g, 32+16g+16) in bytes 16-31.  The lane's scale
-// operand is the E8M0 byte of (its row, block g).  The 16 accumulators of
-// lane l hold C rows 8*(i/4) + 4*(l/32) + i%4, column l%32.
+// operand is the E8M0 byte of (its row, block g).  The instruction computes
+// X . Y^T with lane l's 16 accumulators holding rows 8*(i/4) + 4*(l/32) + i%4,
+// column l%32; the kernel passes the B fragment as X and the A fragment as
+// Y, so a lane holds C row l%32 and the four consecutive columns
+// 8*(i/4) + 4*(l/32) + {0..3} for each i/4 -- 8 contiguous bytes of bf16.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -41,76 +56,176 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 512;
-constexpr int kBK = 128;
-constexpr int kBN = 256;
+constexpr int kThreads = 256;
 
 template <int FMT> struct MfmaFmt;
 template <> struct MfmaFmt<kE4M3> { static constexpr int kCode = 0; };
 template <> struct MfmaFmt<kE2M3> { static constexpr int kCode = 2; };
 template <> struct MfmaFmt<kE2M1> { static constexpr int kCode = 4; };
 
-template <int FMT, int BM, int EPI>
+template <int FMT, int BM, int BN, int MODE, int EPI>
 struct Cfg {
   static constexpr int kBits = FmtTraits<FMT>::kBits;
-  static constexpr int kRowBytes = kBK * kBits / 8;  // 64 / 96 / 128
-  static constexpr int kPitch = kRowBytes + 16;
-  static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row per stage
+  // K elements per stage: whole 128-byte row segments for E2M1 (dense mode,
+  // where K is a multiple of 256) and E4M3; the grouped modes only promise
+  // multiples of 128
+  static constexpr int kBK = (FMT == kE2M1 && MODE == kDense) ? 256 : 128;
+  static constexpr int kRowBytes = kBK * kBits / 8;      // 128 / 96 / 128 bytes per row per stage
+  static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
+  static constexpr int kScaleDw = kBK / 128;             // scale dwords (4 blocks each) per row per stage
   static constexpr int kAOff = 0;
-  static constexpr int kBOff = BM * kPitch;
-  static constexpr int kASOff = kBOff + kBN * kPitch;
-  static constexpr int kBSOff = kASOff + BM * 4;
-  static constexpr int kStage = kBSOff + kBN * 4;
-  static constexpr int kMI = BM / 64;  // MFMA tiles per wavefront along M
-  static constexpr int kNJ = 2;        // along N
-  static constexpr int kAIters = (BM * kChunks + kThreads - 1) / kThreads;
-  static constexpr int kBIters = (kBN * kChunks + kThreads - 1) / kThreads;
+  static constexpr int kBOff = BM * kRowBytes;
+  static constexpr int kSOff = kBOff + BN * kRowBytes;   // scale dwords: [dword][A rows, then B rows] (512 slots)
+  static constexpr int kStage = kSOff + kScaleDw * 512 * 4;
+  static constexpr int kStages = (4 * kStage <= 160 * 1024) ? 4 : ((3 * kStage <= 160 * 1024) ? 3 : 2);
+  static constexpr int kWM = BM / 2, kWN = BN / 2;
+  static constexpr int kMI = kWM / 32, kNJ = kWN / 32;
+  static constexpr int kAIters = BM * kChunks / kThreads;  // 16-byte loads per thread per stage
+  static constexpr int kBIters = BN * kChunks / kThreads;
+  static constexpr int kLoads = kAIters + kBIters + 2 * kScaleDw;  // vector-memory instructions per stage per wave
+  static_assert(BM * kChunks % kThreads == 0 && BN * kChunks % kThreads == 0, "tile / thread mismatch");
+  static_assert(BM + BN <= 512, "scale slots");
   // epilogue staging
-  static constexpr int kZPitch = 128 * 2 + 16;  // SwiGLU: z tile BM x 128 bf16
-  static constexpr int kDPitch = kBN * 2 + 16;  // dSwiGLU: two BM x 256 bf16 tiles
-  static constexpr int kEpiBytes = EPI == kEpiSwiglu ? BM * kZPitch : (EPI == kEpiDSwiglu ? 2 * BM * kDPitch : 0);
-  static constexpr int kSmem = (2 * kStage > kEpiBytes) ? 2 * kStage : kEpiBytes;
+  static constexpr int kCPitch = kWN * 2 + 8;         // bf16 store: per-wave kWM x kWN tile
+  static constexpr int kZPitch = (BN / 2) * 2 + 8;    // SwiGLU: z tile BM x BN/2
+  static constexpr int kDPitch = BN * 2 + 8;          // dSwiGLU: two BM x BN tiles
+  static constexpr int kEpiBytes = EPI == kEpiSwiglu    ? BM * kZPitch
+                                   : EPI == kEpiDSwiglu ? 2 * BM * kDPitch
+                                                        : 4 * kWM * kCPitch;
+  static constexpr int kSmem = (kStages * kStage > kEpiBytes) ? kStages * kStage : kEpiBytes;
+  static_assert(kSmem <= 163840, "LDS budget");
 };
 
-// Read one lane's A/B operand for K step ks (0 or 1) of the stage from a row
-// of the LDS tile.
-template <int FMT>
-__device__ __forceinline__ v8i lds_operand(const uint8_t* rowp, int ks, int g) {
-  v8i r;
-  if constexpr (FMT == kE4M3) {
-    const v4i a = *reinterpret_cast<const v4i*>(rowp + ks * 64 + 16 * g);
-    const v4i b = *reinterpret_cast<const v4i*>(rowp + ks * 64 + 32 + 16 * g);
-    r = v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  } else if constexpr (FMT == kE2M1) {
-    const v4i a = *reinterpret_cast<const v4i*>(rowp + ks * 32 + 16 * g);
-    r = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-  } else {
-    const uint8_t* q = rowp + ks * 48 + 24 * g;
-    const v2i a = *reinterpret_cast<const v2i*>(q);
-    const v2i b = *reinterpret_cast<const v2i*>(q + 8);
-    const v2i c = *reinterpret_cast<const v2i*>(q + 16);
-    r = v8i{a.x, a.y, b.x, b.y, c.x, c.y, 0, 0};
-  }
-  return r;
+// Position of logical 16-byte chunk c of row r among the row's NCH stored
+// chunks, chosen so that the same chunk of 8 (16) consecutive rows falls in
+// distinct LDS banks:  NCH = 8: c ^ ((r ^ (r >> 3)) & 7);  NCH = 4:
+// c ^ (((r >> 1) ^ (r >> 3)) & 3);  NCH = 6: (c + ((r >> 2) & 1)) % 6.
+template <int NCH>
+__device__ __forceinline__ int chunk_pos(int r, int c) {
+  static_assert(NCH == 4 || NCH == 6 || NCH == 8, "chunks per row");
+  if constexpr (NCH == 6) { const int q = c + ((r >> 2) & 1); return q >= 6 ? q - 6 : q; }
+  else if constexpr (NCH == 8) return c ^ ((r ^ (r >> 3)) & 7);
+  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+// Inverse: the logical chunk stored at position pos of row r.
+template <int NCH>
+__device__ __forceinline__ int chunk_at(int r, int pos) {
+  if constexpr (NCH == 6) { const int q = pos - ((r >> 2) & 1); return q < 0 ? q + 6 : q; }
+  else return chunk_pos<NCH>(r, pos);  // the XOR permutations are involutions
 }
 
-template <int FMT, int BM, int MODE, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-  using CF = Cfg<FMT, BM, EPI>;
+// The intrinsics below exist only for the GPU; their bodies are compiled in
+// the device pass alone, so the host pass sees plain declarations.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  // s_waitcnt: vmcnt[3:0] + vmcnt[5:4] at bits 15:14; expcnt (7) and lgkmcnt (15) left unconstrained
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
+
+// Workgroup barrier without a memory fence (the stage loads are awaited
+// explicitly with vmcnt); the empty asm keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#endif
+}
+
+// Direct global -> LDS copy of 16 (4) bytes per lane: lane l's bytes land at
+// lds + 16 * l (lds + 4 * l); lds must be the same for the whole wavefront.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+#endif
+}
+
+// Keep the machine scheduler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+__device__ __forceinline__ int wave_uniform(int v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_readfirstlane(v);
+#else
+  return v;
+#endif
+}
+
+// Read one lane's A/B operand for K step ks of the stage from row r of the
+// LDS tile (row base rowp); g = lane / 32 picks the 32-element K block.
+template <int FMT, int NCH>
+__device__ __forceinline__ v8i lds_operand(const uint8_t* rowp, int r, int ks, int g) {
+  v8i v;
+  if constexpr (FMT == kE4M3) {  // chunks 4 ks + g and 4 ks + 2 + g
+    const v4i a = *reinterpret_cast<const v4i*>(rowp + 16 * chunk_pos<NCH>(r, 4 * ks + g));
+    const v4i b = *reinterpret_cast<const v4i*>(rowp + 16 * chunk_pos<NCH>(r, 4 * ks + 2 + g));
+    v = v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  } else if constexpr (FMT == kE2M1) {  // chunk 2 ks + g
+    const v4i a = *reinterpret_cast<const v4i*>(rowp + 16 * chunk_pos<NCH>(r, 2 * ks + g));
+    v = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  } else {  // 24 bytes = 8-byte pieces 6 ks + 3 g + {0, 1, 2}
+    v2i q[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int piece = 6 * ks + 3 * g + k;
+      q[k] = *reinterpret_cast<const v2i*>(rowp + 16 * chunk_pos<NCH>(r, piece >> 1) + 8 * (piece & 1));
+    }
+    v = v8i{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, 0, 0};
+  }
+  return v;
+}
+
+// Dense tile order: XCD-contiguous ranges, then groups of 8 tile rows.
+__device__ __forceinline__ void dense_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  if ((T & 7) == 0) bid = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * GM;
+  const int gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int r = bid - group * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+template <int FMT, int BM, int BN, int MODE, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+  using CF = Cfg<FMT, BM, BN, MODE, EPI>;
   constexpr int kBits = CF::kBits;
   __shared__ __attribute__((aligned(16))) uint8_t smem[CF::kSmem];
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int lrow = lane & 31, g = lane >> 5;
 
   // ---------------------------------------------------------------- tile
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;  // SwiGLU: blockIdx.x indexes 128-column z blocks
+  int tm, tn;
+  if constexpr (MODE == kDense) {
+    dense_tile(blockIdx.x, (int)(p.M / BM), (int)(p.N / BN), tm, tn);
+  } else {
+    tn = blockIdx.x;
+    tm = blockIdx.y;
+  }
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;  // SwiGLU: tile tn covers z columns [tn*BN/2, (tn+1)*BN/2)
   int64_t kbeg = 0, kend = p.K;
-  int64_t b_row0 = 0;           // first B row of this tile's group
-  int64_t c_off = 0;            // element offset of this tile's group in C
+  int64_t b_row0 = 0;  // first B row of this tile's group
+  int64_t c_off = 0;   // element offset of this tile's group in C
   if constexpr (MODE == kRaggedM) {
     // offsets are a caller invariant; clamping keeps every access inside the
     // buffers even if it is broken
@@ -132,69 +247,62 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   }
   const int64_t row_bytes = p.ktot * kBits / 8;
   const int64_t srow = p.ktot / 32;
-  const int nk = (int)((kend - kbeg) / kBK);
+  const int nk = (int)((kend - kbeg) / CF::kBK);
 
   // LDS row r of the B tile -> global B row
   auto b_row = [&](int r) -> int64_t {
     if constexpr (EPI == kEpiSwiglu) {
-      const int64_t zb = (int64_t)blockIdx.x * 128;
-      return b_row0 + (r < 128 ? zb + r : p.F + zb + (r - 128));
+      const int64_t zb = (int64_t)tn * (BN / 2);
+      return b_row0 + (r < BN / 2 ? zb + r : p.F + zb + (r - BN / 2));
     } else {
       return b_row0 + n0 + r;
     }
   };
 
   // ---------------------------------------------------------------- loads
-  uint4 ra[CF::kAIters], rb[CF::kBIters];
-  uint32_t rs = 0;
-  auto gload = [&](int64_t k0) {
-    const int64_t kb = k0 * kBits / 8;
+  // Stage slot s (16-byte units, s = i * 256 + t for load i of thread t)
+  // holds row s / kChunks, position s % kChunks, i.e. logical chunk
+  // chunk_at(row, position).  Byte offsets are 32-bit (operands < 2 GiB).
+  constexpr int BK = CF::kBK;
+  uint32_t a_off[CF::kAIters], b_off[CF::kBIters];
 #pragma unroll
-    for (int i = 0; i < CF::kAIters; ++i) {
-      const int q = t + kThreads * i;
-      if (q < BM * CF::kChunks) {
-        const int r = q / CF::kChunks, ch = q % CF::kChunks;
-        ra[i] = *reinterpret_cast<const uint4*>(p.a_codes + (m0 + r) * row_bytes + kb + ch * 16);
-      }
-    }
+  for (int i = 0; i < CF::kAIters; ++i) {
+    const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
+    a_off[i] = (uint32_t)((m0 + r) * row_bytes + 16 * chunk_at<CF::kChunks>(r, pos));
+  }
 #pragma unroll
-    for (int i = 0; i < CF::kBIters; ++i) {
-      const int q = t + kThreads * i;
-      if (q < kBN * CF::kChunks) {
-        const int r = q / CF::kChunks, ch = q % CF::kChunks;
-        rb[i] = *reinterpret_cast<const uint4*>(p.b_codes + b_row(r) * row_bytes + kb + ch * 16);
-      }
-    }
-    if (t < BM) {
-      rs = *reinterpret_cast<const uint32_t*>(p.a_scales + (m0 + t) * srow + k0 / 32);
-    } else if (t < BM + kBN) {
-      rs = *reinterpret_cast<const uint32_t*>(p.b_scales + b_row(t - BM) * srow + k0 / 32);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* s = smem + buf * CF::kStage;
+  for (int i = 0; i < CF::kBIters; ++i) {
+    const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
+    b_off[i] = (uint32_t)(b_row(r) * row_bytes + 16 * chunk_at<CF::kChunks>(r, pos));
+  }
+  // scale dwords (4 blocks of 32 along K): slot t and t + 256 of [A rows | B rows];
+  // slots past BM + BN load row 0's scales into unused slots, so every wave
+  // issues the same number of loads
+  const uint8_t* s_src[2];
 #pragma unroll
-    for (int i = 0; i < CF::kAIters; ++i) {
-      const int q = t + kThreads * i;
-      if (q < BM * CF::kChunks) {
-        const int r = q / CF::kChunks, ch = q % CF::kChunks;
-        *reinterpret_cast<uint4*>(s + CF::kAOff + r * CF::kPitch + ch * 16) = ra[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CF::kBIters; ++i) {
-      const int q = t + kThreads * i;
-      if (q < kBN * CF::kChunks) {
-        const int r = q / CF::kChunks, ch = q % CF::kChunks;
-        *reinterpret_cast<uint4*>(s + CF::kBOff + r * CF::kPitch + ch * 16) = rb[i];
-      }
-    }
-    if (t < BM) {
-      *reinterpret_cast<uint32_t*>(s + CF::kASOff + t * 4) = rs;
-    } else if (t < BM + kBN) {
-      *reinterpret_cast<uint32_t*>(s + CF::kBSOff + (t - BM) * 4) = rs;
-    }
-  };
+  for (int j = 0; j < 2; ++j) {
+    const int r = t + 256 * j;
+    s_src[j] = r < BM ? p.a_scales + (m0 + r) * srow
+                      : (r < BM + BN ? p.b_scales + b_row(r - BM) * srow : p.a_scales + m0 * srow);
+  }
+  const int wave_u = wave_uniform(wave);
+
+  // issue the loads of stage k into ring buffer buf
+#define MX_ISSUE(k, buf)                                                                                  \
+  do {                                                                                                   \
+    const int64_t k0_ = kbeg + (int64_t)(k) * BK;                                                        \
+    const uint8_t* ga_ = p.a_codes + k0_ * kBits / 8;                                                    \
+    const uint8_t* gb_ = p.b_codes + k0_ * kBits / 8;                                                    \
+    uint8_t* st_ = smem + (buf) * CF::kStage;                                                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < CF::kAIters; ++i_)                                           \
+      lds_dma16(ga_ + a_off[i_], st_ + CF::kAOff + (i_ * 256 + wave_u * 64) * 16);                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < CF::kBIters; ++i_)                                           \
+      lds_dma16(gb_ + b_off[i_], st_ + CF::kBOff + (i_ * 256 + wave_u * 64) * 16);                      \
+    const int64_t ks_ = (k0_ & ~(int64_t)127) / 32;                                                      \
+    _Pragma("unroll") for (int d_ = 0; d_ < CF::kScaleDw; ++d_)                                          \
+    _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                                                     \
+      lds_dma4(s_src[j_] + ks_ + 4 * d_, st_ + CF::kSOff + (d_ * 512 + j_ * 256 + wave_u * 64) * 4);     \
+  } while (0)
 
   // ---------------------------------------------------------------- main loop
   v16f acc[CF::kMI][CF::kNJ];
@@ -208,92 +316,171 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // LDS rows this lane reads
   int arow[CF::kMI], brow[CF::kNJ];
 #pragma unroll
-  for (int i = 0; i < CF::kMI; ++i) arow[i] = wm * (BM / 2) + 32 * i + lrow;
+  for (int i = 0; i < CF::kMI; ++i) arow[i] = wm * CF::kWM + 32 * i + lrow;
 #pragma unroll
-  for (int j = 0; j < CF::kNJ; ++j)
-    brow[j] = (EPI == kEpiSwiglu) ? (128 * j + 32 * wn + lrow) : (64 * wn + 32 * j + lrow);
-
-  if (nk > 0) {
-    gload(kbeg);
-    lstore(0);
-    __syncthreads();
+  for (int j = 0; j < CF::kNJ; ++j) {
+    if constexpr (EPI == kEpiSwiglu) {  // j < NJ/2: gate columns, j >= NJ/2: the matching up columns
+      constexpr int H = CF::kNJ / 2;
+      brow[j] = (j < H ? 0 : BN / 2) + wn * (CF::kWN / 2) + 32 * (j % H) + lrow;
+    } else {
+      brow[j] = wn * CF::kWN + 32 * j + lrow;
+    }
   }
+
+  constexpr int S = CF::kStages;
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) MX_ISSUE(st, st);
   for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) gload(kbeg + (int64_t)(it + 1) * kBK);
-    const uint8_t* s = smem + cur * CF::kStage;
+    if (it + S - 2 < nk) wait_vmcnt<CF::kLoads * (S - 2)>();  // stage it landed (this wave's part)
+    else wait_vmcnt<0>();
+    stage_barrier();  // ... and every wave's; buffer (it - 1) % S is free again
+    if (it + S - 1 < nk) MX_ISSUE(it + S - 1, (it + S - 1) % S);
+    const uint8_t* sb = smem + (it % S) * CF::kStage;
+    // Scale dwords of this lane's rows (one per 128 K), read once per stage.
+    uint32_t sda[CF::kScaleDw][CF::kMI], sdb[CF::kScaleDw][CF::kNJ];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8i af[CF::kMI], bf[CF::kNJ];
-      int sa[CF::kMI], sb[CF::kNJ];
+    for (int d = 0; d < CF::kScaleDw; ++d) {
 #pragma unroll
-      for (int i = 0; i < CF::kMI; ++i) {
-        af[i] = lds_operand<FMT>(s + CF::kAOff + arow[i] * CF::kPitch, ks, g);
-        sa[i] = (int)(*reinterpret_cast<const uint32_t*>(s + CF::kASOff + arow[i] * 4) >> (8 * (2 * ks + g)));
+      for (int i = 0; i < CF::kMI; ++i)
+        sda[d][i] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + arow[i]) * 4);
+#pragma unroll
+      for (int j = 0; j < CF::kNJ; ++j)
+        sdb[d][j] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + BM + brow[j]) * 4);
+    }
+    sched_fence();
+    // Operand fragments double-buffered in registers: the reads of K step
+    // ks + 1 are in flight while the MFMAs of step ks run.
+    constexpr int KS = BK / 64;
+    v8i af[2][CF::kMI], bf[2][CF::kNJ];
+#pragma unroll
+    for (int i = 0; i < CF::kMI; ++i) af[0][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], 0, g);
+#pragma unroll
+    for (int j = 0; j < CF::kNJ; ++j) bf[0][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], 0, g);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cb = ks & 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < CF::kMI; ++i)
+          af[cb ^ 1][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], ks + 1, g);
+#pragma unroll
+        for (int j = 0; j < CF::kNJ; ++j)
+          bf[cb ^ 1][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], ks + 1, g);
       }
+      sched_fence();  // the reads above are issued before the MFMAs below
+      // E8M0 byte of K block 2 ks + g of the stage (k0 % 128 == 0 at every stage start)
+      const int bi = 2 * ks;
+      int sa[CF::kMI], sbs[CF::kNJ];
 #pragma unroll
-      for (int j = 0; j < CF::kNJ; ++j) {
-        bf[j] = lds_operand<FMT>(s + CF::kBOff + brow[j] * CF::kPitch, ks, g);
-        sb[j] = (int)(*reinterpret_cast<const uint32_t*>(s + CF::kBSOff + brow[j] * 4) >> (8 * (2 * ks + g)));
-      }
+      for (int i = 0; i < CF::kMI; ++i) sa[i] = (int)(sda[bi >> 2][i] >> (8 * ((bi & 3) + g)));
+#pragma unroll
+      for (int j = 0; j < CF::kNJ; ++j) sbs[j] = (int)(sdb[bi >> 2][j] >> (8 * ((bi & 3) + g)));
 #pragma unroll
       for (int i = 0; i < CF::kMI; ++i)
 #pragma unroll
         for (int j = 0; j < CF::kNJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[i], bf[j], acc[i][j], MfmaFmt<FMT>::kCode, MfmaFmt<FMT>::kCode, 0, sa[i], 0, sb[j]);
+              bf[cb][j], af[cb][i], acc[i][j], MfmaFmt<FMT>::kCode, MfmaFmt<FMT>::kCode, 0, sbs[j], 0, sa[i]);
+      sched_fence();
     }
-    if (it + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
   }
+#undef MX_ISSUE
+  __syncthreads();  // all wavefronts are done with the stage ring before the epilogue reuses LDS
 
   // ---------------------------------------------------------------- epilogues
+  // Lane (row lrow, column group q = 8 * (e / 4) + 4 * g) of MFMA tile (i, j)
+  // holds acc[i][j][4 * (e / 4) + 0..3] = C[row][col + 0..3].
   if constexpr (EPI == kEpiStore) {
+    const uint16_t* bias16 = reinterpret_cast<const uint16_t*>(p.bias);
+    const float* bias32 = reinterpret_cast<const float*>(p.bias);
+    if (p.c_f32) {
+      float* C = reinterpret_cast<float*>(p.c) + c_off;
 #pragma unroll
-    for (int j = 0; j < CF::kNJ; ++j) {
-      const int64_t n = n0 + 64 * wn + 32 * j + lrow;
-      float bias = 0.0f;
-      if (p.bias) {
-        bias = p.bias_f32 ? reinterpret_cast<const float*>(p.bias)[n]
-                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(p.bias)[n]);
-      }
+      for (int i = 0; i < CF::kMI; ++i)
 #pragma unroll
-      for (int i = 0; i < CF::kMI; ++i) {
+        for (int j = 0; j < CF::kNJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t m = m0 + wm * (BM / 2) + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
-          const float v = acc[i][j][e] + bias;
-          const int64_t idx = c_off + m * p.ldc + n;
-          if (p.c_f32) reinterpret_cast<float*>(p.c)[idx] = v;
-          else reinterpret_cast<uint16_t*>(p.c)[idx] = (uint16_t)f32_to_bf16(v);
-        }
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int64_t m = m0 + wm * CF::kWM + 32 * i + lrow;
+            const int64_t n = n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float b = 0.0f;
+              if (p.bias) b = p.bias_f32 ? bias32[n + q] : bf16_to_f32(bias16[n + q]);
+              v[q] = acc[i][j][4 * e4 + q] + b;
+            }
+            *reinterpret_cast<float4*>(C + m * p.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+    } else {
+      // bf16: stage the wavefront's tile in LDS with 8-byte writes, then
+      // write 16-byte row chunks
+      uint8_t* wt = smem + wave * CF::kWM * CF::kCPitch;
+#pragma unroll
+      for (int i = 0; i < CF::kMI; ++i)
+#pragma unroll
+        for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int r = 32 * i + lrow, cl = 32 * j + 8 * e4 + 4 * g;
+            const int64_t n = n0 + wn * CF::kWN + cl;
+            uint32_t h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float b = 0.0f;
+              if (p.bias) b = p.bias_f32 ? bias32[n + q] : bf16_to_f32(bias16[n + q]);
+              h[q] = f32_to_bf16(acc[i][j][4 * e4 + q] + b);
+            }
+            *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          }
+      __syncthreads();
+      uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + c_off;
+      constexpr int kRowChunks = CF::kWN / 8;
+#pragma unroll 4
+      for (int q = lane; q < CF::kWM * kRowChunks; q += 64) {
+        const int r = q / kRowChunks, ch = q % kRowChunks;
+        const uint2 lo = *reinterpret_cast<const uint2*>(wt + r * CF::kCPitch + ch * 16);
+        const uint2 hi = *reinterpret_cast<const uint2*>(wt + r * CF::kCPitch + ch * 16 + 8);
+        const int64_t m = m0 + wm * CF::kWM + r;
+        *reinterpret_cast<uint4*>(C + m * p.ldc + n0 + wn * CF::kWN + ch * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     }
   } else if constexpr (EPI == kEpiSwiglu) {
-    // Lane holds gate (j = 0) and up (j = 1) of the same (row, z column).
+    // Lane holds gate (j < NJ/2) and up (j + NJ/2) of the same (row, z columns).
     // H [R][2F] is stored; z = SwiGLU(bf16 gate, bf16 up) goes to LDS only.
+    constexpr int H2 = CF::kNJ / 2;
     uint8_t* zt = smem;
-    const int64_t zb = (int64_t)blockIdx.x * 128;
-    const int zc = 32 * wn + lrow;
-    uint16_t* H = reinterpret_cast<uint16_t*>(p.c);
+    const int64_t zb = (int64_t)tn * (BN / 2);
+    uint16_t* Hc = reinterpret_cast<uint16_t*>(p.c);
 #pragma unroll
-    for (int i = 0; i < CF::kMI; ++i) {
+    for (int i = 0; i < CF::kMI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int ml = wm * (BM / 2) + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
-        const int64_t m = m0 + ml;
-        const float hg = round_bf16(acc[i][0][e]);
-        const float hu = round_bf16(acc[i][1][e]);
-        H[m * 2 * p.F + zb + zc] = (uint16_t)f32_to_bf16(hg);
-        H[m * 2 * p.F + p.F + zb + zc] = (uint16_t)f32_to_bf16(hu);
-        reinterpret_cast<uint16_t*>(zt + ml * CF::kZPitch)[zc] = (uint16_t)f32_to_bf16(swiglu_bf16(hg, hu));
-      }
-    }
+      for (int j = 0; j < H2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int ml = wm * CF::kWM + 32 * i + lrow;
+          const int zc = wn * (CF::kWN / 2) + 32 * j + 8 * e4 + 4 * g;
+          const int64_t m = m0 + ml;
+          uint32_t hg[4], hu[4], z[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g0 = round_bf16(acc[i][j][4 * e4 + q]);
+            const float u0 = round_bf16(acc[i][j + H2][4 * e4 + q]);
+            hg[q] = f32_to_bf16(g0);
+            hu[q] = f32_to_bf16(u0);
+            z[q] = f32_to_bf16(swiglu_bf16(g0, u0));
+          }
+          *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + zb + zc) = make_uint2(hg[0] | (hg[1] << 16), hg[2] | (hg[3] << 16));
+          *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + p.F + zb + zc) =
+              make_uint2(hu[0] | (hu[1] << 16), hu[2] | (hu[3] << 16));
+          *reinterpret_cast<uint2*>(zt + ml * CF::kZPitch + zc * 2) = make_uint2(z[0] | (z[1] << 16), z[2] | (z[3] << 16));
+        }
     __syncthreads();
     constexpr int QB = FmtTraits<FMT>::kBits;
-    // row blocks: BM rows x 4 blocks of 32 z columns
-    for (int q = t; q < BM * 4; q += kThreads) {
-      const int row = q >> 2, blk = q & 3;
+    constexpr int ZC = BN / 2;  // z columns in the tile
+    for (int q = t; q < BM * (ZC / 32); q += kThreads) {
+      const int row = q / (ZC / 32), blk = q % (ZC / 32);
       float v[32];
       lds_row_block(zt, CF::kZPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = zb + 32 * blk;
@@ -304,9 +491,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         quant_store<FMT, kFloor, 0>(v, p.q_row_codes + m * (p.F * QB / 8) + col * QB / 8,
                                     p.q_row_scales + m * (p.F / 32) + col / 32);
     }
-    // column blocks: 128 z columns x BM/32 row blocks (transposed operand)
-    for (int q = t; q < 128 * (BM / 32); q += kThreads) {
-      const int col = q & 127, rb2 = q >> 7;
+    for (int q = t; q < ZC * (BM / 32); q += kThreads) {
+      const int col = q % ZC, rb2 = q / ZC;
       float v[32];
       lds_col_block(zt, CF::kZPitch, rb2 * 32, col, v);
       const int64_t cz = zb + col, m = m0 + 32 * rb2;
@@ -323,30 +509,38 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     uint8_t* tu = smem + BM * CF::kDPitch;
     const uint16_t* H = p.aux;
 #pragma unroll
-    for (int j = 0; j < CF::kNJ; ++j) {
-      const int nl = 64 * wn + 32 * j + lrow;
-      const int64_t n = n0 + nl;
+    for (int j = 0; j < CF::kNJ; ++j)
 #pragma unroll
-      for (int i = 0; i < CF::kMI; ++i) {
+      for (int i = 0; i < CF::kMI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int ml = wm * (BM / 2) + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
-          const int64_t m = m0 + ml;
-          const float dz = round_bf16(acc[i][j][e]);
-          if (p.c) reinterpret_cast<uint16_t*>(p.c)[m * p.F + n] = (uint16_t)f32_to_bf16(dz);
-          const float gv = bf16_to_f32(H[m * 2 * p.F + n]);
-          const float uv = bf16_to_f32(H[m * 2 * p.F + p.F + n]);
-          reinterpret_cast<uint16_t*>(tg + ml * CF::kDPitch)[nl] = (uint16_t)f32_to_bf16(dswiglu_gate_bf16(dz, gv, uv));
-          reinterpret_cast<uint16_t*>(tu + ml * CF::kDPitch)[nl] = (uint16_t)f32_to_bf16(dswiglu_up_bf16(dz, gv));
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int ml = wm * CF::kWM + 32 * i + lrow;
+          const int nl = wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
+          const int64_t m = m0 + ml, n = n0 + nl;
+          const uint2 gw = *reinterpret_cast<const uint2*>(H + m * 2 * p.F + n);
+          const uint2 uw = *reinterpret_cast<const uint2*>(H + m * 2 * p.F + p.F + n);
+          const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+          const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
+          uint32_t dzb[4], dg[4], du[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float dz = round_bf16(acc[i][j][4 * e4 + q]);
+            dzb[q] = f32_to_bf16(dz);
+            dg[q] = f32_to_bf16(dswiglu_gate_bf16(dz, gv[q], uv[q]));
+            du[q] = f32_to_bf16(dswiglu_up_bf16(dz, gv[q]));
+          }
+          if (p.c)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.F + n) =
+                make_uint2(dzb[0] | (dzb[1] << 16), dzb[2] | (dzb[3] << 16));
+          *reinterpret_cast<uint2*>(tg + ml * CF::kDPitch + nl * 2) = make_uint2(dg[0] | (dg[1] << 16), dg[2] | (dg[3] << 16));
+          *reinterpret_cast<uint2*>(tu + ml * CF::kDPitch + nl * 2) = make_uint2(du[0] | (du[1] << 16), du[2] | (du[3] << 16));
         }
-      }
-    }
     __syncthreads();
     constexpr int QB = FmtTraits<FMT>::kBits;
     const int64_t W = 2 * p.F;  // dH width
-    for (int q = t; q < 2 * BM * 8; q += kThreads) {
-      const int half = q / (BM * 8), rq = q % (BM * 8);
-      const int row = rq >> 3, blk = rq & 7;
+    for (int q = t; q < 2 * BM * (BN / 32); q += kThreads) {
+      const int half = q / (BM * (BN / 32)), rq = q % (BM * (BN / 32));
+      const int row = rq / (BN / 32), blk = rq % (BN / 32);
       float v[32];
       lds_row_block(half ? tu : tg, CF::kDPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = (half ? p.F : 0) + n0 + 32 * blk;
@@ -357,9 +551,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         quant_store<FMT, kFloor, 0>(v, p.q_row_codes + m * (W * QB / 8) + col * QB / 8,
                                     p.q_row_scales + m * (W / 32) + col / 32);
     }
-    for (int q = t; q < 2 * kBN * (BM / 32); q += kThreads) {
-      const int half = q / (kBN * (BM / 32)), cq = q % (kBN * (BM / 32));
-      const int col = cq % kBN, rb2 = cq / kBN;
+    for (int q = t; q < 2 * BN * (BM / 32); q += kThreads) {
+      const int half = q / (BN * (BM / 32)), cq = q % (BN * (BM / 32));
+      const int col = cq % BN, rb2 = cq / BN;
       float v[32];
       lds_col_block(half ? tu : tg, CF::kDPitch, rb2 * 32, col, v);
       const int64_t cw = (half ? p.F : 0) + n0 + col, m = m0 + 32 * rb2;
@@ -373,31 +567,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   }
 }
 
-template <int FMT, int BM, int MODE, int EPI>
+template <int FMT, int BM, int BN, int MODE, int EPI>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   dim3 grid;
   if (MODE == kDense) {
-    grid = dim3((unsigned)(p.N / kBN), (unsigned)(p.M / BM), 1);
+    grid = dim3((unsigned)((p.M / BM) * (p.N / BN)), 1, 1);
   } else if (MODE == kRaggedM) {
-    const unsigned nt = EPI == kEpiSwiglu ? (unsigned)(p.F / 128) : (unsigned)(p.N / kBN);
+    const unsigned nt = EPI == kEpiSwiglu ? (unsigned)(2 * p.F / BN) : (unsigned)(p.N / BN);
     grid = dim3(nt, (unsigned)(p.R / BM), 1);
   } else {
-    grid = dim3((unsigned)(p.N / kBN), (unsigned)(p.M / BM), (unsigned)p.G);
+    grid = dim3((unsigned)(p.N / BN), (unsigned)(p.M / BM), (unsigned)p.G);
   }
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, MODE, EPI>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE, EPI>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream) {
-  if (mode == kDense) return launch_one<FMT, 128, kDense, kEpiStore>(p, stream);
-  if (mode == kRaggedM) {
-    if (epi == kEpiSwiglu) return launch_one<FMT, 128, kRaggedM, kEpiSwiglu>(p, stream);
-    if (epi == kEpiDSwiglu) return launch_one<FMT, 128, kRaggedM, kEpiDSwiglu>(p, stream);
-    return launch_one<FMT, 128, kRaggedM, kEpiStore>(p, stream);
+  if (mode == kDense) {
+    // 256 x 256 tiles once they fill the chip; 256 x 128 otherwise
+    const int64_t big = (p.M / 256) * (p.N / 256);
+    if (big >= 256) return launch_one<FMT, 256, 256, kDense, kEpiStore>(p, stream);
+    return launch_one<FMT, 256, 128, kDense, kEpiStore>(p, stream);
   }
-  return launch_one<FMT, 128, kRaggedK, kEpiStore>(p, stream);
+  if (mode == kRaggedM) {
+    if (epi == kEpiSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiSwiglu>(p, stream);
+    if (epi == kEpiDSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiDSwiglu>(p, stream);
+    return launch_one<FMT, 128, 256, kRaggedM, kEpiStore>(p, stream);
+  }
+  return launch_one<FMT, 256, 256, kRaggedK, kEpiStore>(p, stream);
 }
 
 }  // namespace
