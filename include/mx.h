@@ -23,9 +23,17 @@
  *  - bf16 tensors are row-major and dense.  Every device pointer must be
  *    16-byte aligned.
  *  - Packed operands are K-major ("rows x K"): codes [rows][K*bits/8] bytes
- *    with bits = 4, 6 or 8, and scales [rows][K/32] E8M0 bytes.  Code layout
- *    within a row: E2M1 element 2j in the low nibble of byte j and 2j+1 in
- *    the high nibble; E2M3 a little-endian 6-bit stream, element j at bits
+ *    with bits = 4, 6 or 8, and E8M0 scales, one byte per (row, 32-block b),
+ *    in the blocked layout the GEMM reads: the four bytes of one 128-element
+ *    K group form a dword (block b in byte b % 4), and the dwords of one K
+ *    group are stored row after row, i.e. scales [ceil(K/128)][rows][4]
+ *    with (row, b) at byte (b/4 * rows + row) * 4 + b % 4 (mx_scales_bytes
+ *    bytes; pad bytes of a partial last group are 0).  As in [P4] (the
+ *    grouped kernels' blocked E8M0 scale ABI), the quantizer writes the
+ *    blocking the GEMM reads; a ragged-K group of rows [k0, k1), k0 and k1
+ *    multiples of 128, is the run of K groups k0/128 .. k1/128 - 1.  Code layout within a
+ *    row: E2M1 element 2j in the low nibble of byte j and 2j+1 in the high
+ *    nibble; E2M3 a little-endian 6-bit stream, element j at bits
  *    [6j, 6j+6); E4M3 one byte per element.  Every GEMM computes
  *    C = A . B^T on two K-major operands (the NT layout of [P3],
  *    Troubleshooting).
@@ -95,7 +103,7 @@ typedef enum { MX_GROUPED_RAGGED_M = 0, MX_GROUPED_RAGGED_K = 1 } mx_grouped_mod
 
 typedef enum { MX_EPI_NONE = 0, MX_EPI_SWIGLU = 1, MX_EPI_DSWIGLU = 2 } mx_epilogue;
 
-/* One packed operand: codes [rows][K*bits/8] bytes + scales [rows][K/32]. */
+/* One packed operand: codes [rows][K*bits/8] bytes + blocked scales [ceil(K/128)][rows][4]. */
 typedef struct {
   void* codes;
   void* scales;
@@ -127,6 +135,7 @@ typedef struct {
  *                          transposed, i.e. K-major [C] x K=R.
  *               Either pair may be NULL (both members of a pair alike), not
  *               both.
+ *               The batch stride of a scale buffer is mx_scales_bytes(rows, K).
  *  colsum_partials  fp32 [R/32][C]: per-32-row-block column sums of v before
  *               rotation, rows in increasing order from +0 ([P1] commit
  *               messages: the bias gradient is finished from the packer's
@@ -230,9 +239,11 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* args, void* stream);
  * host, synchronizing `stream`, and checks them (MX_ERR_OFFSETS).
  *
  * MX_GROUPED_RAGGED_M (forward and data gradients):
- *   A [R] x K, B [G][N] x K (expert g's rows at B + g*N rows),
+ *   A [R] x K, B [G][N] x K (expert g's rows at B + g*N rows; its scales
+ *   at B.scales + g * mx_scales_bytes(N, K), as written by a batch-G
+ *   mx_quantize),
  *   C[r][n] = sum_k A[r][k] * B_g(r)[n][k], bf16 [R][N].  N, K multiples of
- *   256 (SWIGLU: N/2 a multiple of 128; DSWIGLU: N a multiple of 128).
+ *   256 (SWIGLU: also N/2 a multiple of 128).
  *   epilogue MX_EPI_NONE:    C stored.
  *   epilogue MX_EPI_SWIGLU:  N = 2F; C = H [R][2F] = [gate | up] stored
  *     (the pre-activation kept for the backward); z = SwiGLU(H) is
@@ -272,7 +283,8 @@ int mx_grouped_gemm(const mx_grouped_args* args, void* stream);
 const char* mx_status_str(int status);
 /* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0. */
 int mx_device_supported(int device);
-/* Bytes of one packed operand's codes / scales for rows x K in fmt (0 on bad input). */
+/* Bytes of one packed operand's codes / blocked scales for rows x K in fmt (0 on bad input):
+ * rows * K * bits / 8 and ceil(K/128) * rows * 4. */
 int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K);
 int64_t mx_scales_bytes(int64_t rows, int64_t K);
 /* Library version string. */

@@ -380,7 +380,7 @@ int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K) {
 
 int64_t mx_scales_bytes(int64_t rows, int64_t K) {
   if (rows < 0 || K < 0 || K % 32) return 0;
-  return rows * (K / 32);
+  return mx::scale_bytes(rows, K);
 }
 
 const char* mx_version(void) { return "libmx 0.1 (gfx950)"; }

@@ -43,14 +43,18 @@ __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// binary32 -> bf16 bits, nearest-even; NaN stays NaN (quiet bit set).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
+// binary32 -> bf16 bits, nearest-even; NaN stays NaN (quiet bit set).  The
+// gfx950 conversion instruction follows exactly this rule (checked against
+// (u + 0x7fff + lsb) >> 16, NaN -> (u >> 16) | 0x40, on all 2^32 inputs).
+typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float mx_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const mx_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mx_bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 // Round through bf16 and back.
-__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16(f) << 16); }
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(pack_bf16x2(f, 0.0f) << 16); }
 
 // ------------------------------------------------------------------ E8M0
 // Scale byte from the block's amax, given as the bit pattern of |amax| in

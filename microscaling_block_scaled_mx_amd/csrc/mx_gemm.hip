@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const int64_t n0 = (int64_t)tn * BN;  // SwiGLU: tile tn covers z columns [tn*BN/2, (tn+1)*BN/2)
   int64_t kbeg = 0, kend = p.K;
   int64_t b_row0 = 0;  // first B row of this tile's group
+  int64_t b_soff = 0;  // byte offset of this tile's group in the B scales (one blocked array per group)
   int64_t c_off = 0;   // element offset of this tile's group in C
   if constexpr (MODE == kRaggedM) {
     // offsets are a caller invariant; clamping keeps every access inside the
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     int gi = 0;
     while (p.offsets[gi] <= m0) ++gi;
     b_row0 = (int64_t)gi * p.b_group_rows;
+    b_soff = (int64_t)gi * scale_bytes(p.b_group_rows, p.ktot);
   }
   if constexpr (MODE == kRaggedK) {
     const int gi = blockIdx.z;
@@ -246,7 +248,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     c_off = (int64_t)gi * p.M * p.N;
   }
   const int64_t row_bytes = p.ktot * kBits / 8;
-  const int64_t srow = p.ktot / 32;
+  // rows of the A / B operands (of one group's B): the stride between K
+  // groups of their scales
+  const int64_t a_rows = p.M;
+  const int64_t b_rows = MODE == kRaggedM ? p.b_group_rows : p.N;
   const int nk = (int)((kend - kbeg) / CF::kBK);
 
   // LDS row r of the B tile -> global B row
@@ -275,15 +280,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
     b_off[i] = (uint32_t)(b_row(r) * row_bytes + 16 * chunk_at<CF::kChunks>(r, pos));
   }
-  // scale dwords (4 blocks of 32 along K): slot t and t + 256 of [A rows | B rows];
-  // slots past BM + BN load row 0's scales into unused slots, so every wave
-  // issues the same number of loads
+  // scale dwords (4 blocks of 32 along K, blocked layout): slot t and t + 256
+  // of [A rows | B rows]; slots past BM + BN load row 0's dword into unused
+  // slots, so every wave issues the same number of loads
   const uint8_t* s_src[2];
+  int64_t s_step[2];  // bytes between consecutive K groups
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = t + 256 * j;
-    s_src[j] = r < BM ? p.a_scales + (m0 + r) * srow
-                      : (r < BM + BN ? p.b_scales + b_row(r - BM) * srow : p.a_scales + m0 * srow);
+    const bool is_b = r >= BM && r < BM + BN;
+    s_src[j] = is_b ? p.b_scales + b_soff + (b_row(r - BM) - b_row0) * 4 : p.a_scales + (m0 + (r < BM ? r : 0)) * 4;
+    s_step[j] = (is_b ? b_rows : a_rows) * 4;
   }
   const int wave_u = wave_uniform(wave);
 
@@ -298,10 +305,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_dma16(ga_ + a_off[i_], st_ + CF::kAOff + (i_ * 256 + wave_u * 64) * 16);                      \
     _Pragma("unroll") for (int i_ = 0; i_ < CF::kBIters; ++i_)                                           \
       lds_dma16(gb_ + b_off[i_], st_ + CF::kBOff + (i_ * 256 + wave_u * 64) * 16);                      \
-    const int64_t ks_ = (k0_ & ~(int64_t)127) / 32;                                                      \
+    const int64_t kg_ = k0_ / 128;                                                                       \
     _Pragma("unroll") for (int d_ = 0; d_ < CF::kScaleDw; ++d_)                                          \
     _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                                                     \
-      lds_dma4(s_src[j_] + ks_ + 4 * d_, st_ + CF::kSOff + (d_ * 512 + j_ * 256 + wave_u * 64) * 4);     \
+      lds_dma4(s_src[j_] + (kg_ + d_) * s_step[j_], st_ + CF::kSOff + (d_ * 512 + j_ * 256 + wave_u * 64) * 4); \
   } while (0)
 
   // ---------------------------------------------------------------- main loop
@@ -392,8 +399,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   // Lane (row lrow, column group q = 8 * (e / 4) + 4 * g) of MFMA tile (i, j)
   // holds acc[i][j][4 * (e / 4) + 0..3] = C[row][col + 0..3].
   if constexpr (EPI == kEpiStore) {
-    const uint16_t* bias16 = reinterpret_cast<const uint16_t*>(p.bias);
-    const float* bias32 = reinterpret_cast<const float*>(p.bias);
+    // bias of this lane's columns, read once (one uniform branch)
+    float bv[CF::kNJ][16];
+    if (p.bias == nullptr) {
+#pragma unroll
+      for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) bv[j][e] = 0.0f;
+    } else if (p.bias_f32) {
+      const float* bias32 = reinterpret_cast<const float*>(p.bias);
+#pragma unroll
+      for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float4 q = *reinterpret_cast<const float4*>(bias32 + n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g);
+          bv[j][4 * e4 + 0] = q.x;
+          bv[j][4 * e4 + 1] = q.y;
+          bv[j][4 * e4 + 2] = q.z;
+          bv[j][4 * e4 + 3] = q.w;
+        }
+    } else {
+      const uint16_t* bias16 = reinterpret_cast<const uint16_t*>(p.bias);
+#pragma unroll
+      for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const uint2 q = *reinterpret_cast<const uint2*>(bias16 + n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g);
+          bv[j][4 * e4 + 0] = bf16_lo(q.x);
+          bv[j][4 * e4 + 1] = bf16_hi(q.x);
+          bv[j][4 * e4 + 2] = bf16_lo(q.y);
+          bv[j][4 * e4 + 3] = bf16_hi(q.y);
+        }
+    }
     if (p.c_f32) {
       float* C = reinterpret_cast<float*>(p.c) + c_off;
 #pragma unroll
@@ -404,14 +441,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
           for (int e4 = 0; e4 < 4; ++e4) {
             const int64_t m = m0 + wm * CF::kWM + 32 * i + lrow;
             const int64_t n = n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float b = 0.0f;
-              if (p.bias) b = p.bias_f32 ? bias32[n + q] : bf16_to_f32(bias16[n + q]);
-              v[q] = acc[i][j][4 * e4 + q] + b;
-            }
-            *reinterpret_cast<float4*>(C + m * p.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+            const v16f& a = acc[i][j];
+            *reinterpret_cast<float4*>(C + m * p.ldc + n) =
+                make_float4(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1],
+                            a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]);
           }
     } else {
       // bf16: stage the wavefront's tile in LDS with 8-byte writes, then
@@ -424,15 +457,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
             const int r = 32 * i + lrow, cl = 32 * j + 8 * e4 + 4 * g;
-            const int64_t n = n0 + wn * CF::kWN + cl;
-            uint32_t h[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float b = 0.0f;
-              if (p.bias) b = p.bias_f32 ? bias32[n + q] : bf16_to_f32(bias16[n + q]);
-              h[q] = f32_to_bf16(acc[i][j][4 * e4 + q] + b);
-            }
-            *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            const v16f& a = acc[i][j];
+            *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) =
+                make_uint2(pack_bf16x2(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1]),
+                           pack_bf16x2(a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]));
           }
       __syncthreads();
       uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + c_off;
@@ -467,9 +495,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
           for (int q = 0; q < 4; ++q) {
             const float g0 = round_bf16(acc[i][j][4 * e4 + q]);
             const float u0 = round_bf16(acc[i][j + H2][4 * e4 + q]);
-            hg[q] = f32_to_bf16(g0);
-            hu[q] = f32_to_bf16(u0);
-            z[q] = f32_to_bf16(swiglu_bf16(g0, u0));
+            hg[q] = __float_as_uint(g0) >> 16;
+            hu[q] = __float_as_uint(u0) >> 16;
+            z[q] = __float_as_uint(swiglu_bf16(g0, u0)) >> 16;
           }
           *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + zb + zc) = make_uint2(hg[0] | (hg[1] << 16), hg[2] | (hg[3] << 16));
           *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + p.F + zb + zc) =
@@ -486,10 +514,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       const int64_t m = m0 + row, col = zb + 32 * blk;
       if (p.q_mode == kRceil)
         quant_store<FMT, kRceil, 0>(v, p.q_row_codes + m * (p.F * QB / 8) + col * QB / 8,
-                                    p.q_row_scales + m * (p.F / 32) + col / 32);
+                                    p.q_row_scales + scale_offset(m, col / 32, p.R));
       else
         quant_store<FMT, kFloor, 0>(v, p.q_row_codes + m * (p.F * QB / 8) + col * QB / 8,
-                                    p.q_row_scales + m * (p.F / 32) + col / 32);
+                                    p.q_row_scales + scale_offset(m, col / 32, p.R));
     }
     for (int q = t; q < ZC * (BM / 32); q += kThreads) {
       const int col = q % ZC, rb2 = q / ZC;
@@ -498,10 +526,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       const int64_t cz = zb + col, m = m0 + 32 * rb2;
       if (p.q_mode == kRceil)
         quant_store<FMT, kRceil, 0>(v, p.q_col_codes + cz * (p.R * QB / 8) + m * QB / 8,
-                                    p.q_col_scales + cz * (p.R / 32) + m / 32);
+                                    p.q_col_scales + scale_offset(cz, m / 32, p.F));
       else
         quant_store<FMT, kFloor, 0>(v, p.q_col_codes + cz * (p.R * QB / 8) + m * QB / 8,
-                                    p.q_col_scales + cz * (p.R / 32) + m / 32);
+                                    p.q_col_scales + scale_offset(cz, m / 32, p.F));
     }
   } else {  // kEpiDSwiglu
     // dz = bf16(acc); with H: d_gate -> tile 0, d_up -> tile 1 (LDS only).
@@ -525,9 +553,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float dz = round_bf16(acc[i][j][4 * e4 + q]);
-            dzb[q] = f32_to_bf16(dz);
-            dg[q] = f32_to_bf16(dswiglu_gate_bf16(dz, gv[q], uv[q]));
-            du[q] = f32_to_bf16(dswiglu_up_bf16(dz, gv[q]));
+            dzb[q] = __float_as_uint(dz) >> 16;
+            dg[q] = __float_as_uint(dswiglu_gate_bf16(dz, gv[q], uv[q])) >> 16;
+            du[q] = __float_as_uint(dswiglu_up_bf16(dz, gv[q])) >> 16;
           }
           if (p.c)
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.F + n) =
@@ -546,10 +574,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       const int64_t m = m0 + row, col = (half ? p.F : 0) + n0 + 32 * blk;
       if (p.q_mode == kRceil)
         quant_store<FMT, kRceil, 0>(v, p.q_row_codes + m * (W * QB / 8) + col * QB / 8,
-                                    p.q_row_scales + m * (W / 32) + col / 32);
+                                    p.q_row_scales + scale_offset(m, col / 32, p.R));
       else
         quant_store<FMT, kFloor, 0>(v, p.q_row_codes + m * (W * QB / 8) + col * QB / 8,
-                                    p.q_row_scales + m * (W / 32) + col / 32);
+                                    p.q_row_scales + scale_offset(m, col / 32, p.R));
     }
     for (int q = t; q < 2 * BN * (BM / 32); q += kThreads) {
       const int half = q / (BN * (BM / 32)), cq = q % (BN * (BM / 32));
@@ -559,10 +587,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       const int64_t cw = (half ? p.F : 0) + n0 + col, m = m0 + 32 * rb2;
       if (p.q_mode == kRceil)
         quant_store<FMT, kRceil, 0>(v, p.q_col_codes + cw * (p.R * QB / 8) + m * QB / 8,
-                                    p.q_col_scales + cw * (p.R / 32) + m / 32);
+                                    p.q_col_scales + scale_offset(cw, m / 32, W));
       else
         quant_store<FMT, kFloor, 0>(v, p.q_col_codes + cw * (p.R * QB / 8) + m * QB / 8,
-                                    p.q_col_scales + cw * (p.R / 32) + m / 32);
+                                    p.q_col_scales + scale_offset(cw, m / 32, W));
     }
   }
 }

@@ -6,14 +6,28 @@
 
 namespace mx {
 
+// Blocked E8M0 scale layout of a packed operand with `rows` rows and K
+// elements per row: the four scale bytes of one 128-element K group form a
+// dword (block 4q+i in byte i), and the dwords of one K group are stored row
+// after row -- [ceil(K/128)][rows][4] bytes.  A GEMM stage then reads the
+// scales of a row panel as one contiguous run.  Pad bytes of a last, partial
+// K group are written as 0.
+__host__ __device__ __forceinline__ int64_t scale_offset(int64_t row, int64_t blk, int64_t rows) {
+  return ((blk >> 2) * rows + row) * 4 + (blk & 3);
+}
+__host__ __device__ __forceinline__ int64_t scale_bytes(int64_t rows, int64_t K) {
+  return ((K / 32 + 3) / 4) * rows * 4;
+}
+
+
 struct PackParams {
   const uint16_t* x;    // prologue input (bf16 bits)
   const uint16_t* aux;  // second prologue input or nullptr
   int64_t R, C;         // logical quantized tensor [R][C] per batch entry
   uint8_t* row_codes;   // [R][C*bits/8] or nullptr
-  uint8_t* row_scales;  // [R][C/32]
+  uint8_t* row_scales;  // blocked layout, rows R, K = C
   uint8_t* col_codes;   // [C][R*bits/8] or nullptr
-  uint8_t* col_scales;  // [C][R/32]
+  uint8_t* col_scales;  // blocked layout, rows C, K = R
   float* partials;      // [R/32][C] or nullptr
 };
 

@@ -130,12 +130,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   if (p.row_codes) {
     const int row = t >> 2, blk = t & 3;
     const int64_t r = r0 + row, c = c0 + blk * 32;
+    uint8_t* scales = p.row_scales + z * scale_bytes(p.R, p.C) + scale_offset(r, c / 32, p.R);
     if (r < p.R && c < p.C) {
       float v[32];
       lds_row_block(tile, kPitch, row, blk * 32, v);
       uint8_t* codes = p.row_codes + z * p.R * (p.C * B / 8) + r * (p.C * B / 8) + c * B / 8;
-      uint8_t* scales = p.row_scales + z * p.R * (p.C / 32) + r * (p.C / 32) + c / 32;
       quant_store<FMT, MODE, HAD>(v, codes, scales);
+    } else if (r < p.R) {
+      *scales = 0;  // pad byte of the row's last scale dword (the tile spans exactly one dword)
     }
   }
 
@@ -143,6 +145,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   if (p.col_codes || p.partials) {
     const int col = t & 127, blk = t >> 7;
     const int64_t c = c0 + col, r = r0 + blk * 32;
+    if (c < p.C) {
+      // pad bytes of the column's last scale dword: a dword spans 4 row
+      // blocks = two 64-row tiles; the even tile writes the odd one's bytes
+      // as 0 when that tile does not exist, and a block past R is 0 as well
+      uint8_t* cscale = p.col_codes ? p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C) : nullptr;
+      if (cscale && r >= p.R) *cscale = 0;
+      if (cscale && (blockIdx.y & 1) == 0 && r0 + kTileR >= p.R) cscale[2] = 0;
+    }
     if (c < p.C && r < p.R) {
       float v[32];
       lds_col_block(tile, kPitch, blk * 32, col, v);
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
       }
       if (p.col_codes) {
         uint8_t* codes = p.col_codes + z * p.C * (p.R * B / 8) + c * (p.R * B / 8) + r * B / 8;
-        uint8_t* scales = p.col_scales + z * p.C * (p.R / 32) + c * (p.R / 32) + r / 32;
+        uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
         quant_store<FMT, MODE, HAD>(v, codes, scales);
       }
     }

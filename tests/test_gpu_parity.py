@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from microscaling_block_scaled_mx_amd import inputs as I
+from scale_layout import blocked, blocked_shape, unblocked
 
 pytestmark = pytest.mark.gpu
 
@@ -85,13 +86,15 @@ def gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, row=True, col=True, col
     xd = dev(x)
     ad = dev(aux) if aux is not None else None
     shp = (lambda r, k: (r, k) if batch == 1 else (batch, r, k))
+    bshp = (lambda r, k: blocked_shape(r, k, None if batch == 1 else batch))
     rowp = colp = None
+    # poisoned buffers: every byte, pad bytes included, must be written
     if row:
-        rowp = (torch.zeros(shp(R, C * mxl.BITS[fmt] // 8), dtype=torch.uint8, device="cuda"),
-                torch.zeros(shp(R, C // 32), dtype=torch.uint8, device="cuda"))
+        rowp = (torch.full(shp(R, C * mxl.BITS[fmt] // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(bshp(R, C), 0xA5, dtype=torch.uint8, device="cuda"))
     if col:
-        colp = (torch.zeros(shp(C, R * mxl.BITS[fmt] // 8), dtype=torch.uint8, device="cuda"),
-                torch.zeros(shp(C, R // 32), dtype=torch.uint8, device="cuda"))
+        colp = (torch.full(shp(C, R * mxl.BITS[fmt] // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(bshp(C, R), 0xA5, dtype=torch.uint8, device="cuda"))
     part = sums = None
     if colsum:
         part = torch.zeros(shp(R // 32, C), dtype=torch.float32, device="cuda")
@@ -100,9 +103,9 @@ def gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, row=True, col=True, col
                  batch=batch)
     out = {}
     if row:
-        out["row_codes"], out["row_scales"] = host(rowp[0]), host(rowp[1])
+        out["row_codes"], out["row_scales"] = host(rowp[0]), unblocked(host(rowp[1]), C // 32)
     if col:
-        out["col_codes"], out["col_scales"] = host(colp[0]), host(colp[1])
+        out["col_codes"], out["col_scales"] = host(colp[0]), unblocked(host(colp[1]), R // 32)
     if colsum:
         out["colsum_partials"], out["colsum"] = host(part), host(sums)
     return out
@@ -166,8 +169,8 @@ def gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed, bias=False):
     pa = orc.quantize(A, M, K, fmt, mode, had)
     pb = orc.quantize(B, N, K, fmt, mode, had)
     ref = orc.gemm(pa["row_codes"], pa["row_scales"], pb["row_codes"], pb["row_scales"], M, N, K, fmt, bias=b)
-    a = (dev(pa["row_codes"]), dev(pa["row_scales"]))
-    bb = (dev(pb["row_codes"]), dev(pb["row_scales"]))
+    a = (dev(pa["row_codes"]), dev(blocked(pa["row_scales"])))
+    bb = (dev(pb["row_codes"]), dev(blocked(pb["row_scales"])))
     c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     c16 = bf16_empty(M, N)
     bd = dev(b) if b is not None else None
@@ -216,7 +219,7 @@ def test_gemm_exact_products_bitwise(mxl, orc, fmt):
     bc, bsc = packed(N)
     ref = orc.gemm(ac, asc, bc, bsc, M, N, K, fmt)
     c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    mxl.gemm((dev(ac), dev(asc)), (dev(bc), dev(bsc)), M, N, K, fmt, c32, c_dtype=mxl.F32)
+    mxl.gemm((dev(ac), dev(blocked(asc))), (dev(bc), dev(blocked(bsc))), M, N, K, fmt, c32, c_dtype=mxl.F32)
     assert np.array_equal(host(c32).astype(np.float64), ref)
 
 
@@ -225,10 +228,7 @@ def test_gemm_determinism(mxl, orc):
     M, N, K = 512, 512, 1024
     A = I.bf16_normal(rng, (M, K))
     B = I.bf16_normal(rng, (N, K), 0.02)
-    pa = (torch.empty((M, K * 3 // 4), dtype=torch.uint8, device="cuda"),
-          torch.empty((M, K // 32), dtype=torch.uint8, device="cuda"))
-    pb = (torch.empty((N, K * 3 // 4), dtype=torch.uint8, device="cuda"),
-          torch.empty((N, K // 32), dtype=torch.uint8, device="cuda"))
+    pa, pb = mxl.alloc_packed(M, K, 2), mxl.alloc_packed(N, K, 2)
     mxl.quantize(dev(A), M, K, 2, 0, True, row=pa)
     mxl.quantize(dev(B), N, K, 2, 0, True, row=pb)
     c1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -273,25 +273,26 @@ def test_fused_mlp_parity_small(mxl, orc):
     t = run_mlp(mxl, X, W1, b1, W2, dY, M, D, F)
     h = host(t["h"])
     fwd = orc.mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=h)
+    KN = dict(Xr=D, W1r=D, W2r=F, Xc=M, W1c=F, W2c=D)
     for name, key in (("Xr", "X"), ("W1r", "W1"), ("W2r", "W2")):
         assert np.array_equal(host(t[name][0]), fwd[key]["row_codes"]), name
-        assert np.array_equal(host(t[name][1]), fwd[key]["row_scales"]), name
+        assert np.array_equal(unblocked(host(t[name][1]), KN[name] // 32), fwd[key]["row_scales"]), name
     for name, key in (("Xc", "X"), ("W1c", "W1"), ("W2c", "W2")):
         assert np.array_equal(host(t[name][0]), fwd[key]["col_codes"]), name
-        assert np.array_equal(host(t[name][1]), fwd[key]["col_scales"]), name
+        assert np.array_equal(unblocked(host(t[name][1]), KN[name] // 32), fwd[key]["col_scales"]), name
     assert bf16_close(h, fwd["h64"])
     # activation packs, bit-exact given the GPU's h
     assert np.array_equal(host(t["ar"][0]), fwd["a"]["row_codes"])
-    assert np.array_equal(host(t["ar"][1]), fwd["a"]["row_scales"])
+    assert np.array_equal(unblocked(host(t["ar"][1]), (F) // 32), fwd["a"]["row_scales"])
     assert np.array_equal(host(t["ac"][0]), fwd["a"]["col_codes"])
-    assert np.array_equal(host(t["ac"][1]), fwd["a"]["col_scales"])
+    assert np.array_equal(unblocked(host(t["ac"][1]), (M) // 32), fwd["a"]["col_scales"])
     assert bf16_close(host(t["Y"]), fwd["Y64"])
     da = host(t["da"])
     bwd = orc.mlp_bwd_ref(dY, fwd, M, D, F, da_in=da, h_in=h)
     assert bf16_close(da, bwd["da64"])
     assert np.array_equal(host(t["dhr"][0]), bwd["dh"]["row_codes"])
     assert np.array_equal(host(t["dhc"][0]), bwd["dh"]["col_codes"])
-    assert np.array_equal(host(t["dhc"][1]), bwd["dh"]["col_scales"])
+    assert np.array_equal(unblocked(host(t["dhc"][1]), (M) // 32), bwd["dh"]["col_scales"])
     assert np.array_equal(host(t["db1"]).view(np.uint32), bwd["db1"].view(np.uint32))
     assert bf16_close(host(t["dX"]), bwd["dX64"])
     assert bf16_close(host(t["dW1"]), bwd["dW1_64"])
@@ -342,17 +343,17 @@ def test_grouped_parity_small(mxl, orc):
     fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H)
     assert bf16_close(H, fwd["H64"])
     assert np.array_equal(host(t["zr"][0]), fwd["z"]["row_codes"])
-    assert np.array_equal(host(t["zr"][1]), fwd["z"]["row_scales"])
+    assert np.array_equal(unblocked(host(t["zr"][1]), (F) // 32), fwd["z"]["row_scales"])
     assert np.array_equal(host(t["zc"][0]), fwd["z"]["col_codes"])
-    assert np.array_equal(host(t["zc"][1]), fwd["z"]["col_scales"])
+    assert np.array_equal(unblocked(host(t["zc"][1]), (R) // 32), fwd["z"]["col_scales"])
     assert bf16_close(host(t["Y"]), fwd["Y64"])
     dz = host(t["dz"])
     bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=dz, H_in=H)
     assert bf16_close(dz, bwd["dz64"])
     assert np.array_equal(host(t["dHr"][0]), bwd["dH"]["row_codes"])
-    assert np.array_equal(host(t["dHr"][1]), bwd["dH"]["row_scales"])
+    assert np.array_equal(unblocked(host(t["dHr"][1]), (2 * F) // 32), bwd["dH"]["row_scales"])
     assert np.array_equal(host(t["dHc"][0]), bwd["dH"]["col_codes"])
-    assert np.array_equal(host(t["dHc"][1]), bwd["dH"]["col_scales"])
+    assert np.array_equal(unblocked(host(t["dHc"][1]), (R) // 32), bwd["dH"]["col_scales"])
     assert bf16_close(host(t["dX"]), bwd["dX64"])
     dW1, dW2 = host(t["dW1"]), host(t["dW2"])
     assert not np.any(dW1[2]) and not np.any(dW2[2])  # zero-token expert: zeros written
@@ -375,12 +376,15 @@ def test_grouped_inactive_tail_untouched(mxl, orc):
     mxl.quantize(dev(W1), 2 * F, D, fmt, 1, row=w1r, batch=G)
     H = torch.full((R, 2 * F), 0x1234, dtype=torch.int16, device="cuda")
     zr = (torch.full((R, F), 0xAB, dtype=torch.uint8, device="cuda"),
-          torch.full((R, F // 32), 0xAB, dtype=torch.uint8, device="cuda"))
+          torch.full(blocked_shape(R, F), 0xAB, dtype=torch.uint8, device="cuda"))
     zc = (torch.full((F, R), 0xAB, dtype=torch.uint8, device="cuda"),
-          torch.full((F, R // 32), 0xAB, dtype=torch.uint8, device="cuda"))
+          torch.full(blocked_shape(F, R), 0xAB, dtype=torch.uint8, device="cuda"))
     mxl.grouped_gemm(mxl.RAGGED_M, G, R, dev(offsets), xr, w1r, H, epilogue=mxl.EPI_SWIGLU, N=2 * F, K=D,
                      out_row=zr, out_col=zc)
     Hh = host(H)
     assert np.all(Hh[640:] == 0x1234) and not np.any(Hh[:640] == 0x1234)
     assert np.all(host(zr[0])[640:] == 0xAB) and np.all(host(zc[0])[:, 640:] == 0xAB)
+    zrs, zcs = host(zr[1]), host(zc[1])  # [F/128][R][4], [R/128][F][4]
+    assert np.all(zrs[:, 640:] == 0xAB) and not np.any(zrs[:, :640] == 0xAB)
+    assert np.all(zcs[640 // 128:] == 0xAB) and not np.any(zcs[:640 // 128] == 0xAB)
     assert not np.any(np.isnan(I.bf16_bits_to_f32(Hh[:640])))
