@@ -294,21 +294,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   }
   const int wave_u = wave_uniform(wave);
 
-  // issue the loads of stage k into ring buffer buf
-#define MX_ISSUE(k, buf)                                                                                  \
+  // Load q (0 <= q < kLoads) of stage k into ring buffer buf: A chunks, then
+  // B chunks, then scale dwords (K group d, slot half j).  Every use sits in
+  // fully unrolled code, so q is a constant and each use compiles to one
+  // load instruction.
+#define MX_PIECE(k, buf, q)                                                                               \
   do {                                                                                                   \
     const int64_t k0_ = kbeg + (int64_t)(k) * BK;                                                        \
-    const uint8_t* ga_ = p.a_codes + k0_ * kBits / 8;                                                    \
-    const uint8_t* gb_ = p.b_codes + k0_ * kBits / 8;                                                    \
     uint8_t* st_ = smem + (buf) * CF::kStage;                                                            \
-    _Pragma("unroll") for (int i_ = 0; i_ < CF::kAIters; ++i_)                                           \
-      lds_dma16(ga_ + a_off[i_], st_ + CF::kAOff + (i_ * 256 + wave_u * 64) * 16);                      \
-    _Pragma("unroll") for (int i_ = 0; i_ < CF::kBIters; ++i_)                                           \
-      lds_dma16(gb_ + b_off[i_], st_ + CF::kBOff + (i_ * 256 + wave_u * 64) * 16);                      \
-    const int64_t kg_ = k0_ / 128;                                                                       \
-    _Pragma("unroll") for (int d_ = 0; d_ < CF::kScaleDw; ++d_)                                          \
-    _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                                                     \
-      lds_dma4(s_src[j_] + (kg_ + d_) * s_step[j_], st_ + CF::kSOff + (d_ * 512 + j_ * 256 + wave_u * 64) * 4); \
+    if ((q) < CF::kAIters) {                                                                             \
+      const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
+      lds_dma16(p.a_codes + k0_ * kBits / 8 + a_off[i_], st_ + CF::kAOff + (i_ * 256 + wave_u * 64) * 16); \
+    } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
+      const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
+      lds_dma16(p.b_codes + k0_ * kBits / 8 + b_off[i_], st_ + CF::kBOff + (i_ * 256 + wave_u * 64) * 16); \
+    } else {                                                                                             \
+      const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
+      const int d_ = e_ / 2, j_ = e_ % 2;                                                                \
+      lds_dma4(s_src[j_] + (k0_ / 128 + d_) * s_step[j_],                                               \
+               st_ + CF::kSOff + (d_ * 512 + j_ * 256 + wave_u * 64) * 4);                              \
+    }                                                                                                    \
+  } while (0)
+#define MX_ISSUE(k, buf)                                                                                  \
+  do {                                                                                                   \
+    _Pragma("unroll") for (int q_ = 0; q_ < CF::kLoads; ++q_) MX_PIECE(k, buf, q_);                     \
   } while (0)
 
   // ---------------------------------------------------------------- main loop
@@ -335,63 +344,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   }
 
   constexpr int S = CF::kStages;
+  constexpr int KS = BK / 64;
+  // Loads of the stage S - 1 ahead are spread over this stage's MFMAs, kPer
+  // per K step, one after every kEvery-th MFMA: issued in one burst they
+  // stall the wavefront at issue while the address units drain them.
+  constexpr int kMf = CF::kMI * CF::kNJ;
+  constexpr int kPer = (CF::kLoads + KS - 1) / KS;
+  constexpr int kEvery = kMf / kPer > 0 ? kMf / kPer : 1;
+  static_assert(kPer <= kMf, "every load needs an MFMA slot");
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nk) MX_ISSUE(st, st);
-  for (int it = 0; it < nk; ++it) {
-    if (it + S - 2 < nk) wait_vmcnt<CF::kLoads * (S - 2)>();  // stage it landed (this wave's part)
-    else wait_vmcnt<0>();
-    stage_barrier();  // ... and every wave's; buffer (it - 1) % S is free again
-    if (it + S - 1 < nk) MX_ISSUE(it + S - 1, (it + S - 1) % S);
-    const uint8_t* sb = smem + (it % S) * CF::kStage;
-    // Scale dwords of this lane's rows (one per 128 K), read once per stage.
-    uint32_t sda[CF::kScaleDw][CF::kMI], sdb[CF::kScaleDw][CF::kNJ];
-#pragma unroll
-    for (int d = 0; d < CF::kScaleDw; ++d) {
-#pragma unroll
-      for (int i = 0; i < CF::kMI; ++i)
-        sda[d][i] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + arow[i]) * 4);
-#pragma unroll
-      for (int j = 0; j < CF::kNJ; ++j)
-        sdb[d][j] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + BM + brow[j]) * 4);
-    }
-    sched_fence();
-    // Operand fragments double-buffered in registers: the reads of K step
-    // ks + 1 are in flight while the MFMAs of step ks run.
-    constexpr int KS = BK / 64;
-    v8i af[2][CF::kMI], bf[2][CF::kNJ];
-#pragma unroll
-    for (int i = 0; i < CF::kMI; ++i) af[0][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], 0, g);
-#pragma unroll
-    for (int j = 0; j < CF::kNJ; ++j) bf[0][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], 0, g);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cb = ks & 1;
-      if (ks + 1 < KS) {
-#pragma unroll
-        for (int i = 0; i < CF::kMI; ++i)
-          af[cb ^ 1][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], ks + 1, g);
-#pragma unroll
-        for (int j = 0; j < CF::kNJ; ++j)
-          bf[cb ^ 1][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], ks + 1, g);
-      }
-      sched_fence();  // the reads above are issued before the MFMAs below
-      // E8M0 byte of K block 2 ks + g of the stage (k0 % 128 == 0 at every stage start)
-      const int bi = 2 * ks;
-      int sa[CF::kMI], sbs[CF::kNJ];
-#pragma unroll
-      for (int i = 0; i < CF::kMI; ++i) sa[i] = (int)(sda[bi >> 2][i] >> (8 * ((bi & 3) + g)));
-#pragma unroll
-      for (int j = 0; j < CF::kNJ; ++j) sbs[j] = (int)(sdb[bi >> 2][j] >> (8 * ((bi & 3) + g)));
-#pragma unroll
-      for (int i = 0; i < CF::kMI; ++i)
-#pragma unroll
-        for (int j = 0; j < CF::kNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              bf[cb][j], af[cb][i], acc[i][j], MfmaFmt<FMT>::kCode, MfmaFmt<FMT>::kCode, 0, sbs[j], 0, sa[i]);
-      sched_fence();
-    }
-  }
+
+  // One stage: wait for it, then its MFMAs, with (ISSUE) the loads of stage
+  // it + S - 1 threaded between them.
+#define MX_STAGE(ISSUE)                                                                                   \
+  do {                                                                                                   \
+    if (ISSUE) wait_vmcnt<CF::kLoads * (S - 2)>(); /* stage it landed (this wave's part) */              \
+    else wait_vmcnt<0>();                                                                                \
+    stage_barrier(); /* ... and every wave's; buffer (it - 1) % S is free again */                       \
+    const uint8_t* sb = smem + (it % S) * CF::kStage;                                                    \
+    const int nb_ = (it + S - 1) % S;                                                                    \
+    /* scale dwords of this lane's rows (one per 128 K), read once per stage */                         \
+    uint32_t sda[CF::kScaleDw][CF::kMI], sdb[CF::kScaleDw][CF::kNJ];                                     \
+    _Pragma("unroll") for (int d = 0; d < CF::kScaleDw; ++d) {                                           \
+      _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                                \
+        sda[d][i] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + arow[i]) * 4);       \
+      _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j)                                                \
+        sdb[d][j] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + BM + brow[j]) * 4);  \
+    }                                                                                                    \
+    sched_fence();                                                                                       \
+    /* operand fragments double-buffered in registers: the reads of K step */                           \
+    /* ks + 1 are in flight while the MFMAs of step ks run */                                            \
+    v8i af[2][CF::kMI], bf[2][CF::kNJ];                                                                  \
+    _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                                  \
+      af[0][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], 0, g); \
+    _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j)                                                  \
+      bf[0][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], 0, g); \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                                  \
+      const int cb = ks & 1;                                                                             \
+      if (ks + 1 < KS) {                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                              \
+          af[cb ^ 1][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], ks + 1, g); \
+        _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j)                                              \
+          bf[cb ^ 1][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], ks + 1, g); \
+      }                                                                                                  \
+      sched_fence(); /* the reads above are issued before the MFMAs below */                             \
+      /* E8M0 byte of K block 2 ks + g of the stage (k0 % 128 == 0 at every stage start) */             \
+      const int bi = 2 * ks;                                                                             \
+      int sa[CF::kMI], sbs[CF::kNJ];                                                                     \
+      _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i) sa[i] = (int)(sda[bi >> 2][i] >> (8 * ((bi & 3) + g))); \
+      _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j) sbs[j] = (int)(sdb[bi >> 2][j] >> (8 * ((bi & 3) + g))); \
+      _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                                \
+      _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j) {                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                     \
+            bf[cb][j], af[cb][i], acc[i][j], MfmaFmt<FMT>::kCode, MfmaFmt<FMT>::kCode, 0, sbs[j], 0, sa[i]); \
+        const int f_ = i * CF::kNJ + j;                                                                  \
+        if (ISSUE && f_ % kEvery == kEvery - 1 && f_ / kEvery < kPer) {                                  \
+          const int q_ = ks * kPer + f_ / kEvery;                                                        \
+          if (q_ < CF::kLoads) {                                                                         \
+            sched_fence();                                                                               \
+            MX_PIECE(it + S - 1, nb_, q_);                                                               \
+            sched_fence();                                                                               \
+          }                                                                                              \
+        }                                                                                                \
+      }                                                                                                  \
+      sched_fence();                                                                                     \
+    }                                                                                                    \
+  } while (0)
+
+  int it = 0;
+  for (; it + S - 1 < nk; ++it) MX_STAGE(true);
+  for (; it < nk; ++it) MX_STAGE(false);
+#undef MX_STAGE
+#undef MX_PIECE
 #undef MX_ISSUE
   __syncthreads();  // all wavefronts are done with the stage ring before the epilogue reuses LDS
 
