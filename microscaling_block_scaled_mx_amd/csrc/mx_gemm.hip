@@ -97,20 +97,22 @@ struct Cfg {
 };
 
 // Position of logical 16-byte chunk c of row r among the row's NCH stored
-// chunks, chosen so that the same chunk of 8 (16) consecutive rows falls in
-// distinct LDS banks:  NCH = 8: c ^ ((r ^ (r >> 3)) & 7);  NCH = 4:
-// c ^ (((r >> 1) ^ (r >> 3)) & 3);  NCH = 6: (c + ((r >> 2) & 1)) % 6.
+// chunks, chosen so that reads of one chunk by consecutive rows spread over
+// the 64 banks of the LDS:  NCH = 8: c ^ ((r ^ (r >> 3)) & 7);  NCH = 4:
+// c ^ (((r >> 1) ^ (r >> 3)) & 3);  NCH = 6 (96-byte rows, whose bases repeat
+// every 8 rows modulo 64 banks): (c + ((r >> 3) & 1)) % 6, which moves rows
+// 8..15 of every 16 by one 4-bank step.
 template <int NCH>
 __device__ __forceinline__ int chunk_pos(int r, int c) {
   static_assert(NCH == 4 || NCH == 6 || NCH == 8, "chunks per row");
-  if constexpr (NCH == 6) { const int q = c + ((r >> 2) & 1); return q >= 6 ? q - 6 : q; }
+  if constexpr (NCH == 6) { const int q = c + ((r >> 3) & 1); return q >= 6 ? q - 6 : q; }
   else if constexpr (NCH == 8) return c ^ ((r ^ (r >> 3)) & 7);
   else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
 }
 // Inverse: the logical chunk stored at position pos of row r.
 template <int NCH>
 __device__ __forceinline__ int chunk_at(int r, int pos) {
-  if constexpr (NCH == 6) { const int q = pos - ((r >> 2) & 1); return q < 0 ? q + 6 : q; }
+  if constexpr (NCH == 6) { const int q = pos - ((r >> 3) & 1); return q < 0 ? q + 6 : q; }
   else return chunk_pos<NCH>(r, pos);  // the XOR permutations are involutions
 }
 
@@ -174,8 +176,10 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* rowp, int r, int ks, i
     const v4i b = *reinterpret_cast<const v4i*>(rowp + 16 * chunk_pos<NCH>(r, 4 * ks + 2 + g));
     v = v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   } else if constexpr (FMT == kE2M1) {  // chunk 2 ks + g
+    // the instruction reads 4 dwords of an E2M1 operand: the upper half is
+    // left undefined so that those registers stay free
     const v4i a = *reinterpret_cast<const v4i*>(rowp + 16 * chunk_pos<NCH>(r, 2 * ks + g));
-    v = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+    v = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
   } else {  // 24 bytes = 8-byte pieces 6 ks + 3 g + {0, 1, 2}
     v2i q[3];
 #pragma unroll
@@ -183,7 +187,10 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* rowp, int r, int ks, i
       const int piece = 6 * ks + 3 * g + k;
       q[k] = *reinterpret_cast<const v2i*>(rowp + 16 * chunk_pos<NCH>(r, piece >> 1) + 8 * (piece & 1));
     }
-    v = v8i{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, 0, 0};
+    // the instruction reads 6 dwords of an E2M3 operand
+    const v4i q01 = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3);
+    const v4i q2 = __builtin_shufflevector(q[2], q[2], 0, 1, -1, -1);
+    v = __builtin_shufflevector(q01, q2, 0, 1, 2, 3, 4, 5, -1, -1);
   }
   return v;
 }
