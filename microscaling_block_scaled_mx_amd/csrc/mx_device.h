@@ -81,51 +81,6 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t amax_bits) {
   return amax_bits >= 0x7f800000u ? 0xffu : (uint32_t)(X + 127);
 }
 
-// 2^-X as a binary32 (X in [-127, 125] from the selection above, so the
-// result is always a normal number).
-__device__ __forceinline__ float inv_scale(uint32_t byte) {
-  return __uint_as_float((254u - byte) << 23);
-}
-
-// ------------------------------------------------------------------ encode
-// Encode a scaled value v (|v| within the format's range up to saturation):
-// round to the nearest code, ties to the even code, saturate at the largest
-// finite magnitude, keep the sign (negative values rounding to zero give the
-// negative-zero code).  With E = max(floor(log2 |v|), emin) the code is
-// rint(|v| * 2^(mant - E)) + ((E - emin) << mant): inside one binade the
-// codes are evenly spaced, and a round-up across a binade edge lands on the
-// next binade's first code.
-template <int FMT>
-__device__ __forceinline__ uint32_t encode(float v) {
-  using T = FmtTraits<FMT>;
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 31) ? T::kSign : 0u;
-  uint32_t a = u & 0x7fffffffu;
-  int E = (int)(a >> 23) - 127;
-  E = E < T::kEmin ? T::kEmin : E;
-  E = E > 8 ? 8 : E;  // |v| <= 512 by construction; keeps the factor normal
-  float f = __uint_as_float((uint32_t)(127 + T::kMant - E) << 23);
-  float t = __uint_as_float(a) * f;
-  uint32_t code = (uint32_t)(int)__builtin_rintf(t) + ((uint32_t)(E - T::kEmin) << T::kMant);
-  code = code > T::kMaxCode ? T::kMaxCode : code;
-  return code | sign;
-}
-
-// ------------------------------------------------------------------ packing
-// Pack 32 codes of one block into the in-memory layout (dwords, little
-// endian): E2M1 4 dwords, E2M3 6 dwords, E4M3 8 dwords.
-template <int FMT>
-__device__ __forceinline__ void pack32(const uint32_t (&c)[32], uint32_t (&w)[FmtTraits<FMT>::kBits]) {
-  constexpr int B = FmtTraits<FMT>::kBits;
-#pragma unroll
-  for (int i = 0; i < B; ++i) w[i] = 0u;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const int bit = j * B, wd = bit >> 5, off = bit & 31;
-    w[wd] |= c[j] << off;
-    if (off + B > 32) w[wd + 1] |= c[j] >> (32 - off);
-  }
-}
 
 // ------------------------------------------------------------------ Hadamard
 // Normalised 32-point Walsh-Hadamard rotation in Sylvester order ([P1]
@@ -152,21 +107,81 @@ __device__ __forceinline__ void hadamard32(float (&y)[32]) {
 
 // ------------------------------------------------------------------ quantize one block
 // v: 32 values (prologue applied, bf16-rounded, rotated if asked).
-// Returns the scale byte; fills the packed words.
+// Returns the scale byte; fills the packed words (E2M1 4 dwords, element 2j
+// in the low nibble of byte j; E2M3 6 dwords, a little-endian 6-bit stream;
+// E4M3 8 dwords, one byte per element).
+//
+// The codes come from the gfx950 scaled conversions, which compute x / 2^X
+// exactly and round it to the format's nearest code, ties to the even code,
+// saturating at the largest magnitude and keeping the sign (-0 included).
+// That was checked against the nearest-even encoding rule over every code,
+// every midpoint and its neighbours, saturation, signed zeros and
+// denormals.  Two adjustments: E4M3 returns NaN past 448 instead of
+// saturating, so a FLOOR-scaled block (where |x| / 2^X < 512) is clamped to
+// +-448 * 2^X first; and 2^-127 is not a normal binary32, so a block with
+// X = -127 is converted as (x * 2^64) / 2^-63.  A NaN/Inf block gets zero
+// codes.
 template <int FMT, int MODE>
 __device__ __forceinline__ uint32_t quant_block(const float (&v)[32], uint32_t (&w)[FmtTraits<FMT>::kBits]) {
+  constexpr int B = FmtTraits<FMT>::kBits;
   uint32_t amax = 0u;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+    const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
     amax = amax > b ? amax : b;
   }
   const uint32_t s = scale_byte<FMT, MODE>(amax);
-  const float f = inv_scale(s == 0xffu ? 127u : s);
-  uint32_t c[32];
+#if defined(__HIP_DEVICE_COMPILE__)
+  const bool tiny = s == 0u;
+  const float pre = tiny ? 0x1p64f : 1.0f;
+  const float sc = __uint_as_float((tiny ? 64u : (s == 0xffu ? 127u : s)) << 23);  // 2^X (2^-63 if tiny)
+  float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) c[i] = (s == 0xffu) ? 0u : encode<FMT>(v[i] * f);
-  pack32<FMT>(c, w);
+  for (int i = 0; i < 32; ++i) x[i] = v[i] * pre;
+  if constexpr (FMT == kE4M3 && MODE == kFloor) {
+    const float bound = 448.0f * sc;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __builtin_fminf(__builtin_fmaxf(x[i], -bound), bound);
+  }
+  if constexpr (FMT == kE2M1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t q = 0u;
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[8 * d + 0], x[8 * d + 1], sc, 0);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[8 * d + 2], x[8 * d + 3], sc, 1);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[8 * d + 4], x[8 * d + 5], sc, 2);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[8 * d + 6], x[8 * d + 7], sc, 3);
+      w[d] = q;
+    }
+  } else if constexpr (FMT == kE4M3) {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      s2 q = {0, 0};
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, x[4 * d + 0], x[4 * d + 1], sc, false);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, x[4 * d + 2], x[4 * d + 3], sc, true);
+      w[d] = __builtin_bit_cast(uint32_t, q);
+    }
+  } else {
+    // the conversion interleaves its two 16-value operands (slot 2i <- a[i],
+    // slot 2i + 1 <- b[i]): even elements go in a, odd ones in b
+    typedef float f16v __attribute__((ext_vector_type(16)));
+    typedef int i6v __attribute__((ext_vector_type(6)));
+    f16v a, b;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a[i] = x[2 * i];
+      b[i] = x[2 * i + 1];
+    }
+    const i6v q = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, sc);
+#pragma unroll
+    for (int d = 0; d < 6; ++d) w[d] = (uint32_t)q[d];
+  }
+  if (s == 0xffu) {
+#pragma unroll
+    for (int d = 0; d < B; ++d) w[d] = 0u;
+  }
+#endif
   return s;
 }
 
