@@ -10,16 +10,17 @@
 //      gemm": rowwise 1x32 and columnwise 32x1 quantization, RCEIL scales,
 //      NaN-propagating amax (commit messages).
 //
-// Work split.  One 256-thread workgroup owns a 64-row x 128-column tile.
-//  1. Load: each thread reads four 16-byte chunks (8 bf16) -- a row of the
+// Work split.  One 256-thread workgroup owns a 128-row x 128-column tile.
+//  1. Load: each thread reads eight 16-byte chunks (8 bf16) -- a row of the
 //     tile is 16 chunks, so a wavefront covers 4 rows x 256 B per load, fully
 //     coalesced -- applies the prologue in registers, rounds to bf16 and
 //     writes the tile to LDS.  The prologue output exists only on chip.
-//  2. Row pass: thread t quantizes the 1x32 block (row t/4, block t%4).
-//  3. Column pass: thread t quantizes the 32x1 block (column t%128, row block
-//     t/128); adjacent lanes hold adjacent columns, so the LDS reads are
-//     conflict-free; its codes land in row (c0 + column) of the transposed
-//     operand.
+//  2. Row pass: threads quantize the 1x32 blocks (row q/4, block q%4).
+//  3. Column pass: threads quantize the 32x1 blocks (column q/4, row block
+//     q%4), written transposed as a K-major operand.
+//     In both passes the four blocks a row or column has in the tile sit in
+//     four adjacent lanes, so each store instruction writes 16 runs of 4
+//     consecutive blocks plus 16 whole scale dwords.
 // Rows/columns past R/C (multiples of 32) are masked per chunk.
 #include "mx_device.h"
 #include "mx_kernels.h"
@@ -28,144 +29,184 @@ namespace mx {
 
 namespace {
 
-constexpr int kTileR = 64, kTileC = 128;
-constexpr int kPitch = kTileC * 2 + 16;  // bytes per LDS row (16 B pad)
+constexpr int kTileR = 128, kTileC = 128;
+// bytes per LDS row: 256 B of data + 16 B pad; every 32-row block is
+// shifted by a further 32 B so that the four row blocks of a column read
+// in one column-pass instruction fall in different banks
+constexpr int kPitch = kTileC * 2 + 16;
+constexpr int kBlockSkew = 32;
+constexpr int kTileBytes = kTileR * kPitch + 3 * kBlockSkew;
+constexpr int kChunksPerRow = kTileC / 8;  // 16-byte chunks (8 bf16) per tile row
+constexpr int kLoads = kTileR * kChunksPerRow / 256;  // chunks per thread
+__device__ __forceinline__ int lds_row(int row) { return row * kPitch + (row >> 5) * kBlockSkew; }
 
 struct Chunk8 {
   uint32_t w[4];  // 8 bf16, element 2i in the low half of w[i]
 };
 
-__device__ __forceinline__ Chunk8 ld_chunk(const uint16_t* p) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
+// Raw input chunks of one tile position: up to three bf16 inputs.
+template <int PRO>
+struct Raw {
+  static constexpr int kN = (PRO == kDGelu || PRO == kSwiglu) ? 2 : (PRO == kDSwiglu ? 3 : 1);
+  uint4 in[kN];
+};
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ Chunk8 as_chunk(const uint4 v) {
   Chunk8 c;
   c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
   return c;
 }
 
+// Global loads of the inputs behind logical chunk (r, c..c+7).
 template <int PRO>
-__device__ __forceinline__ Chunk8 prologue_chunk(const PackParams& p, const uint16_t* xb, const uint16_t* ab,
-                                                 int64_t r, int64_t c) {
-  Chunk8 out;
-  if constexpr (PRO == kIdentity) {
-    out = ld_chunk(xb + r * p.C + c);
-  } else if constexpr (PRO == kGelu) {
-    Chunk8 h = ld_chunk(xb + r * p.C + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = f32_to_bf16(gelu_bf16(bf16_lo(h.w[i])));
-      uint32_t hi = f32_to_bf16(gelu_bf16(bf16_hi(h.w[i])));
-      out.w[i] = lo | (hi << 16);
-    }
+__device__ __forceinline__ Raw<PRO> load_raw(const PackParams& p, const uint16_t* xb, const uint16_t* ab, int64_t r,
+                                             int64_t c) {
+  Raw<PRO> q;
+  if constexpr (PRO == kIdentity || PRO == kGelu) {
+    q.in[0] = ld16(xb + r * p.C + c);
   } else if constexpr (PRO == kDGelu) {
-    Chunk8 d = ld_chunk(xb + r * p.C + c);
-    Chunk8 h = ld_chunk(ab + r * p.C + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = f32_to_bf16(dgelu_bf16(bf16_lo(d.w[i]), bf16_lo(h.w[i])));
-      uint32_t hi = f32_to_bf16(dgelu_bf16(bf16_hi(d.w[i]), bf16_hi(h.w[i])));
-      out.w[i] = lo | (hi << 16);
-    }
-  } else if constexpr (PRO == kSwiglu) {
-    // x = H [R][2C] = [gate | up]
-    Chunk8 g = ld_chunk(xb + r * 2 * p.C + c);
-    Chunk8 u = ld_chunk(xb + r * 2 * p.C + p.C + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = f32_to_bf16(swiglu_bf16(bf16_lo(g.w[i]), bf16_lo(u.w[i])));
-      uint32_t hi = f32_to_bf16(swiglu_bf16(bf16_hi(g.w[i]), bf16_hi(u.w[i])));
-      out.w[i] = lo | (hi << 16);
-    }
+    q.in[0] = ld16(xb + r * p.C + c);
+    q.in[1] = ld16(ab + r * p.C + c);
+  } else if constexpr (PRO == kSwiglu) {  // x = H [R][2C] = [gate | up]
+    q.in[0] = ld16(xb + r * 2 * p.C + c);
+    q.in[1] = ld16(xb + r * 2 * p.C + p.C + c);
   } else {  // kDSwiglu: C = 2F, x = dz [R][F], aux = H [R][2F]
     const int64_t F = p.C / 2;
-    const bool gate = c < F;
-    const int64_t j = gate ? c : c - F;
-    Chunk8 dz = ld_chunk(xb + r * F + j);
-    Chunk8 g = ld_chunk(ab + r * p.C + j);
-    Chunk8 u = ld_chunk(ab + r * p.C + F + j);
+    const int64_t j = c < F ? c : c - F;
+    q.in[0] = ld16(xb + r * F + j);
+    q.in[1] = ld16(ab + r * p.C + j);
+    q.in[2] = ld16(ab + r * p.C + F + j);
+  }
+  return q;
+}
+
+// The prologue on one chunk, each result rounded to bf16 ([P1] commit
+// messages: the activation epilogue becomes the packer's prologue).
+template <int PRO>
+__device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<PRO>& q, int64_t c) {
+  if constexpr (PRO == kIdentity) {
+    return as_chunk(q.in[0]);
+  } else {
+    Chunk8 out;
+    const Chunk8 x = as_chunk(q.in[0]);
+    const Chunk8 y = as_chunk(q.in[Raw<PRO>::kN > 1 ? 1 : 0]);
+    const Chunk8 u = as_chunk(q.in[Raw<PRO>::kN - 1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float lo, hi;
-      if (gate) {
-        lo = dswiglu_gate_bf16(bf16_lo(dz.w[i]), bf16_lo(g.w[i]), bf16_lo(u.w[i]));
-        hi = dswiglu_gate_bf16(bf16_hi(dz.w[i]), bf16_hi(g.w[i]), bf16_hi(u.w[i]));
+      if constexpr (PRO == kGelu) {
+        lo = gelu_bf16(bf16_lo(x.w[i]));
+        hi = gelu_bf16(bf16_hi(x.w[i]));
+      } else if constexpr (PRO == kDGelu) {
+        lo = dgelu_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]));
+        hi = dgelu_bf16(bf16_hi(x.w[i]), bf16_hi(y.w[i]));
+      } else if constexpr (PRO == kSwiglu) {
+        lo = swiglu_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]));
+        hi = swiglu_bf16(bf16_hi(x.w[i]), bf16_hi(y.w[i]));
       } else {
-        lo = dswiglu_up_bf16(bf16_lo(dz.w[i]), bf16_lo(g.w[i]));
-        hi = dswiglu_up_bf16(bf16_hi(dz.w[i]), bf16_hi(g.w[i]));
+        if (c < p.C / 2) {
+          lo = dswiglu_gate_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]), bf16_lo(u.w[i]));
+          hi = dswiglu_gate_bf16(bf16_hi(x.w[i]), bf16_hi(y.w[i]), bf16_hi(u.w[i]));
+        } else {
+          lo = dswiglu_up_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]));
+          hi = dswiglu_up_bf16(bf16_hi(x.w[i]), bf16_hi(y.w[i]));
+        }
       }
-      out.w[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+      // results are exact bf16 values
+      out.w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
     }
+    return out;
   }
-  return out;
 }
 
+// One workgroup packs one 128 x 128 tile of one batch entry.
 template <int FMT, int MODE, int HAD, int PRO>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
   constexpr int B = FmtTraits<FMT>::kBits;
   const int t = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.y * kTileR, c0 = (int64_t)blockIdx.x * kTileC;
   const int64_t z = blockIdx.z;
-  // per-problem bases
   const int64_t in_cols = (PRO == kSwiglu) ? 2 * p.C : (PRO == kDSwiglu ? p.C / 2 : p.C);
   const uint16_t* xb = p.x + z * p.R * in_cols;
   const uint16_t* ab = p.aux ? p.aux + z * p.R * p.C : nullptr;
 
-  // 1. load + prologue -> LDS
+  // 1. load + prologue -> LDS (rows / columns past R / C are zero)
+  Raw<PRO> raw[kLoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int q = t + 256 * i;
-    const int row = q >> 4, ch = q & 15;
+    const int64_t r = r0 + q / kChunksPerRow, c = c0 + (q % kChunksPerRow) * 8;
+    if (r < p.R && c < p.C) raw[i] = load_raw<PRO>(p, xb, ab, r, c);
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int q = t + 256 * i;
+    const int row = q / kChunksPerRow, ch = q % kChunksPerRow;
     const int64_t r = r0 + row, c = c0 + ch * 8;
     Chunk8 v;
     if (r < p.R && c < p.C) {
-      v = prologue_chunk<PRO>(p, xb, ab, r, c);
+      v = apply_prologue<PRO>(p, raw[i], c);
     } else {
       v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u;
     }
-    *reinterpret_cast<uint4*>(tile + row * kPitch + ch * 16) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+    *reinterpret_cast<uint4*>(tile + lds_row(row) + ch * 16) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
   }
   __syncthreads();
 
-  // 2. row pass: block (row t/4, blk t%4) along dim 1
+  // 2. row pass: blocks (row q/4, blk q%4) along dim 1, q = t, t + 256; the
+  //    four blocks of a row come from four adjacent lanes, so their codes and
+  //    their scale dword are written as one contiguous run
   if (p.row_codes) {
-    const int row = t >> 2, blk = t & 3;
-    const int64_t r = r0 + row, c = c0 + blk * 32;
-    uint8_t* scales = p.row_scales + z * scale_bytes(p.R, p.C) + scale_offset(r, c / 32, p.R);
-    if (r < p.R && c < p.C) {
-      float v[32];
-      lds_row_block(tile, kPitch, row, blk * 32, v);
-      uint8_t* codes = p.row_codes + z * p.R * (p.C * B / 8) + r * (p.C * B / 8) + c * B / 8;
-      quant_store<FMT, MODE, HAD>(v, codes, scales);
-    } else if (r < p.R) {
-      *scales = 0;  // pad byte of the row's last scale dword (the tile spans exactly one dword)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = t + 256 * h;
+      const int row = q >> 2, blk = q & 3;
+      const int64_t r = r0 + row, c = c0 + blk * 32;
+      if (r < p.R) {
+        uint8_t* scales = p.row_scales + z * scale_bytes(p.R, p.C) + scale_offset(r, c / 32, p.R);
+        if (c < p.C) {
+          float v[32];
+          lds_row_block(tile + lds_row(row), 0, 0, blk * 32, v);
+          uint8_t* codes = p.row_codes + z * p.R * (p.C * B / 8) + r * (p.C * B / 8) + c * B / 8;
+          quant_store<FMT, MODE, HAD>(v, codes, scales);
+        } else {
+          *scales = 0;  // pad byte of the row's last scale dword (a tile spans one dword)
+        }
+      }
     }
   }
 
-  // 3. column pass: block (column t%128, rows 32*(t/128) .. +31) along dim 0
+  // 3. column pass: blocks (column q/4, rows 32*(q%4) .. +31) along dim 0,
+  //    q = t, t + 256; a column's four blocks come from four adjacent lanes
   if (p.col_codes || p.partials) {
-    const int col = t & 127, blk = t >> 7;
-    const int64_t c = c0 + col, r = r0 + blk * 32;
-    if (c < p.C) {
-      // pad bytes of the column's last scale dword: a dword spans 4 row
-      // blocks = two 64-row tiles; the even tile writes the odd one's bytes
-      // as 0 when that tile does not exist, and a block past R is 0 as well
-      uint8_t* cscale = p.col_codes ? p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C) : nullptr;
-      if (cscale && r >= p.R) *cscale = 0;
-      if (cscale && (blockIdx.y & 1) == 0 && r0 + kTileR >= p.R) cscale[2] = 0;
-    }
-    if (c < p.C && r < p.R) {
-      float v[32];
-      lds_col_block(tile, kPitch, blk * 32, col, v);
-      if (p.partials) {
-        float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) part = part + v[i];
-        p.partials[z * (p.R / 32) * p.C + (r / 32) * p.C + c] = part;
-      }
-      if (p.col_codes) {
-        uint8_t* codes = p.col_codes + z * p.C * (p.R * B / 8) + c * (p.R * B / 8) + r * B / 8;
-        uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
-        quant_store<FMT, MODE, HAD>(v, codes, scales);
+    for (int h = 0; h < 2; ++h) {
+      const int q = t + 256 * h;
+      const int col = q >> 2, blk = q & 3;
+      const int64_t c = c0 + col, r = r0 + blk * 32;
+      if (c < p.C) {
+        if (r < p.R) {
+          float v[32];
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(tile + lds_row(32 * blk)) + col;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(src[i * (kPitch / 2)]);
+          if (p.partials) {
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) part = part + v[i];
+            p.partials[z * (p.R / 32) * p.C + (r / 32) * p.C + c] = part;
+          }
+          if (p.col_codes) {
+            uint8_t* codes = p.col_codes + z * p.C * (p.R * B / 8) + c * (p.R * B / 8) + r * B / 8;
+            uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
+            quant_store<FMT, MODE, HAD>(v, codes, scales);
+          }
+        } else if (p.col_codes) {
+          // a 128-row tile spans one scale dword; blocks past R are pad
+          p.col_scales[z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C)] = 0;
+        }
       }
     }
   }
