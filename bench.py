@@ -18,7 +18,11 @@ MXFP6 MLP at M=8192 (3072 -> 12288 -> 3072), the MXFP4 sweep over the five
 Flux-12B block linears at M=16384 and the MXFP8 grouped SwiGLU MLP
 (G=8, D=2048, F=768, R=32768).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--extra all|none] [--no-cpu-baseline]
+The timed steps replay one captured HIP graph per input copy (--no-graph:
+eager launches); per-launch durations come from HIP events around each
+launch in a second loop over the same steps.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--extra all|none] [--no-cpu-baseline] [--no-graph]
 """
 import argparse
 import json
@@ -117,6 +121,44 @@ def time_steps(fn, steps, warmup, T):
     dt = time.perf_counter() - t0
     T.on = False
     return dt / steps
+
+
+def capture_steps(step, copies):
+    """One HIP graph per input copy, each holding one whole step (the six
+    launches), so that the timed loop replays launches without host work in
+    between.  The captured calls are the same C-ABI entry points, enqueued
+    on torch's capture stream."""
+    import torch
+    T = Timer()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(copies):
+            step.run(c, T)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.run(c, T)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graph_steps(graphs, steps, warmup):
+    """Wall time per step of `steps` replays (rotating input copies), between
+    two device synchronizations."""
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[(warmup + i) % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -297,6 +339,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extra", choices=["all", "none"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--only", default=None,
                     help="profile one kernel config instead: gemm:FMT:M:N:K or pack:FMT:R:C (FMT = 4, 6 or 8)")
     args = ap.parse_args()
@@ -319,7 +362,14 @@ def main():
     step = LinearStep(mx, M, N, K, mx.E2M3, mx.FLOOR, True, 201)
     print(f"[bench] linear MXFP6 {M}x{N}x{K}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
-    sec = time_steps(lambda i: step.run(i, T), args.steps, args.warmup, T)
+    if args.no_graph:
+        sec = time_steps(lambda i: step.run(i, T), args.steps, args.warmup, Timer())
+    else:
+        graphs = capture_steps(step, len(step.inp))
+        sec = time_graph_steps(graphs, args.steps, args.warmup)
+    # per-launch durations: HIP events around each launch on the launch stream
+    # (separate loop, so that the event records do not stretch the steps)
+    time_steps(lambda i: step.run(i, T), args.steps, 1, T)
     k = T.summary()
     value = step.flops() / sec / 1e12
     gemm_us = float(np.mean([k["gemm_fwd"], k["gemm_dgrad"], k["gemm_wgrad"]]))
@@ -335,6 +385,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp6 (e2m3 x e2m3, fp32 accumulate)", "data": "synthetic",
+        "launch": "eager" if args.no_graph else "hip_graph (one captured step per input copy)",
         "config": {"workload": "MXFP6 linear (E2M3, FLOOR, Hadamard-32) X[4096,3072] W[3072,3072]: dual packs "
                                "of X, W, dY + fwd, dgrad, wgrad GEMMs, bf16 out",
                    "M": M, "N": N, "K": K, "format": "mxfp6", "gemm_flops_per_step": step.flops()},
