@@ -170,6 +170,11 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
  *  c            output [M][ldc] of dtype c_dtype (MX_BF16 rounds to nearest
  *               even; MX_F32 stores the accumulator).  ldc >= N, a multiple
  *               of 8.
+ * Tiling: the output is cut into 256x256, 256x192, 192x256, 192x192 or
+ * 256x128 tiles, whichever costs the fewest rounds x tile area with one tile
+ * per compute unit; the environment variable MX_DENSE_TILE=<BM>x<BN>
+ * restricts the choice to one of these shapes when it divides M x N (a test
+ * hook; results agree to the tolerance of the accumulation order only).
  * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
  * MX_ERR_INDEX_OVERFLOW, MX_ERR_DEVICE, MX_ERR_LAUNCH.
  */

@@ -44,6 +44,10 @@
 // column l%32; the kernel passes the B fragment as X and the A fragment as
 // Y, so a lane holds C row l%32 and the four consecutive columns
 // 8*(i/4) + 4*(l/32) + {0..3} for each i/4 -- 8 contiguous bytes of bf16.
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -73,17 +77,24 @@ struct Cfg {
   static constexpr int kRowBytes = kBK * kBits / 8;      // 128 / 96 / 128 bytes per row per stage
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
   static constexpr int kScaleDw = kBK / 128;             // scale dwords (4 blocks each) per row per stage
+  // 16-byte loads per thread per stage; a tile side whose chunks do not fill
+  // whole loads (192 rows of 96 bytes) leaves the last load of some
+  // wavefronts idle: they load a valid chunk into a junk area, so that every
+  // wavefront issues the same number of loads (the vmcnt waits count them)
+  static constexpr int kAIters = (BM * kChunks + kThreads - 1) / kThreads;
+  static constexpr int kBIters = (BN * kChunks + kThreads - 1) / kThreads;
+  static constexpr int kARem = (BM * kChunks) % kThreads;  // slots of a partial last load (0: none)
+  static constexpr int kBRem = (BN * kChunks) % kThreads;
+  static_assert(kARem % 64 == 0 && kBRem % 64 == 0, "partial loads cover whole wavefronts");
   static constexpr int kAOff = 0;
   static constexpr int kBOff = BM * kRowBytes;
   static constexpr int kSOff = kBOff + BN * kRowBytes;   // scale dwords: [dword][A rows, then B rows] (512 slots)
-  static constexpr int kStage = kSOff + kScaleDw * 512 * 4;
+  static constexpr int kJOff = kSOff + kScaleDw * 512 * 4;
+  static constexpr int kStage = kJOff + ((kARem || kBRem) ? 1024 : 0);
   static constexpr int kStages = (4 * kStage <= 160 * 1024) ? 4 : ((3 * kStage <= 160 * 1024) ? 3 : 2);
   static constexpr int kWM = BM / 2, kWN = BN / 2;
   static constexpr int kMI = kWM / 32, kNJ = kWN / 32;
-  static constexpr int kAIters = BM * kChunks / kThreads;  // 16-byte loads per thread per stage
-  static constexpr int kBIters = BN * kChunks / kThreads;
   static constexpr int kLoads = kAIters + kBIters + 2 * kScaleDw;  // vector-memory instructions per stage per wave
-  static_assert(BM * kChunks % kThreads == 0 && BN * kChunks % kThreads == 0, "tile / thread mismatch");
   static_assert(BM + BN <= 512, "scale slots");
   // epilogue staging
   static constexpr int kCPitch = kWN * 2 + 8;         // bf16 store: per-wave kWM x kWN tile
@@ -280,12 +291,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < CF::kAIters; ++i) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
-    a_off[i] = (uint32_t)((m0 + r) * row_bytes + 16 * chunk_at<CF::kChunks>(r, pos));
+    const int rr = r < BM ? r : 0;  // junk slots read a valid chunk
+    a_off[i] = (uint32_t)((m0 + rr) * row_bytes + 16 * chunk_at<CF::kChunks>(rr, pos));
   }
 #pragma unroll
   for (int i = 0; i < CF::kBIters; ++i) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
-    b_off[i] = (uint32_t)(b_row(r) * row_bytes + 16 * chunk_at<CF::kChunks>(r, pos));
+    const int rr = r < BN ? r : 0;
+    b_off[i] = (uint32_t)(b_row(rr) * row_bytes + 16 * chunk_at<CF::kChunks>(rr, pos));
   }
   // scale dwords (4 blocks of 32 along K, blocked layout): slot t and t + 256
   // of [A rows | B rows]; slots past BM + BN load row 0's dword into unused
@@ -311,10 +324,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     uint8_t* st_ = smem + (buf) * CF::kStage;                                                            \
     if ((q) < CF::kAIters) {                                                                             \
       const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
-      lds_dma16(p.a_codes + k0_ * kBits / 8 + a_off[i_], st_ + CF::kAOff + (i_ * 256 + wave_u * 64) * 16); \
+      const bool junk_ = CF::kARem && i_ == CF::kAIters - 1 && wave_u * 64 >= CF::kARem;                 \
+      lds_dma16(p.a_codes + k0_ * kBits / 8 + a_off[i_],                                                 \
+                st_ + (junk_ ? CF::kJOff : CF::kAOff + (i_ * 256 + wave_u * 64) * 16));                  \
     } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
       const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
-      lds_dma16(p.b_codes + k0_ * kBits / 8 + b_off[i_], st_ + CF::kBOff + (i_ * 256 + wave_u * 64) * 16); \
+      const bool junk_ = CF::kBRem && i_ == CF::kBIters - 1 && wave_u * 64 >= CF::kBRem;                 \
+      lds_dma16(p.b_codes + k0_ * kBits / 8 + b_off[i_],                                                 \
+                st_ + (junk_ ? CF::kJOff : CF::kBOff + (i_ * 256 + wave_u * 64) * 16));                  \
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
       const int d_ = e_ / 2, j_ = e_ % 2;                                                                \
@@ -644,14 +661,64 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Dense tile shape: the one whose rounds of one tile per compute unit cost
+// the least output area (rounds x BM x BN), larger tiles first on ties --
+// e.g. 4096 x 3072 takes 256 tiles of 256 x 192 in one round instead of 192
+// tiles of 256 x 256 on 192 of the 256 compute units.
+template <int FMT>
+hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
+  static constexpr int kShapes[5][2] = {{256, 256}, {256, 192}, {192, 256}, {192, 192}, {256, 128}};
+  const int64_t cus = cu_count();
+  // MX_DENSE_TILE=<BM>x<BN> restricts the choice to that shape (tests use it
+  // to cover every shape at small sizes); unset, or not dividing M x N, it
+  // has no effect
+  int force = -1;
+  if (const char* env = getenv("MX_DENSE_TILE")) {
+    int fm = 0, fn = 0;
+    if (sscanf(env, "%dx%d", &fm, &fn) == 2)
+      for (int i = 0; i < 5; ++i)
+        if (kShapes[i][0] == fm && kShapes[i][1] == fn && p.M % fm == 0 && p.N % fn == 0) force = i;
+  }
+  int best = -1;
+  int64_t best_cost = 0;
+  for (int i = 0; i < 5; ++i) {
+    const int bm = kShapes[i][0], bn = kShapes[i][1];
+    if (p.M % bm || p.N % bn || (force >= 0 && i != force)) continue;
+    const int64_t tiles = (p.M / bm) * (p.N / bn);
+    const int64_t cost = ((tiles + cus - 1) / cus) * bm * bn;
+    if (best < 0 || cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  switch (best) {
+    case 0: return launch_one<FMT, 256, 256, kDense, kEpiStore>(p, stream);
+    case 1: return launch_one<FMT, 256, 192, kDense, kEpiStore>(p, stream);
+    case 2: return launch_one<FMT, 192, 256, kDense, kEpiStore>(p, stream);
+    case 3: return launch_one<FMT, 192, 192, kDense, kEpiStore>(p, stream);
+    case 4: return launch_one<FMT, 256, 128, kDense, kEpiStore>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int FMT>
 hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream) {
-  if (mode == kDense) {
-    // 256 x 256 tiles once they fill the chip; 256 x 128 otherwise
-    const int64_t big = (p.M / 256) * (p.N / 256);
-    if (big >= 256) return launch_one<FMT, 256, 256, kDense, kEpiStore>(p, stream);
-    return launch_one<FMT, 256, 128, kDense, kEpiStore>(p, stream);
-  }
+  if (mode == kDense) return launch_dense<FMT>(p, stream);
   if (mode == kRaggedM) {
     if (epi == kEpiSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiSwiglu>(p, stream);
     if (epi == kEpiDSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiDSwiglu>(p, stream);

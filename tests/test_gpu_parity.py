@@ -192,6 +192,19 @@ def test_gemm_parity(mxl, orc, fmt, mode, had, shape):
     assert np.array_equal(c16, want16)
 
 
+@pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
+@pytest.mark.parametrize("tile", ["256x256", "256x192", "192x256", "192x192", "256x128"])
+def test_gemm_parity_every_tile_shape(mxl, orc, fmt, mode, had, tile, monkeypatch):
+    # the dense GEMM picks its tile shape from M, N and the compute-unit
+    # count; force each shape at a size all of them divide
+    monkeypatch.setenv("MX_DENSE_TILE", tile)
+    M, N, K = 768, 768, 512
+    ref, c32, c16 = gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed=900 + fmt, bias=True)
+    err = np.max(np.abs(c32.astype(np.float64) - ref)) / np.max(np.abs(ref))
+    assert err <= REL, err
+    assert np.array_equal(c16, I.f32_to_bf16_bits(c32))
+
+
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_gemm_exact_products_bitwise(mxl, orc, fmt):
     # one shared scale per operand and codes whose products are multiples of
