@@ -37,6 +37,22 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quantizer GB/s"
+# HBM bytes per GEMM launch of the headline step (mean of its three launches),
+# from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a plain copy
+# (profiles/mxfp6_gemm_pack_hbm_traffic.md); valid only for the GEMM sources
+# they were taken with
+GEMM_TRAFFIC = {"bytes_per_launch": 79.0e6, "sources_sha1": "36972c0dfe31d95f38bbc21d1cd97ff28dc20f99"}
+GEMM_SOURCES = ("mx_gemm.hip", "mx_device.h", "mx_kernels.h")
+
+
+def gemm_traffic():
+    """The measured traffic if the GEMM sources are unchanged since, else None."""
+    import hashlib
+    h = hashlib.sha1()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "microscaling_block_scaled_mx_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return GEMM_TRAFFIC["bytes_per_launch"] if h.hexdigest() == GEMM_TRAFFIC["sources_sha1"] else None
 PEAK_TFLOPS = {"fp4": 10100.0, "fp6": 10100.0, "fp8": 5000.0}  # MI355X dense MFMA
 HBM_GBS = 8000.0
 # algorithmic bytes per element of a pack: 2 B bf16 in + (bits/8 + 1/32) per output axis
@@ -305,6 +321,15 @@ def only(mx, spec, steps, warmup, T):
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     kind, fbits, *dims = spec.split(":")
+    if kind == "copy":  # plain device copy of fbits bytes: the reference for the traffic counters
+        n = int(fbits)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        sec = time_steps(lambda i: T.run("copy", dst.copy_, src), steps, warmup, T)
+        us = T.summary()["copy"]
+        print(json.dumps({"only": spec, "us": us, "gbs": 2 * n / (us * 1e-6) / 1e9, "ms_per_iter": sec * 1e3}),
+              flush=True)
+        return
     fmt = {"4": mx.E2M1, "6": mx.E2M3, "8": mx.E4M3}[fbits]
     mode = mx.RCEIL if fmt == mx.E4M3 else mx.FLOOR
     had = fmt == mx.E2M3
@@ -341,7 +366,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel config instead: gemm:FMT:M:N:K or pack:FMT:R:C (FMT = 4, 6 or 8)")
+                    help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C (FMT = 4, 6 or 8) "
+                         "or copy:BYTES (a plain device copy)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
@@ -391,7 +417,8 @@ def main():
                    "M": M, "N": N, "K": K, "format": "mxfp6", "gemm_flops_per_step": step.flops()},
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel<E2M3> (fwd/dgrad/wgrad launches, 77.3 GFLOP each)",
                      "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp6"], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": None},
+                     "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": gemm_traffic(),
+                     "traffic_unit": "bytes per launch (HBM read + write)"},
         "quantizer": {"kernel": "pack_kernel<E2M3, Hadamard> dual pack of X", "achieved_gbs":
                       round(pack_bytes / (k["pack_X"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
                       "frac": round(pack_bytes / (k["pack_X"] * 1e-6) / 1e9 / HBM_GBS, 4)},
