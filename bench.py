@@ -178,33 +178,28 @@ def time_graph_steps(graphs, steps, warmup):
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(step: LinearStep, rows=1024):
-    """The oracle (never tuned for this) on the host cores: full dual packs of
-    X, W, dY plus `rows` output rows of each GEMM; the full-step time is
-    extrapolated from the sampled rows."""
+def cpu_baseline(step: LinearStep, repeats=3):
+    """The oracle (never tuned for this) on the host cores, running the whole
+    headline step -- dual packs of X, W and dY, then all rows of the fwd,
+    dgrad and wgrad GEMMs -- `repeats` times (about 10 s on 16 cores)."""
     from oracle import oracle as orc
     X, W, dY = step.host
     M, N, K, f, m, h = step.M, step.N, step.K, step.fmt, step.mode, step.had
     t0 = time.perf_counter()
-    px = orc.quantize(X, M, K, f, m, h, row=True, col=True)
-    pw = orc.quantize(W, N, K, f, m, h, row=True, col=True)
-    pd = orc.quantize(dY, M, N, f, m, h, row=True, col=True)
-    t_pack = time.perf_counter() - t0
-    t_gemm = 0.0
-    # (A operand, B operand, M, N, K) of the fwd, dgrad and wgrad GEMMs
-    gemms = ((px, "row", pw, "row", M, N, K), (pd, "row", pw, "col", M, K, N), (pd, "col", px, "col", N, K, M))
-    for pa, sa, pb, sb, MM, NN, KK in gemms:
-        r = min(rows, MM)
-        t1 = time.perf_counter()
-        orc.gemm(pa[sa + "_codes"], pa[sa + "_scales"], pb[sb + "_codes"], pb[sb + "_scales"], MM, NN, KK, f,
-                 rows=np.arange(r))
-        t_gemm += (time.perf_counter() - t1) * (MM / r)
-    total = t_pack + t_gemm
+    for _ in range(repeats):
+        px = orc.quantize(X, M, K, f, m, h, row=True, col=True)
+        pw = orc.quantize(W, N, K, f, m, h, row=True, col=True)
+        pd = orc.quantize(dY, M, N, f, m, h, row=True, col=True)
+        # (A operand, B operand, M, N, K) of the fwd, dgrad and wgrad GEMMs
+        for pa, sa, pb, sb, MM, NN, KK in ((px, "row", pw, "row", M, N, K), (pd, "row", pw, "col", M, K, N),
+                                           (pd, "col", px, "col", N, K, M)):
+            orc.gemm(pa[sa + "_codes"], pa[sa + "_scales"], pb[sb + "_codes"], pb[sb + "_scales"], MM, NN, KK, f)
+    total = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return {"value": step.flops() / total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"full dual packs of X, W, dY ({t_pack:.1f} s) + {rows} output rows of each of the 3 GEMMs, "
-                      f"GEMM time scaled to all rows; step estimate {total:.1f} s",
-            "seconds_measured": round(time.perf_counter() - t0, 2)}
+    return {"value": step.flops() * repeats / total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{repeats} whole steps (dual packs of X, W, dY + all rows of the fwd, dgrad and wgrad "
+                      f"GEMMs), {total / repeats:.2f} s per step",
+            "seconds_measured": round(total, 2)}
 
 
 # ------------------------------------------------------------------ other workloads
