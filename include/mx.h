@@ -22,21 +22,24 @@
  *    Work is enqueued asynchronously on it; the call returns once enqueued.
  *  - bf16 tensors are row-major and dense.  Every device pointer must be
  *    16-byte aligned.
- *  - Packed operands are K-major ("rows x K"): codes [rows][K*bits/8] bytes
- *    with bits = 4, 6 or 8, and E8M0 scales, one byte per (row, 32-block b),
- *    in the blocked layout the GEMM reads: the four bytes of one 128-element
- *    K group form a dword (block b in byte b % 4), and the dwords of one K
- *    group are stored row after row, i.e. scales [ceil(K/128)][rows][4]
- *    with (row, b) at byte (b/4 * rows + row) * 4 + b % 4 (mx_scales_bytes
- *    bytes; pad bytes of a partial last group are 0).  As in [P4] (the
- *    grouped kernels' blocked E8M0 scale ABI), the quantizer writes the
- *    blocking the GEMM reads; a ragged-K group of rows [k0, k1), k0 and k1
- *    multiples of 128, is the run of K groups k0/128 .. k1/128 - 1.  Code layout within a
- *    row: E2M1 element 2j in the low nibble of byte j and 2j+1 in the high
- *    nibble; E2M3 a little-endian 6-bit stream, element j at bits
- *    [6j, 6j+6); E4M3 one byte per element.  Every GEMM computes
- *    C = A . B^T on two K-major operands (the NT layout of [P3],
- *    Troubleshooting).
+ *  - Packed operands ("rows x K", bits = 4, 6 or 8 per element) are stored
+ *    K-group-major, the layout the GEMM reads: K is cut into groups of 128
+ *    elements, and each group holds, row after row, the group's codes of
+ *    every row.  Codes: [ceil(K/128)][rows][16*bits] bytes, the 128 codes
+ *    of (row, group q) packed as below at byte (q * rows + row) * 16*bits
+ *    (mx_codes_bytes bytes).  E8M0 scales, one byte per (row, 32-block b):
+ *    [ceil(K/128)][rows][4], the four blocks of a group forming a dword,
+ *    (row, b) at byte (b/4 * rows + row) * 4 + b % 4 (mx_scales_bytes
+ *    bytes).  Pad bytes of a partial last group are 0.  A GEMM stage then
+ *    reads the codes and the scales of a panel of rows as contiguous runs.
+ *    As in [P4] (the grouped kernels' blocked E8M0 scale ABI), the
+ *    quantizer writes the blocking the GEMM reads.  A ragged-K group of
+ *    rows [k0, k1), k0 and k1 multiples of 128, is the run of K groups
+ *    k0/128 .. k1/128 - 1.  Packing of the codes within a group: E2M1
+ *    element 2j in the low nibble of byte j and 2j+1 in the high nibble;
+ *    E2M3 a little-endian 6-bit stream, element j at bits [6j, 6j+6); E4M3
+ *    one byte per element.  Every GEMM computes C = A . B^T on two such
+ *    operands (the NT layout of [P3], Troubleshooting).
  *  - Return value: MX_OK, or an mx_status error.  Arguments are validated on
  *    the host before anything is enqueued; on error nothing is enqueued and
  *    no output is touched.  There is no fallback path: a call the kernels
@@ -103,7 +106,7 @@ typedef enum { MX_GROUPED_RAGGED_M = 0, MX_GROUPED_RAGGED_K = 1 } mx_grouped_mod
 
 typedef enum { MX_EPI_NONE = 0, MX_EPI_SWIGLU = 1, MX_EPI_DSWIGLU = 2 } mx_epilogue;
 
-/* One packed operand: codes [rows][K*bits/8] bytes + blocked scales [ceil(K/128)][rows][4]. */
+/* One packed operand: codes [ceil(K/128)][rows][16*bits] + scales [ceil(K/128)][rows][4] bytes. */
 typedef struct {
   void* codes;
   void* scales;
@@ -289,7 +292,7 @@ const char* mx_status_str(int status);
 /* 1 if HIP device `device` is a gfx950 (MI355X-class) GPU, else 0. */
 int mx_device_supported(int device);
 /* Bytes of one packed operand's codes / blocked scales for rows x K in fmt (0 on bad input):
- * rows * K * bits / 8 and ceil(K/128) * rows * 4. */
+ * ceil(K/128) * rows * 16 * bits and ceil(K/128) * rows * 4. */
 int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K);
 int64_t mx_scales_bytes(int64_t rows, int64_t K);
 /* Library version string. */

@@ -375,7 +375,7 @@ int mx_device_supported(int device) { return device_state(device) == 1 ? 1 : 0; 
 int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K) {
   const int b = bits_of(fmt);
   if (!b || rows < 0 || K < 0 || K % 32) return 0;
-  return rows * (K * b / 8);
+  return mx::code_bytes(rows, K, b);
 }
 
 int64_t mx_scales_bytes(int64_t rows, int64_t K) {

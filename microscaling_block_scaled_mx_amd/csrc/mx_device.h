@@ -224,6 +224,15 @@ __device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t (&w)[Fm
   }
 }
 
+// Zero codes of one block (a pad block of a partial K group).
+template <int FMT>
+__device__ __forceinline__ void zero_block(uint8_t* dst) {
+  uint32_t w[FmtTraits<FMT>::kBits];
+#pragma unroll
+  for (int i = 0; i < FmtTraits<FMT>::kBits; ++i) w[i] = 0u;
+  store_block<FMT>(dst, w);
+}
+
 // Quantize 32 values and write codes + scale byte.
 template <int FMT, int MODE, int HAD>
 __device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* codes, uint8_t* scale) {

@@ -244,6 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   int64_t kbeg = 0, kend = p.K;
   int64_t b_row0 = 0;  // first B row of this tile's group
   int64_t b_soff = 0;  // byte offset of this tile's group in the B scales (one blocked array per group)
+  int64_t b_coff = 0;  // byte offset of this tile's group in the B codes (one K-group-major array per group)
   int64_t c_off = 0;   // element offset of this tile's group in C
   if constexpr (MODE == kRaggedM) {
     // offsets are a caller invariant; clamping keeps every access inside the
@@ -255,6 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     while (p.offsets[gi] <= m0) ++gi;
     b_row0 = (int64_t)gi * p.b_group_rows;
     b_soff = (int64_t)gi * scale_bytes(p.b_group_rows, p.ktot);
+    b_coff = (int64_t)gi * code_bytes(p.b_group_rows, p.ktot, kBits);
   }
   if constexpr (MODE == kRaggedK) {
     const int gi = blockIdx.z;
@@ -265,11 +267,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     if (kend < kbeg) kend = kbeg;
     c_off = (int64_t)gi * p.M * p.N;
   }
-  const int64_t row_bytes = p.ktot * kBits / 8;
   // rows of the A / B operands (of one group's B): the stride between K
-  // groups of their scales
+  // groups of their codes and scales
   const int64_t a_rows = p.M;
   const int64_t b_rows = MODE == kRaggedM ? p.b_group_rows : p.N;
+  constexpr int kGB = 16 * kBits;  // code bytes of one row in one 128-element K group
   const int nk = (int)((kend - kbeg) / CF::kBK);
 
   // LDS row r of the B tile -> global B row
@@ -285,20 +287,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   // ---------------------------------------------------------------- loads
   // Stage slot s (16-byte units, s = i * 256 + t for load i of thread t)
   // holds row s / kChunks, position s % kChunks, i.e. logical chunk
-  // chunk_at(row, position).  Byte offsets are 32-bit (operands < 2 GiB).
+  // chunk_at(row, position) of the row's stage segment.  Byte 16c of that
+  // segment lies in K group c*16/kGB of the stage, at byte 16c % kGB of the
+  // row's kGB-byte run.  Offsets from the stage's first K group are 32-bit
+  // (operands < 2 GiB).
   constexpr int BK = CF::kBK;
   uint32_t a_off[CF::kAIters], b_off[CF::kBIters];
 #pragma unroll
   for (int i = 0; i < CF::kAIters; ++i) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
     const int rr = r < BM ? r : 0;  // junk slots read a valid chunk
-    a_off[i] = (uint32_t)((m0 + rr) * row_bytes + 16 * chunk_at<CF::kChunks>(rr, pos));
+    const int c = chunk_at<CF::kChunks>(rr, pos);
+    a_off[i] = (uint32_t)(((16 * c) / kGB) * a_rows * kGB + (m0 + rr) * kGB + (16 * c) % kGB);
   }
 #pragma unroll
   for (int i = 0; i < CF::kBIters; ++i) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
     const int rr = r < BN ? r : 0;
-    b_off[i] = (uint32_t)(b_row(rr) * row_bytes + 16 * chunk_at<CF::kChunks>(rr, pos));
+    const int c = chunk_at<CF::kChunks>(rr, pos);
+    b_off[i] = (uint32_t)(b_coff + ((16 * c) / kGB) * b_rows * kGB + (b_row(rr) - b_row0) * kGB + (16 * c) % kGB);
   }
   // scale dwords (4 blocks of 32 along K, blocked layout): slot t and t + 256
   // of [A rows | B rows]; slots past BM + BN load row 0's dword into unused
@@ -325,12 +332,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     if ((q) < CF::kAIters) {                                                                             \
       const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
       const bool junk_ = CF::kARem && i_ == CF::kAIters - 1 && wave_u * 64 >= CF::kARem;                 \
-      lds_dma16(p.a_codes + k0_ * kBits / 8 + a_off[i_],                                                 \
+      lds_dma16(p.a_codes + (k0_ / 128) * a_rows * kGB + a_off[i_],                                      \
                 st_ + (junk_ ? CF::kJOff : CF::kAOff + (i_ * 256 + wave_u * 64) * 16));                  \
     } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
       const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
       const bool junk_ = CF::kBRem && i_ == CF::kBIters - 1 && wave_u * 64 >= CF::kBRem;                 \
-      lds_dma16(p.b_codes + k0_ * kBits / 8 + b_off[i_],                                                 \
+      lds_dma16(p.b_codes + (k0_ / 128) * b_rows * kGB + b_off[i_],                                      \
                 st_ + (junk_ ? CF::kJOff : CF::kBOff + (i_ * 256 + wave_u * 64) * 16));                  \
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
@@ -563,10 +570,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_row_block(zt, CF::kZPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = zb + 32 * blk;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + m * (p.F * QB / 8) + col * QB / 8,
+        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + code_offset(m, col, p.R, QB),
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + m * (p.F * QB / 8) + col * QB / 8,
+        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + code_offset(m, col, p.R, QB),
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
     }
     for (int q = t; q < ZC * (BM / 32); q += kThreads) {
@@ -575,10 +582,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_col_block(zt, CF::kZPitch, rb2 * 32, col, v);
       const int64_t cz = zb + col, m = m0 + 32 * rb2;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + cz * (p.R * QB / 8) + m * QB / 8,
+        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + code_offset(cz, m, p.F, QB),
                                     p.q_col_scales + scale_offset(cz, m / 32, p.F));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + cz * (p.R * QB / 8) + m * QB / 8,
+        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + code_offset(cz, m, p.F, QB),
                                     p.q_col_scales + scale_offset(cz, m / 32, p.F));
     }
   } else {  // kEpiDSwiglu
@@ -623,10 +630,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_row_block(half ? tu : tg, CF::kDPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = (half ? p.F : 0) + n0 + 32 * blk;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + m * (W * QB / 8) + col * QB / 8,
+        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + code_offset(m, col, p.R, QB),
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + m * (W * QB / 8) + col * QB / 8,
+        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + code_offset(m, col, p.R, QB),
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
     }
     for (int q = t; q < 2 * BN * (BM / 32); q += kThreads) {
@@ -636,10 +643,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_col_block(half ? tu : tg, CF::kDPitch, rb2 * 32, col, v);
       const int64_t cw = (half ? p.F : 0) + n0 + col, m = m0 + 32 * rb2;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + cw * (p.R * QB / 8) + m * QB / 8,
+        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + code_offset(cw, m, W, QB),
                                     p.q_col_scales + scale_offset(cw, m / 32, W));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + cw * (p.R * QB / 8) + m * QB / 8,
+        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + code_offset(cw, m, W, QB),
                                     p.q_col_scales + scale_offset(cw, m / 32, W));
     }
   }

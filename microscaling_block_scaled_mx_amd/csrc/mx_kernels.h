@@ -19,14 +19,27 @@ __host__ __device__ __forceinline__ int64_t scale_bytes(int64_t rows, int64_t K)
   return ((K / 32 + 3) / 4) * rows * 4;
 }
 
+// Codes use the same K-group-major order: the codes of one row's 128-element
+// K group take 16 * bits contiguous bytes (the plain packing of those 128
+// elements), and the groups of one K group are stored row after row --
+// [ceil(K/128)][rows][16 * bits] bytes.  A GEMM stage then reads a row
+// panel's codes as one contiguous run.  k is a multiple of 32 (a block
+// start); pad bytes of a partial last group are 0.
+__host__ __device__ __forceinline__ int64_t code_offset(int64_t row, int64_t k, int64_t rows, int bits) {
+  return ((k >> 7) * rows + row) * (16 * bits) + (k & 127) * bits / 8;
+}
+__host__ __device__ __forceinline__ int64_t code_bytes(int64_t rows, int64_t K, int bits) {
+  return ((K + 127) / 128) * rows * (16 * bits);
+}
+
 
 struct PackParams {
   const uint16_t* x;    // prologue input (bf16 bits)
   const uint16_t* aux;  // second prologue input or nullptr
   int64_t R, C;         // logical quantized tensor [R][C] per batch entry
-  uint8_t* row_codes;   // [R][C*bits/8] or nullptr
+  uint8_t* row_codes;   // K-group-major codes, rows R, K = C, or nullptr
   uint8_t* row_scales;  // blocked layout, rows R, K = C
-  uint8_t* col_codes;   // [C][R*bits/8] or nullptr
+  uint8_t* col_codes;   // K-group-major codes, rows C, K = R, or nullptr
   uint8_t* col_scales;  // blocked layout, rows C, K = R
   float* partials;      // [R/32][C] or nullptr
 };

@@ -166,13 +166,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
       const int64_t r = r0 + row, c = c0 + blk * 32;
       if (r < p.R) {
         uint8_t* scales = p.row_scales + z * scale_bytes(p.R, p.C) + scale_offset(r, c / 32, p.R);
+        uint8_t* codes = p.row_codes + z * code_bytes(p.R, p.C, B) + code_offset(r, c, p.R, B);
         if (c < p.C) {
           float v[32];
           lds_row_block(tile + lds_row(row), 0, 0, blk * 32, v);
-          uint8_t* codes = p.row_codes + z * p.R * (p.C * B / 8) + r * (p.C * B / 8) + c * B / 8;
           quant_store<FMT, MODE, HAD>(v, codes, scales);
         } else {
-          *scales = 0;  // pad byte of the row's last scale dword (a tile spans one dword)
+          // pad block of the row's last K group (a tile spans one group)
+          *scales = 0;
+          zero_block<FMT>(codes);
         }
       }
     }
@@ -199,13 +201,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
             p.partials[z * (p.R / 32) * p.C + (r / 32) * p.C + c] = part;
           }
           if (p.col_codes) {
-            uint8_t* codes = p.col_codes + z * p.C * (p.R * B / 8) + c * (p.R * B / 8) + r * B / 8;
+            uint8_t* codes = p.col_codes + z * code_bytes(p.C, p.R, B) + code_offset(c, r, p.C, B);
             uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
             quant_store<FMT, MODE, HAD>(v, codes, scales);
           }
         } else if (p.col_codes) {
-          // a 128-row tile spans one scale dword; blocks past R are pad
+          // a 128-row tile spans one K group; blocks past R are pad
           p.col_scales[z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C)] = 0;
+          zero_block<FMT>(p.col_codes + z * code_bytes(p.C, p.R, B) + code_offset(c, r, p.C, B));
         }
       }
     }

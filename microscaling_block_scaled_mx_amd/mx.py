@@ -123,11 +123,14 @@ def _check(st: int, what: str):
 
 # ---------------------------------------------------------------- buffers
 def alloc_packed(rows: int, K: int, fmt: int, device="cuda", batch: int | None = None):
-    """(codes, scales) uint8 tensors for a packed operand [rows] x K: codes
-    [rows][K*bits/8], scales in the blocked layout [ceil(K/128)][rows][4]."""
-    shape = (rows, K * BITS[fmt] // 8) if batch is None else (batch, rows, K * BITS[fmt] // 8)
-    sshape = ((K // 32 + 3) // 4, rows, 4)
-    sshape = sshape if batch is None else (batch, *sshape)
+    """(codes, scales) uint8 tensors for a packed operand [rows] x K in the
+    K-group-major layout: codes [ceil(K/128)][rows][16*bits], scales
+    [ceil(K/128)][rows][4]."""
+    groups = (K + 127) // 128
+    shape = (groups, rows, 16 * BITS[fmt])
+    sshape = (groups, rows, 4)
+    if batch is not None:
+        shape, sshape = (batch, *shape), (batch, *sshape)
     return (torch.empty(shape, dtype=torch.uint8, device=device),
             torch.empty(sshape, dtype=torch.uint8, device=device))
 

@@ -44,6 +44,7 @@ def test_status_strings_and_sizes():
     assert L.mx_codes_bytes(9, 256, 256) == 0 and L.mx_codes_bytes(mx.E2M1, 1, 33) == 0
     assert L.mx_scales_bytes(256, 512) == 256 * 16
     assert L.mx_scales_bytes(256, 160) == 2 * 256 * 4  # blocked: ceil(5 / 4) K groups of 4 bytes per row
+    assert L.mx_codes_bytes(mx.E2M3, 256, 160) == 2 * 256 * 96  # K-group-major: 2 groups of 96 bytes per row
     assert "gfx950" in mx.version()
 
 

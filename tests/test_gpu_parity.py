@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from microscaling_block_scaled_mx_amd import inputs as I
-from scale_layout import blocked, blocked_shape, unblocked
+from packed_layout import blocked, blocked_shape, tiled, tiled_shape, unblocked, untiled
 
 pytestmark = pytest.mark.gpu
 
@@ -89,11 +89,13 @@ def gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, row=True, col=True, col
     bshp = (lambda r, k: blocked_shape(r, k, None if batch == 1 else batch))
     rowp = colp = None
     # poisoned buffers: every byte, pad bytes included, must be written
+    bits = mxl.BITS[fmt]
+    tshp = (lambda r, k: tiled_shape(r, k, bits, None if batch == 1 else batch))
     if row:
-        rowp = (torch.full(shp(R, C * mxl.BITS[fmt] // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+        rowp = (torch.full(tshp(R, C), 0xA5, dtype=torch.uint8, device="cuda"),
                 torch.full(bshp(R, C), 0xA5, dtype=torch.uint8, device="cuda"))
     if col:
-        colp = (torch.full(shp(C, R * mxl.BITS[fmt] // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+        colp = (torch.full(tshp(C, R), 0xA5, dtype=torch.uint8, device="cuda"),
                 torch.full(bshp(C, R), 0xA5, dtype=torch.uint8, device="cuda"))
     part = sums = None
     if colsum:
@@ -103,9 +105,9 @@ def gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, row=True, col=True, col
                  batch=batch)
     out = {}
     if row:
-        out["row_codes"], out["row_scales"] = host(rowp[0]), unblocked(host(rowp[1]), C // 32)
+        out["row_codes"], out["row_scales"] = untiled(host(rowp[0]), C, bits), unblocked(host(rowp[1]), C // 32)
     if col:
-        out["col_codes"], out["col_scales"] = host(colp[0]), unblocked(host(colp[1]), R // 32)
+        out["col_codes"], out["col_scales"] = untiled(host(colp[0]), R, bits), unblocked(host(colp[1]), R // 32)
     if colsum:
         out["colsum_partials"], out["colsum"] = host(part), host(sums)
     return out
@@ -169,8 +171,9 @@ def gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed, bias=False):
     pa = orc.quantize(A, M, K, fmt, mode, had)
     pb = orc.quantize(B, N, K, fmt, mode, had)
     ref = orc.gemm(pa["row_codes"], pa["row_scales"], pb["row_codes"], pb["row_scales"], M, N, K, fmt, bias=b)
-    a = (dev(pa["row_codes"]), dev(blocked(pa["row_scales"])))
-    bb = (dev(pb["row_codes"]), dev(blocked(pb["row_scales"])))
+    bits = mxl.BITS[fmt]
+    a = (dev(tiled(pa["row_codes"], bits)), dev(blocked(pa["row_scales"])))
+    bb = (dev(tiled(pb["row_codes"], bits)), dev(blocked(pb["row_scales"])))
     c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     c16 = bf16_empty(M, N)
     bd = dev(b) if b is not None else None
@@ -232,7 +235,8 @@ def test_gemm_exact_products_bitwise(mxl, orc, fmt):
     bc, bsc = packed(N)
     ref = orc.gemm(ac, asc, bc, bsc, M, N, K, fmt)
     c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    mxl.gemm((dev(ac), dev(blocked(asc))), (dev(bc), dev(blocked(bsc))), M, N, K, fmt, c32, c_dtype=mxl.F32)
+    mxl.gemm((dev(tiled(ac, bits)), dev(blocked(asc))), (dev(tiled(bc, bits)), dev(blocked(bsc))), M, N, K, fmt, c32,
+             c_dtype=mxl.F32)
     assert np.array_equal(host(c32).astype(np.float64), ref)
 
 
@@ -287,24 +291,25 @@ def test_fused_mlp_parity_small(mxl, orc):
     h = host(t["h"])
     fwd = orc.mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=h)
     KN = dict(Xr=D, W1r=D, W2r=F, Xc=M, W1c=F, W2c=D)
+    BITS = 6
     for name, key in (("Xr", "X"), ("W1r", "W1"), ("W2r", "W2")):
-        assert np.array_equal(host(t[name][0]), fwd[key]["row_codes"]), name
+        assert np.array_equal(untiled(host(t[name][0]), KN[name], BITS), fwd[key]["row_codes"]), name
         assert np.array_equal(unblocked(host(t[name][1]), KN[name] // 32), fwd[key]["row_scales"]), name
     for name, key in (("Xc", "X"), ("W1c", "W1"), ("W2c", "W2")):
-        assert np.array_equal(host(t[name][0]), fwd[key]["col_codes"]), name
+        assert np.array_equal(untiled(host(t[name][0]), KN[name], BITS), fwd[key]["col_codes"]), name
         assert np.array_equal(unblocked(host(t[name][1]), KN[name] // 32), fwd[key]["col_scales"]), name
     assert bf16_close(h, fwd["h64"])
     # activation packs, bit-exact given the GPU's h
-    assert np.array_equal(host(t["ar"][0]), fwd["a"]["row_codes"])
+    assert np.array_equal(untiled(host(t["ar"][0]), F, BITS), fwd["a"]["row_codes"])
     assert np.array_equal(unblocked(host(t["ar"][1]), (F) // 32), fwd["a"]["row_scales"])
-    assert np.array_equal(host(t["ac"][0]), fwd["a"]["col_codes"])
+    assert np.array_equal(untiled(host(t["ac"][0]), M, BITS), fwd["a"]["col_codes"])
     assert np.array_equal(unblocked(host(t["ac"][1]), (M) // 32), fwd["a"]["col_scales"])
     assert bf16_close(host(t["Y"]), fwd["Y64"])
     da = host(t["da"])
     bwd = orc.mlp_bwd_ref(dY, fwd, M, D, F, da_in=da, h_in=h)
     assert bf16_close(da, bwd["da64"])
-    assert np.array_equal(host(t["dhr"][0]), bwd["dh"]["row_codes"])
-    assert np.array_equal(host(t["dhc"][0]), bwd["dh"]["col_codes"])
+    assert np.array_equal(untiled(host(t["dhr"][0]), F, BITS), bwd["dh"]["row_codes"])
+    assert np.array_equal(untiled(host(t["dhc"][0]), M, BITS), bwd["dh"]["col_codes"])
     assert np.array_equal(unblocked(host(t["dhc"][1]), (M) // 32), bwd["dh"]["col_scales"])
     assert np.array_equal(host(t["db1"]).view(np.uint32), bwd["db1"].view(np.uint32))
     assert bf16_close(host(t["dX"]), bwd["dX64"])
@@ -352,20 +357,21 @@ def test_grouped_parity_small(mxl, orc):
     R, D, F, G = 1024, 256, 256, 4
     counts, offsets, X, W1, W2, dY = I.grouped_mlp(502, R, D, F, G, zero_expert=2)
     t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G)
+    BITS = 8
     H = host(t["H"])
     fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H)
     assert bf16_close(H, fwd["H64"])
-    assert np.array_equal(host(t["zr"][0]), fwd["z"]["row_codes"])
+    assert np.array_equal(untiled(host(t["zr"][0]), F, BITS), fwd["z"]["row_codes"])
     assert np.array_equal(unblocked(host(t["zr"][1]), (F) // 32), fwd["z"]["row_scales"])
-    assert np.array_equal(host(t["zc"][0]), fwd["z"]["col_codes"])
+    assert np.array_equal(untiled(host(t["zc"][0]), R, BITS), fwd["z"]["col_codes"])
     assert np.array_equal(unblocked(host(t["zc"][1]), (R) // 32), fwd["z"]["col_scales"])
     assert bf16_close(host(t["Y"]), fwd["Y64"])
     dz = host(t["dz"])
     bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=dz, H_in=H)
     assert bf16_close(dz, bwd["dz64"])
-    assert np.array_equal(host(t["dHr"][0]), bwd["dH"]["row_codes"])
+    assert np.array_equal(untiled(host(t["dHr"][0]), 2 * F, BITS), bwd["dH"]["row_codes"])
     assert np.array_equal(unblocked(host(t["dHr"][1]), (2 * F) // 32), bwd["dH"]["row_scales"])
-    assert np.array_equal(host(t["dHc"][0]), bwd["dH"]["col_codes"])
+    assert np.array_equal(untiled(host(t["dHc"][0]), R, BITS), bwd["dH"]["col_codes"])
     assert np.array_equal(unblocked(host(t["dHc"][1]), (R) // 32), bwd["dH"]["col_scales"])
     assert bf16_close(host(t["dX"]), bwd["dX64"])
     dW1, dW2 = host(t["dW1"]), host(t["dW2"])
@@ -388,15 +394,17 @@ def test_grouped_inactive_tail_untouched(mxl, orc):
     w1r = mxl.alloc_packed(2 * F, D, fmt, batch=G)
     mxl.quantize(dev(W1), 2 * F, D, fmt, 1, row=w1r, batch=G)
     H = torch.full((R, 2 * F), 0x1234, dtype=torch.int16, device="cuda")
-    zr = (torch.full((R, F), 0xAB, dtype=torch.uint8, device="cuda"),
+    zr = (torch.full(tiled_shape(R, F, 8), 0xAB, dtype=torch.uint8, device="cuda"),
           torch.full(blocked_shape(R, F), 0xAB, dtype=torch.uint8, device="cuda"))
-    zc = (torch.full((F, R), 0xAB, dtype=torch.uint8, device="cuda"),
+    zc = (torch.full(tiled_shape(F, R, 8), 0xAB, dtype=torch.uint8, device="cuda"),
           torch.full(blocked_shape(F, R), 0xAB, dtype=torch.uint8, device="cuda"))
     mxl.grouped_gemm(mxl.RAGGED_M, G, R, dev(offsets), xr, w1r, H, epilogue=mxl.EPI_SWIGLU, N=2 * F, K=D,
                      out_row=zr, out_col=zc)
     Hh = host(H)
     assert np.all(Hh[640:] == 0x1234) and not np.any(Hh[:640] == 0x1234)
-    assert np.all(host(zr[0])[640:] == 0xAB) and np.all(host(zc[0])[:, 640:] == 0xAB)
+    zrc, zcc = host(zr[0]), host(zc[0])  # [F/128][R][128], [R/128][F][128]
+    assert np.all(zrc[:, 640:] == 0xAB)
+    assert np.all(zcc[640 // 128:] == 0xAB)
     zrs, zcs = host(zr[1]), host(zc[1])  # [F/128][R][4], [R/128][F][4]
     assert np.all(zrs[:, 640:] == 0xAB) and not np.any(zrs[:, :640] == 0xAB)
     assert np.all(zcs[640 // 128:] == 0xAB) and not np.any(zcs[:640 // 128] == 0xAB)
