@@ -35,11 +35,15 @@
  *    As in [P4] (the grouped kernels' blocked E8M0 scale ABI), the
  *    quantizer writes the blocking the GEMM reads.  A ragged-K group of
  *    rows [k0, k1), k0 and k1 multiples of 128, is the run of K groups
- *    k0/128 .. k1/128 - 1.  Packing of the codes within a group: E2M1
- *    element 2j in the low nibble of byte j and 2j+1 in the high nibble;
- *    E2M3 a little-endian 6-bit stream, element j at bits [6j, 6j+6); E4M3
- *    one byte per element.  Every GEMM computes C = A . B^T on two such
- *    operands (the NT layout of [P3], Troubleshooting).
+ *    k0/128 .. k1/128 - 1.  Packing of the codes within a group, block by
+ *    block (32 elements): E2M1 element 2j in the low nibble of byte j and
+ *    2j+1 in the high nibble, 16 B per block; E4M3 one byte per element,
+ *    32 B per block; E2M3 a little-endian 6-bit stream, element j at bits
+ *    [6j, 6j+6) of the block's 24 B, of which the first 16 B lie at byte
+ *    16b of the group and the last 8 B at byte 64 + 8b (block b = 0..3), so
+ *    that each matrix-core operand is one 16-byte and one 8-byte read.
+ *    Every GEMM computes C = A . B^T on two such operands (the NT layout of
+ *    [P3], Troubleshooting).
  *  - Return value: MX_OK, or an mx_status error.  Arguments are validated on
  *    the host before anything is enqueued; on error nothing is enqueued and
  *    no output is touched.  There is no fallback path: a call the kernels

@@ -206,19 +206,18 @@ __device__ __forceinline__ void lds_col_block(const uint8_t* tile, int pitch, in
   for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(src[i * (pitch / 2)]);
 }
 
-// Store one block's packed codes (E2M1 16 B, E2M3 24 B at 8-byte alignment,
-// E4M3 32 B).
+// Store one block's packed codes into its K group (group base g, block
+// blk = 0..3 of the group): E2M1 16 B at 16 blk, E4M3 32 B at 32 blk, E2M3
+// its first 16 B at 16 blk and its last 8 B at 64 + 8 blk.
 template <int FMT>
-__device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t (&w)[FmtTraits<FMT>::kBits]) {
+__device__ __forceinline__ void store_block(uint8_t* g, int blk, const uint32_t (&w)[FmtTraits<FMT>::kBits]) {
   if constexpr (FMT == kE2M1) {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(g + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
   } else if constexpr (FMT == kE2M3) {
-    uint2* d = reinterpret_cast<uint2*>(dst);
-    d[0] = make_uint2(w[0], w[1]);
-    d[1] = make_uint2(w[2], w[3]);
-    d[2] = make_uint2(w[4], w[5]);
+    *reinterpret_cast<uint4*>(g + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint2*>(g + 64 + 8 * blk) = make_uint2(w[4], w[5]);
   } else {
-    uint4* d = reinterpret_cast<uint4*>(dst);
+    uint4* d = reinterpret_cast<uint4*>(g + 32 * blk);
     d[0] = make_uint4(w[0], w[1], w[2], w[3]);
     d[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
@@ -226,20 +225,20 @@ __device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t (&w)[Fm
 
 // Zero codes of one block (a pad block of a partial K group).
 template <int FMT>
-__device__ __forceinline__ void zero_block(uint8_t* dst) {
+__device__ __forceinline__ void zero_block(uint8_t* g, int blk) {
   uint32_t w[FmtTraits<FMT>::kBits];
 #pragma unroll
   for (int i = 0; i < FmtTraits<FMT>::kBits; ++i) w[i] = 0u;
-  store_block<FMT>(dst, w);
+  store_block<FMT>(g, blk, w);
 }
 
-// Quantize 32 values and write codes + scale byte.
+// Quantize 32 values and write codes (block blk of group g) + scale byte.
 template <int FMT, int MODE, int HAD>
-__device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* codes, uint8_t* scale) {
+__device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* g, int blk, uint8_t* scale) {
   if constexpr (HAD) hadamard32(v);
   uint32_t w[FmtTraits<FMT>::kBits];
   const uint32_t s = quant_block<FMT, MODE>(v, w);
-  store_block<FMT>(codes, w);
+  store_block<FMT>(g, blk, w);
   *scale = (uint8_t)s;
 }
 

@@ -20,13 +20,16 @@ __host__ __device__ __forceinline__ int64_t scale_bytes(int64_t rows, int64_t K)
 }
 
 // Codes use the same K-group-major order: the codes of one row's 128-element
-// K group take 16 * bits contiguous bytes (the plain packing of those 128
-// elements), and the groups of one K group are stored row after row --
-// [ceil(K/128)][rows][16 * bits] bytes.  A GEMM stage then reads a row
-// panel's codes as one contiguous run.  k is a multiple of 32 (a block
-// start); pad bytes of a partial last group are 0.
-__host__ __device__ __forceinline__ int64_t code_offset(int64_t row, int64_t k, int64_t rows, int bits) {
-  return ((k >> 7) * rows + row) * (16 * bits) + (k & 127) * bits / 8;
+// K group take 16 * bits contiguous bytes, and the groups of one K group are
+// stored row after row -- [ceil(K/128)][rows][16 * bits] bytes.  A GEMM
+// stage then reads a row panel's codes as one contiguous run.  Inside a
+// group, E2M1 and E4M3 blocks (32 codes, 16 / 32 bytes) follow each other;
+// an E2M3 block (24 bytes) is split so that each MFMA operand is one 16-byte
+// and one 8-byte read: block b's first 16 bytes at 16 b, its last 8 bytes
+// at 64 + 8 b.  Pad bytes of a partial last group are 0.
+// Byte offset of the group holding element k (any k) of a row:
+__host__ __device__ __forceinline__ int64_t code_group(int64_t row, int64_t k, int64_t rows, int bits) {
+  return ((k >> 7) * rows + row) * (16 * bits);
 }
 __host__ __device__ __forceinline__ int64_t code_bytes(int64_t rows, int64_t K, int bits) {
   return ((K + 127) / 128) * rows * (16 * bits);

@@ -166,15 +166,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
       const int64_t r = r0 + row, c = c0 + blk * 32;
       if (r < p.R) {
         uint8_t* scales = p.row_scales + z * scale_bytes(p.R, p.C) + scale_offset(r, c / 32, p.R);
-        uint8_t* codes = p.row_codes + z * code_bytes(p.R, p.C, B) + code_offset(r, c, p.R, B);
+        uint8_t* group = p.row_codes + z * code_bytes(p.R, p.C, B) + code_group(r, c, p.R, B);
         if (c < p.C) {
           float v[32];
           lds_row_block(tile + lds_row(row), 0, 0, blk * 32, v);
-          quant_store<FMT, MODE, HAD>(v, codes, scales);
+          quant_store<FMT, MODE, HAD>(v, group, blk, scales);
         } else {
           // pad block of the row's last K group (a tile spans one group)
           *scales = 0;
-          zero_block<FMT>(codes);
+          zero_block<FMT>(group, blk);
         }
       }
     }
@@ -201,14 +201,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
             p.partials[z * (p.R / 32) * p.C + (r / 32) * p.C + c] = part;
           }
           if (p.col_codes) {
-            uint8_t* codes = p.col_codes + z * code_bytes(p.C, p.R, B) + code_offset(c, r, p.C, B);
+            uint8_t* group = p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B);
             uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
-            quant_store<FMT, MODE, HAD>(v, codes, scales);
+            quant_store<FMT, MODE, HAD>(v, group, blk, scales);
           }
         } else if (p.col_codes) {
           // a 128-row tile spans one K group; blocks past R are pad
           p.col_scales[z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C)] = 0;
-          zero_block<FMT>(p.col_codes + z * code_bytes(p.C, p.R, B) + code_offset(c, r, p.C, B));
+          zero_block<FMT>(p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B), blk);
         }
       }
     }
