@@ -40,8 +40,9 @@
  *    2j+1 in the high nibble, 16 B per block; E4M3 one byte per element,
  *    32 B per block; E2M3 a little-endian 6-bit stream, element j at bits
  *    [6j, 6j+6) of the block's 24 B, of which the first 16 B lie at byte
- *    16b of the group and the last 8 B at byte 64 + 8b (block b = 0..3), so
- *    that each matrix-core operand is one 16-byte and one 8-byte read.
+ *    16b of the group and the last 8 B at byte 64 + 8(b ^ s) (block
+ *    b = 0..3, s = bit 4 of the row), so that each matrix-core operand is one
+ *    16-byte and one 8-byte read, both free of LDS bank conflicts.
  *    Every GEMM computes C = A . B^T on two such operands (the NT layout of
  *    [P3], Troubleshooting).
  *  - Return value: MX_OK, or an mx_status error.  Arguments are validated on

@@ -207,15 +207,19 @@ __device__ __forceinline__ void lds_col_block(const uint8_t* tile, int pitch, in
 }
 
 // Store one block's packed codes into its K group (group base g, block
-// blk = 0..3 of the group): E2M1 16 B at 16 blk, E4M3 32 B at 32 blk, E2M3
-// its first 16 B at 16 blk and its last 8 B at 64 + 8 blk.
+// blk = 0..3 of the group, row = the packed operand's row): E2M1 16 B at
+// 16 blk, E4M3 32 B at 32 blk, E2M3 its first 16 B at 16 blk and its last
+// 8 B at 64 + 8 (blk ^ ((row >> 4) & 1)) -- rows with bit 4 set swap the two
+// 8-byte tails that share a 16-byte chunk, so that the 8-byte reads of 32
+// consecutive rows fall in distinct LDS banks.
 template <int FMT>
-__device__ __forceinline__ void store_block(uint8_t* g, int blk, const uint32_t (&w)[FmtTraits<FMT>::kBits]) {
+__device__ __forceinline__ void store_block(uint8_t* g, int blk, int64_t row,
+                                            const uint32_t (&w)[FmtTraits<FMT>::kBits]) {
   if constexpr (FMT == kE2M1) {
     *reinterpret_cast<uint4*>(g + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
   } else if constexpr (FMT == kE2M3) {
     *reinterpret_cast<uint4*>(g + 16 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint2*>(g + 64 + 8 * blk) = make_uint2(w[4], w[5]);
+    *reinterpret_cast<uint2*>(g + 64 + 8 * (blk ^ (int)((row >> 4) & 1))) = make_uint2(w[4], w[5]);
   } else {
     uint4* d = reinterpret_cast<uint4*>(g + 32 * blk);
     d[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -225,20 +229,21 @@ __device__ __forceinline__ void store_block(uint8_t* g, int blk, const uint32_t 
 
 // Zero codes of one block (a pad block of a partial K group).
 template <int FMT>
-__device__ __forceinline__ void zero_block(uint8_t* g, int blk) {
+__device__ __forceinline__ void zero_block(uint8_t* g, int blk, int64_t row) {
   uint32_t w[FmtTraits<FMT>::kBits];
 #pragma unroll
   for (int i = 0; i < FmtTraits<FMT>::kBits; ++i) w[i] = 0u;
-  store_block<FMT>(g, blk, w);
+  store_block<FMT>(g, blk, row, w);
 }
 
-// Quantize 32 values and write codes (block blk of group g) + scale byte.
+// Quantize 32 values and write codes (block blk of group g of the packed
+// operand's row `row`) + scale byte.
 template <int FMT, int MODE, int HAD>
-__device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* g, int blk, uint8_t* scale) {
+__device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* g, int blk, int64_t row, uint8_t* scale) {
   if constexpr (HAD) hadamard32(v);
   uint32_t w[FmtTraits<FMT>::kBits];
   const uint32_t s = quant_block<FMT, MODE>(v, w);
-  store_block<FMT>(g, blk, w);
+  store_block<FMT>(g, blk, row, w);
   *scale = (uint8_t)s;
 }
 

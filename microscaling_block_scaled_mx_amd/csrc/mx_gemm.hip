@@ -193,10 +193,11 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* rowp, int r, int ks, i
     v = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
   } else {
     // block b = 2 ks + g of the group: its first 16 bytes are chunk b, its
-    // last 8 bytes half g of chunk 4 + ks (the E2M3 order inside a K group);
-    // the instruction reads 6 dwords of an E2M3 operand
+    // last 8 bytes half g (g ^ 1 in rows with bit 4 set) of chunk 4 + ks (the
+    // E2M3 order inside a K group); the instruction reads 6 dwords of an
+    // E2M3 operand.  Both reads are conflict-free across the 64 banks.
     const v4i w = *reinterpret_cast<const v4i*>(rowp + 16 * chunk_pos<NCH>(r, 2 * ks + g));
-    const v2i h = *reinterpret_cast<const v2i*>(rowp + 16 * chunk_pos<NCH>(r, 4 + ks) + 8 * g);
+    const v2i h = *reinterpret_cast<const v2i*>(rowp + 16 * chunk_pos<NCH>(r, 4 + ks) + 8 * (g ^ ((r >> 4) & 1)));
     const v4i h4 = __builtin_shufflevector(h, h, 0, 1, -1, -1);
     v = __builtin_shufflevector(w, h4, 0, 1, 2, 3, 4, 5, -1, -1);
   }
@@ -567,10 +568,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_row_block(zt, CF::kZPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = zb + 32 * blk;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3),
+        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3), m,
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3),
+        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3), m,
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
     }
     for (int q = t; q < ZC * (BM / 32); q += kThreads) {
@@ -579,10 +580,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_col_block(zt, CF::kZPitch, rb2 * 32, col, v);
       const int64_t cz = zb + col, m = m0 + 32 * rb2;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + code_group(cz, m, p.F, QB), (int)((m >> 5) & 3),
+        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + code_group(cz, m, p.F, QB), (int)((m >> 5) & 3), cz,
                                     p.q_col_scales + scale_offset(cz, m / 32, p.F));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + code_group(cz, m, p.F, QB), (int)((m >> 5) & 3),
+        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + code_group(cz, m, p.F, QB), (int)((m >> 5) & 3), cz,
                                     p.q_col_scales + scale_offset(cz, m / 32, p.F));
     }
   } else {  // kEpiDSwiglu
@@ -627,10 +628,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_row_block(half ? tu : tg, CF::kDPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = (half ? p.F : 0) + n0 + 32 * blk;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3),
+        quant_store<FMT, kRceil, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3), m,
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3),
+        quant_store<FMT, kFloor, 0>(v, p.q_row_codes + code_group(m, col, p.R, QB), (int)((col >> 5) & 3), m,
                                     p.q_row_scales + scale_offset(m, col / 32, p.R));
     }
     for (int q = t; q < 2 * BN * (BM / 32); q += kThreads) {
@@ -640,10 +641,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       lds_col_block(half ? tu : tg, CF::kDPitch, rb2 * 32, col, v);
       const int64_t cw = (half ? p.F : 0) + n0 + col, m = m0 + 32 * rb2;
       if (p.q_mode == kRceil)
-        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + code_group(cw, m, W, QB), (int)((m >> 5) & 3),
+        quant_store<FMT, kRceil, 0>(v, p.q_col_codes + code_group(cw, m, W, QB), (int)((m >> 5) & 3), cw,
                                     p.q_col_scales + scale_offset(cw, m / 32, W));
       else
-        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + code_group(cw, m, W, QB), (int)((m >> 5) & 3),
+        quant_store<FMT, kFloor, 0>(v, p.q_col_codes + code_group(cw, m, W, QB), (int)((m >> 5) & 3), cw,
                                     p.q_col_scales + scale_offset(cw, m / 32, W));
     }
   }

@@ -26,7 +26,8 @@ __host__ __device__ __forceinline__ int64_t scale_bytes(int64_t rows, int64_t K)
 // group, E2M1 and E4M3 blocks (32 codes, 16 / 32 bytes) follow each other;
 // an E2M3 block (24 bytes) is split so that each MFMA operand is one 16-byte
 // and one 8-byte read: block b's first 16 bytes at 16 b, its last 8 bytes
-// at 64 + 8 b.  Pad bytes of a partial last group are 0.
+// at 64 + 8 (b ^ s), s = bit 4 of the row.  Pad bytes of a partial last
+// group are 0.
 // Byte offset of the group holding element k (any k) of a row:
 __host__ __device__ __forceinline__ int64_t code_group(int64_t row, int64_t k, int64_t rows, int bits) {
   return ((k >> 7) * rows + row) * (16 * bits);

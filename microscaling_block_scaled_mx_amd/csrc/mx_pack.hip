@@ -170,11 +170,11 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
         if (c < p.C) {
           float v[32];
           lds_row_block(tile + lds_row(row), 0, 0, blk * 32, v);
-          quant_store<FMT, MODE, HAD>(v, group, blk, scales);
+          quant_store<FMT, MODE, HAD>(v, group, blk, r, scales);
         } else {
           // pad block of the row's last K group (a tile spans one group)
           *scales = 0;
-          zero_block<FMT>(group, blk);
+          zero_block<FMT>(group, blk, r);
         }
       }
     }
@@ -203,12 +203,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
           if (p.col_codes) {
             uint8_t* group = p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B);
             uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
-            quant_store<FMT, MODE, HAD>(v, group, blk, scales);
+            quant_store<FMT, MODE, HAD>(v, group, blk, c, scales);
           }
         } else if (p.col_codes) {
           // a 128-row tile spans one K group; blocks past R are pad
           p.col_scales[z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C)] = 0;
-          zero_block<FMT>(p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B), blk);
+          zero_block<FMT>(p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B), blk, c);
         }
       }
     }
