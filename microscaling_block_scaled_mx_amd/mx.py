@@ -139,11 +139,40 @@ def _packed(p):
     return Packed(_ptr(p[0]), _ptr(p[1])) if p is not None else Packed(None, None)
 
 
+# The C ABI takes bare pointers and cannot see buffer sizes; when the
+# arguments are torch tensors, their sizes are checked here against what the
+# call will touch (a short buffer, e.g. one packed in another format, would
+# otherwise be read or written out of bounds).
+def _nbytes(t):
+    return t.numel() * t.element_size() if isinstance(t, torch.Tensor) else None
+
+
+def _need(t, nbytes: int, what: str):
+    n = _nbytes(t)
+    if n is not None and n < nbytes:
+        raise MXError(2, f"{what}: buffer holds {n} bytes, the call touches {nbytes}")
+
+
+def _need_packed(p, rows: int, K: int, fmt: int, what: str, batch: int = 1):
+    if p is None or fmt not in BITS:
+        return
+    _need(p[0], batch * lib().mx_codes_bytes(fmt, rows, K), what + " codes")
+    _need(p[1], batch * lib().mx_scales_bytes(rows, K), what + " scales")
+
+
 # ---------------------------------------------------------------- entry points
 def quantize(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = False,
              prologue: int = PRO_IDENTITY, aux=None, row=None, col=None, colsum_partials=None, colsum=None,
              batch: int = 1, stream=None):
     """mx_quantize: row=(codes, scales) [R] x K=C, col=(codes, scales) [C] x K=R."""
+    in_cols = 2 * C if prologue == PRO_SWIGLU else (C // 2 if prologue == PRO_DSWIGLU else C)
+    _need(x, 2 * batch * R * in_cols, "quantize input")
+    if prologue in (PRO_DGELU_TANH, PRO_DSWIGLU):
+        _need(aux, 2 * batch * R * C, "quantize aux")
+    _need_packed(row, R, C, fmt, "quantize row", batch)
+    _need_packed(col, C, R, fmt, "quantize col", batch)
+    _need(colsum_partials, 4 * batch * (R // 32) * C, "colsum partials")
+    _need(colsum, 4 * batch * C, "colsum")
     st = lib().mx_quantize(_ptr(x), _ptr(aux), batch, R, C, fmt, scale_mode, int(hadamard), prologue,
                            _ptr(row[0]) if row else None, _ptr(row[1]) if row else None,
                            _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
@@ -154,6 +183,10 @@ def quantize(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = Fals
 def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16, c_dtype: int = BF16,
          ldc: int | None = None, stream=None):
     """mx_gemm: c [M][ldc] = A . B^T (+ bias); a, b = (codes, scales)."""
+    _need_packed(a, M, K, fmt, "gemm A")
+    _need_packed(b, N, K, fmt, "gemm B")
+    _need(c, (4 if c_dtype == F32 else 2) * M * (N if ldc is None else ldc), "gemm C")
+    _need(bias, (4 if bias_dtype == F32 else 2) * N, "gemm bias")
     st = lib().mx_gemm(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
                        _ptr(c), c_dtype, N if ldc is None else ldc, _stream(stream))
     _check(st, "mx_gemm")
@@ -161,6 +194,12 @@ def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int =
 
 def fused_mlp_fwd(M, D, F, X, W1, b1, W2, h, Y, Xr, Xc, W1r, W1c, W2r, W2c, ar, ac, fmt=E2M3,
                   scale_mode=FLOOR, hadamard=True, stream=None):
+    for t, n, what in ((X, M * D, "X"), (W1, F * D, "W1"), (b1, F, "b1"), (W2, D * F, "W2"), (h, M * F, "h"),
+                       (Y, M * D, "Y")):
+        _need(t, 2 * n, "fused fwd " + what)
+    for p, r, k, what in ((Xr, M, D, "Xr"), (Xc, D, M, "Xc"), (W1r, F, D, "W1r"), (W1c, D, F, "W1c"),
+                          (W2r, D, F, "W2r"), (W2c, F, D, "W2c"), (ar, M, F, "ar"), (ac, F, M, "ac")):
+        _need_packed(p, r, k, fmt, "fused fwd " + what)
     a = MlpFwdArgs(M, D, F, fmt, scale_mode, int(hadamard), 0, _ptr(X), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(h),
                    _ptr(Y), _packed(Xr), _packed(Xc), _packed(W1r), _packed(W1c), _packed(W2r), _packed(W2c),
                    _packed(ar), _packed(ac))
@@ -169,6 +208,13 @@ def fused_mlp_fwd(M, D, F, X, W1, b1, W2, h, Y, Xr, Xc, W1r, W1c, W2r, W2c, ar, 
 
 def fused_mlp_bwd(M, D, F, dY, h, Xc, W1c, W2c, ac, da, dX, dW1, dW2, db1, db1_partials, dYr, dYc, dhr, dhc,
                   fmt=E2M3, scale_mode=FLOOR, hadamard=True, stream=None):
+    for t, n, what in ((dY, 2 * M * D, "dY"), (h, 2 * M * F, "h"), (da, 2 * M * F, "da"), (dX, 2 * M * D, "dX"),
+                       (dW1, 2 * F * D, "dW1"), (dW2, 2 * D * F, "dW2"), (db1, 4 * F, "db1"),
+                       (db1_partials, 4 * (M // 32) * F, "db1 partials")):
+        _need(t, n, "fused bwd " + what)
+    for p, r, k, what in ((Xc, D, M, "Xc"), (W1c, D, F, "W1c"), (W2c, F, D, "W2c"), (ac, F, M, "ac"),
+                          (dYr, M, D, "dYr"), (dYc, D, M, "dYc"), (dhr, M, F, "dhr"), (dhc, F, M, "dhc")):
+        _need_packed(p, r, k, fmt, "fused bwd " + what)
     a = MlpBwdArgs(M, D, F, fmt, scale_mode, int(hadamard), 0, _ptr(dY), _ptr(h), _packed(Xc), _packed(W1c),
                    _packed(W2c), _packed(ac), _ptr(da), _ptr(dX), _ptr(dW1), _ptr(dW2), _ptr(db1),
                    _ptr(db1_partials), _packed(dYr), _packed(dYc), _packed(dhr), _packed(dhc))
@@ -177,6 +223,23 @@ def fused_mlp_bwd(M, D, F, dY, h, Xc, W1c, W2c, ac, da, dX, dW1, dW2, db1, db1_p
 
 def grouped_gemm(mode, G, R, offsets, A, B, C, fmt=E4M3, epilogue=EPI_NONE, scale_mode=RCEIL, M=0, N=0, K=0,
                  aux=None, out_row=None, out_col=None, validate_offsets=False, stream=None):
+    _need(offsets, 4 * G, "grouped offsets")
+    if mode == RAGGED_M:
+        F = N // 2 if epilogue == EPI_SWIGLU else N
+        _need_packed(A, R, K, fmt, "grouped A")
+        _need_packed(B, N, K, fmt, "grouped B", G)
+        _need(C, 2 * R * (F if epilogue == EPI_DSWIGLU else N), "grouped C")
+        if epilogue == EPI_SWIGLU:
+            _need_packed(out_row, R, F, fmt, "grouped out_row")
+            _need_packed(out_col, F, R, fmt, "grouped out_col")
+        elif epilogue == EPI_DSWIGLU:
+            _need(aux, 2 * R * 2 * N, "grouped aux")
+            _need_packed(out_row, R, 2 * N, fmt, "grouped out_row")
+            _need_packed(out_col, 2 * N, R, fmt, "grouped out_col")
+    else:
+        _need_packed(A, M, R, fmt, "grouped A")
+        _need_packed(B, N, R, fmt, "grouped B")
+        _need(C, 2 * G * M * N, "grouped C")
     a = GroupedArgs(mode, epilogue, fmt, scale_mode, G, int(validate_offsets), R, M, N, K, _ptr(offsets),
                     _packed(A), _packed(B), _ptr(C), _ptr(aux), _packed(out_row), _packed(out_col))
     _check(lib().mx_grouped_gemm(ctypes.byref(a), _stream(stream)), "mx_grouped_gemm")

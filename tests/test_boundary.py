@@ -175,3 +175,22 @@ def test_fused_mlp_rejections():
     assert st in (OK, DEVICE)
     b = mx.MlpBwdArgs()
     assert L.mx_fused_mlp_bwd(ctypes.byref(b), None) == NULL
+
+
+def test_binding_rejects_short_buffers_before_the_call():
+    # Buffers packed for E2M1 are half the size an E4M3 call touches: the
+    # binding must refuse before the C ABI (which sees only pointers) runs.
+    import torch
+    M, N, K = 256, 256, 512
+    small = mx.alloc_packed(M, K, mx.E2M1, device="cpu")
+    b = mx.alloc_packed(N, K, mx.E4M3, device="cpu")
+    C = torch.empty(M, N, dtype=torch.int16)
+    with pytest.raises(mx.MXError, match="gemm A codes"):
+        mx.gemm(small, b, M, N, K, mx.E4M3, C)
+    with pytest.raises(mx.MXError, match="gemm C"):
+        mx.gemm(mx.alloc_packed(M, K, mx.E4M3, device="cpu"), b, M, N, K, mx.E4M3, C[:128])
+    with pytest.raises(mx.MXError, match="quantize row codes"):
+        mx.quantize(torch.empty(M, K, dtype=torch.int16), M, K, mx.E4M3, mx.RCEIL, row=small)
+    off = torch.tensor([M], dtype=torch.int32)
+    with pytest.raises(mx.MXError, match="grouped A codes"):
+        mx.grouped_gemm(mx.RAGGED_M, 1, M, off, small, b, C, N=N, K=K)
