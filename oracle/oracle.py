@@ -275,37 +275,37 @@ def _kslice(codes, scales, fmt, k0, k1):
             np.ascontiguousarray(scales[:, k0 // 32:k1 // 32]))
 
 
-def mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=None, rows=None):
-    """Fused MXFP6 MLP forward [P1 description and Summary]: fc1 (+ bias in the
+def mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=None, rows=None, fmt=E2M3, mode=FLOOR, had=True):
+    """Fused MLP forward [P1 description and Summary]: fc1 (+ bias in the
     accumulator), tanh-GELU taken by the packer as a prologue, fc2.  All packs
-    are E2M3, FLOOR scales, Hadamard-32 along each GEMM's K.  ``h_in``: the
-    bf16 pre-activation to pack from (defaults to this oracle's own h); pass
-    the GPU's h to check the activation packs bit-for-bit."""
-    fmt = E2M3
-    px = quantize(X, M, D, fmt, FLOOR, True, row=True, col=True)
-    pw1 = quantize(W1, F, D, fmt, FLOOR, True, row=True, col=True)
-    pw2 = quantize(W2, D, F, fmt, FLOOR, True, row=True, col=True)
+    use fmt / mode / had (the pages' recipe: E2M3, FLOOR scales, Hadamard-32
+    along each GEMM's K).  ``h_in``: the bf16 pre-activation to pack from
+    (defaults to this oracle's own h); pass the GPU's h to check the
+    activation packs bit-for-bit."""
+    px = quantize(X, M, D, fmt, mode, had, row=True, col=True)
+    pw1 = quantize(W1, F, D, fmt, mode, had, row=True, col=True)
+    pw2 = quantize(W2, D, F, fmt, mode, had, row=True, col=True)
     h64 = gemm(px["row_codes"], px["row_scales"], pw1["row_codes"], pw1["row_scales"], M, F, D, fmt,
                bias=b1)
     h = round_bf16(h64) if h_in is None else h_in
-    pa = quantize(h, M, F, fmt, FLOOR, True, pro=PRO_GELU, row=True, col=True)
+    pa = quantize(h, M, F, fmt, mode, had, pro=PRO_GELU, row=True, col=True)
     y64 = gemm(pa["row_codes"], pa["row_scales"], pw2["row_codes"], pw2["row_scales"], M, D, F, fmt,
                rows=rows)
-    return {"X": px, "W1": pw1, "W2": pw2, "h64": h64, "h": h, "a": pa, "Y64": y64}
+    return {"X": px, "W1": pw1, "W2": pw2, "h64": h64, "h": h, "a": pa, "Y64": y64, "fmt": (fmt, mode, had)}
 
 
 def mlp_bwd_ref(dY, fwd, M, D, F, da_in=None, h_in=None, rows=None):
     """Fused MXFP6 MLP backward [P1 description]: fc2 dgrad gives da (stored);
     the packer takes dGELU(da, h) as its prologue, so dh is never stored, and
     returns the fc1 bias gradient as a column sum; then fc1 dgrad and both
-    weight gradients."""
-    fmt = E2M3
-    pdy = quantize(dY, M, D, fmt, FLOOR, True, row=True, col=True)
+    weight gradients.  Format, scale mode and rotation are the forward's."""
+    fmt, mode, had = fwd["fmt"]
+    pdy = quantize(dY, M, D, fmt, mode, had, row=True, col=True)
     da64 = gemm(pdy["row_codes"], pdy["row_scales"], fwd["W2"]["col_codes"], fwd["W2"]["col_scales"],
                 M, F, D, fmt)
     da = round_bf16(da64) if da_in is None else da_in
     h = fwd["h"] if h_in is None else h_in
-    pdh = quantize(da, M, F, fmt, FLOOR, True, pro=PRO_DGELU, aux=h, row=True, col=True, colsum=True)
+    pdh = quantize(da, M, F, fmt, mode, had, pro=PRO_DGELU, aux=h, row=True, col=True, colsum=True)
     dx64 = gemm(pdh["row_codes"], pdh["row_scales"], fwd["W1"]["col_codes"], fwd["W1"]["col_scales"],
                 M, D, F, fmt, rows=rows)
     dw1 = gemm(pdh["col_codes"], pdh["col_scales"], fwd["X"]["col_codes"], fwd["X"]["col_scales"],
@@ -322,42 +322,42 @@ def grouped_ranges(offsets):
     return list(zip(starts, ends))
 
 
-def grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=None):
-    """Routed-expert SwiGLU MLP forward, MXFP8 E4M3 with RCEIL scales
-    [P4 commit messages]: expert g owns rows [off[g-1], off[g]) (cumulative
-    ends); per-expert counts are multiples of 128.  FC1 -> H (bf16, saved,
-    [gate|up]); SwiGLU -> z, quantized rowwise 1x32 and columnwise 32x1;
-    FC2 -> Y.  Rows at or past off[G-1] are not computed."""
-    fmt = E4M3
+def grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=None, fmt=E4M3, mode=RCEIL):
+    """Routed-expert SwiGLU MLP forward (the pages' recipe: MXFP8 E4M3 with
+    RCEIL scales [P4 commit messages]): expert g owns rows [off[g-1], off[g])
+    (cumulative ends); per-expert counts are multiples of 128.  FC1 -> H
+    (bf16, saved, [gate|up]); SwiGLU -> z, quantized rowwise 1x32 and
+    columnwise 32x1; FC2 -> Y.  Rows at or past off[G-1] are not computed."""
     G = len(offsets)
     Ract = int(offsets[-1])
-    px = quantize(X[:Ract], Ract, D, fmt, RCEIL, row=True, col=True) if Ract else None
+    px = quantize(X[:Ract], Ract, D, fmt, mode, row=True, col=True) if Ract else None
     H64 = np.zeros((Ract, 2 * F))
-    w1 = [quantize(W1[g], 2 * F, D, fmt, RCEIL, row=True, col=True) for g in range(G)]
-    w2 = [quantize(W2[g], D, F, fmt, RCEIL, row=True, col=True) for g in range(G)]
+    w1 = [quantize(W1[g], 2 * F, D, fmt, mode, row=True, col=True) for g in range(G)]
+    w2 = [quantize(W2[g], D, F, fmt, mode, row=True, col=True) for g in range(G)]
     for g, (s, e) in enumerate(grouped_ranges(offsets)):
         if e > s:
             H64[s:e] = gemm(px["row_codes"][s:e], px["row_scales"][s:e], w1[g]["row_codes"],
                             w1[g]["row_scales"], e - s, 2 * F, D, fmt)
     H = round_bf16(H64) if H_in is None else H_in[:Ract]
-    pz = quantize(np.ascontiguousarray(H), Ract, F, fmt, RCEIL, pro=PRO_SWIGLU, row=True, col=True) \
+    pz = quantize(np.ascontiguousarray(H), Ract, F, fmt, mode, pro=PRO_SWIGLU, row=True, col=True) \
         if Ract else None
     Y64 = np.zeros((Ract, D))
     for g, (s, e) in enumerate(grouped_ranges(offsets)):
         if e > s:
             Y64[s:e] = gemm(pz["row_codes"][s:e], pz["row_scales"][s:e], w2[g]["row_codes"],
                             w2[g]["row_scales"], e - s, D, F, fmt)
-    return {"X": px, "W1": w1, "W2": w2, "H64": H64, "H": H, "z": pz, "Y64": Y64}
+    return {"X": px, "W1": w1, "W2": w2, "H64": H64, "H": H, "z": pz, "Y64": Y64, "fmt": (fmt, mode)}
 
 
 def grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=None, H_in=None):
     """Routed-expert SwiGLU MLP backward: FC2 dgrad -> dz; dSwiGLU(dz, H) ->
     dH quantized rowwise and columnwise; FC1 dgrad; ragged-K weight
-    gradients (K = the expert's tokens; an empty expert's gradient is 0)."""
-    fmt = E4M3
+    gradients (K = the expert's tokens; an empty expert's gradient is 0).
+    Format and scale mode are the forward's."""
+    fmt, mode = fwd["fmt"]
     G = len(offsets)
     Ract = int(offsets[-1])
-    pdy = quantize(dY[:Ract], Ract, D, fmt, RCEIL, row=True, col=True) if Ract else None
+    pdy = quantize(dY[:Ract], Ract, D, fmt, mode, row=True, col=True) if Ract else None
     dz64 = np.zeros((Ract, F))
     for g, (s, e) in enumerate(grouped_ranges(offsets)):
         if e > s:
@@ -365,7 +365,7 @@ def grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=None, H_in=None):
                              fwd["W2"][g]["col_scales"], e - s, F, D, fmt)
     dz = round_bf16(dz64) if dz_in is None else dz_in[:Ract]
     H = fwd["H"] if H_in is None else H_in[:Ract]
-    pdh = quantize(np.ascontiguousarray(dz), Ract, 2 * F, fmt, RCEIL, pro=PRO_DSWIGLU,
+    pdh = quantize(np.ascontiguousarray(dz), Ract, 2 * F, fmt, mode, pro=PRO_DSWIGLU,
                    aux=np.ascontiguousarray(H), row=True, col=True) if Ract else None
     dX64 = np.zeros((Ract, D))
     dW1 = np.zeros((G, 2 * F, D))

@@ -284,14 +284,15 @@ def bf16_close(got_bf16, ref64):
     return np.all(np.abs(g - ref64) <= REL * np.max(np.abs(ref64)) + half_ulp)
 
 
-def test_fused_mlp_parity_small(mxl, orc):
+@pytest.mark.parametrize("fmt,mode,had", [(2, 0, True), (1, 0, False), (3, 1, False)])
+def test_fused_mlp_parity_small(mxl, orc, fmt, mode, had):
     M, D, F = 256, 256, 512
     X, W1, b1, W2, dY = I.mlp(302, M, D, F)
-    t = run_mlp(mxl, X, W1, b1, W2, dY, M, D, F)
+    t = run_mlp(mxl, X, W1, b1, W2, dY, M, D, F, fmt=fmt, mode=mode, had=had)
     h = host(t["h"])
-    fwd = orc.mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=h)
+    fwd = orc.mlp_fwd_ref(X, W1, b1, W2, M, D, F, h_in=h, fmt=fmt, mode=mode, had=had)
     KN = dict(Xr=D, W1r=D, W2r=F, Xc=M, W1c=F, W2c=D)
-    BITS = 6
+    BITS = mxl.BITS[fmt]
     for name, key in (("Xr", "X"), ("W1r", "W1"), ("W2r", "W2")):
         assert np.array_equal(untiled(host(t[name][0]), KN[name], BITS), fwd[key]["row_codes"]), name
         assert np.array_equal(unblocked(host(t[name][1]), KN[name] // 32), fwd[key]["row_scales"]), name
@@ -329,8 +330,7 @@ def test_fused_mlp_zero_output_projection(mxl):
 
 
 # ------------------------------------------------------------------ grouped
-def run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G):
-    fmt, mode = 3, 1
+def run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=3, mode=1):
     P = lambda r, k, b=None: mxl.alloc_packed(r, k, fmt, batch=b)
     off = dev(offsets.astype(np.int32))
     t = dict(Xr=P(R, D), Xc=P(D, R), W1r=P(2 * F, D, G), W1c=P(D, 2 * F, G), W2r=P(D, F, G), W2c=P(F, D, G),
@@ -342,24 +342,25 @@ def run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G):
     mxl.quantize(W1d, 2 * F, D, fmt, mode, row=t["W1r"], col=t["W1c"], batch=G)
     mxl.quantize(W2d, D, F, fmt, mode, row=t["W2r"], col=t["W2c"], batch=G)
     mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["Xr"], t["W1r"], t["H"], epilogue=mxl.EPI_SWIGLU, N=2 * F, K=D,
-                     out_row=t["zr"], out_col=t["zc"], validate_offsets=True)
-    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["zr"], t["W2r"], t["Y"], N=D, K=F)
+                     out_row=t["zr"], out_col=t["zc"], validate_offsets=True, fmt=fmt, scale_mode=mode)
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["zr"], t["W2r"], t["Y"], N=D, K=F, fmt=fmt, scale_mode=mode)
     mxl.quantize(dYd, R, D, fmt, mode, row=t["dYr"], col=t["dYc"])
     mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["dYr"], t["W2c"], t["dz"], epilogue=mxl.EPI_DSWIGLU, N=F, K=D,
-                     aux=t["H"], out_row=t["dHr"], out_col=t["dHc"])
-    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["dHr"], t["W1c"], t["dX"], N=D, K=2 * F)
-    mxl.grouped_gemm(mxl.RAGGED_K, G, R, off, t["dYc"], t["zc"], t["dW2"], M=D, N=F)
-    mxl.grouped_gemm(mxl.RAGGED_K, G, R, off, t["dHc"], t["Xc"], t["dW1"], M=2 * F, N=D)
+                     aux=t["H"], out_row=t["dHr"], out_col=t["dHc"], fmt=fmt, scale_mode=mode)
+    mxl.grouped_gemm(mxl.RAGGED_M, G, R, off, t["dHr"], t["W1c"], t["dX"], N=D, K=2 * F, fmt=fmt, scale_mode=mode)
+    mxl.grouped_gemm(mxl.RAGGED_K, G, R, off, t["dYc"], t["zc"], t["dW2"], M=D, N=F, fmt=fmt, scale_mode=mode)
+    mxl.grouped_gemm(mxl.RAGGED_K, G, R, off, t["dHc"], t["Xc"], t["dW1"], M=2 * F, N=D, fmt=fmt, scale_mode=mode)
     return t
 
 
-def test_grouped_parity_small(mxl, orc):
+@pytest.mark.parametrize("fmt,mode", [(3, 1), (1, 0), (2, 0)])
+def test_grouped_parity_small(mxl, orc, fmt, mode):
     R, D, F, G = 1024, 256, 256, 4
     counts, offsets, X, W1, W2, dY = I.grouped_mlp(502, R, D, F, G, zero_expert=2)
-    t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G)
-    BITS = 8
+    t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=fmt, mode=mode)
+    BITS = mxl.BITS[fmt]
     H = host(t["H"])
-    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H)
+    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H, fmt=fmt, mode=mode)
     assert bf16_close(H, fwd["H64"])
     assert np.array_equal(untiled(host(t["zr"][0]), F, BITS), fwd["z"]["row_codes"])
     assert np.array_equal(unblocked(host(t["zr"][1]), (F) // 32), fwd["z"]["row_scales"])
