@@ -18,17 +18,19 @@
 // Tiling.  256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN output
 // tile; a wavefront owns (BM/2) x (BN/2) = (BM/64) x (BN/64) MFMA tiles of
 // 32 x 32, whose accumulators live in AGPRs (one wavefront per SIMD).  K
-// advances BK elements per stage (128 for E2M1/E2M3, 64 for E4M3).  Stages
-// form a ring of S buffers in LDS filled by direct global -> LDS loads
-// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane), so
-// S - 1 stages are in flight while one is multiplied and no registers are
-// spent on staging.  A stage's rows are stored densely; the 16-byte chunks
-// of each row are permuted (XOR for E2M1 / E4M3, a rotation for E2M3's six
-// chunks) so that the 32 rows one operand read touches spread over all LDS
-// banks.  The loads of a stage are awaited with an explicit vmcnt, then one
-// barrier per stage publishes it to all wavefronts and frees the buffer that
-// the next issue overwrites.
-//
+// advances BK elements per stage (128 for E2M1/E2M3, 64 for E4M3), in steps
+// of 64 (one MFMA per output tile).  Stages form a ring of S = 3 or 4
+// buffers in LDS filled by direct global -> LDS loads (global_load_lds:
+// each lane's 16 bytes land at M0 + 16 * lane), so no registers are spent
+// on staging.  A stage's rows are stored densely; the 16-byte chunks of each
+// row are permuted (XOR for E2M1 / E4M3, a rotation for E2M3's six chunks)
+// so that the 32 rows one operand read touches spread over all LDS banks.
+// The main loop is software-pipelined by step: the LDS reads of the next
+// step's operands, and the global loads of a stage S - 1 ahead, are threaded
+// between the current step's MFMAs, and the one barrier per stage sits at
+// the start of its last step, so that the next stage's first operands are
+// read while the current stage's last MFMAs run.
+
 // Dense tiles are ordered for cache reuse: workgroups are dealt round-robin
 // to the 8 XCDs (each with its own L2), so consecutive workgroup ids are
 // remapped to give every XCD a contiguous range of tiles, and each range is
@@ -47,6 +49,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 #include "mx_device.h"
 #include "mx_kernels.h"
@@ -70,13 +73,13 @@ template <> struct MfmaFmt<kE2M1> { static constexpr int kCode = 4; };
 template <int FMT, int BM, int BN, int MODE, int EPI>
 struct Cfg {
   static constexpr int kBits = FmtTraits<FMT>::kBits;
-  // K elements per stage: whole 128-byte row segments for E2M1 (dense mode,
-  // where K is a multiple of 256) and E4M3; the grouped modes only promise
-  // multiples of 128
-  static constexpr int kBK = (FMT == kE2M1 && MODE == kDense) ? 256 : 128;
-  static constexpr int kRowBytes = kBK * kBits / 8;      // 128 / 96 / 128 bytes per row per stage
+  // K elements per stage: one 128-element K group (64 / 96 bytes per row)
+  // for E2M1 / E2M3, half of one (64 bytes) for E4M3, so that every stage
+  // fits a ring of three or four in the LDS
+  static constexpr int kBK = FMT == kE4M3 ? 64 : 128;
+  static constexpr int kRowBytes = kBK * kBits / 8;      // 64 / 96 / 64 bytes per row per stage
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
-  static constexpr int kScaleDw = kBK / 128;             // scale dwords (4 blocks each) per row per stage
+  static constexpr int kScaleDw = 1;                     // scale dword (4 blocks of 32 along K) per row per stage
   // 16-byte loads per thread per stage; a tile side whose chunks do not fill
   // whole loads (192 rows of 96 bytes) leaves the last load of some
   // wavefronts idle: they load a valid chunk into a junk area, so that every
@@ -91,7 +94,8 @@ struct Cfg {
   static constexpr int kSOff = kBOff + BN * kRowBytes;   // scale dwords: [dword][A rows, then B rows] (512 slots)
   static constexpr int kJOff = kSOff + kScaleDw * 512 * 4;
   static constexpr int kStage = kJOff + ((kARem || kBRem) ? 1024 : 0);
-  static constexpr int kStages = (4 * kStage <= 160 * 1024) ? 4 : ((3 * kStage <= 160 * 1024) ? 3 : 2);
+  static constexpr int kStages = (4 * kStage <= 160 * 1024) ? 4 : 3;
+  static_assert(kStages * kStage <= 160 * 1024, "three stages fit the LDS");
   static constexpr int kWM = BM / 2, kWN = BN / 2;
   static constexpr int kMI = kWM / 32, kNJ = kWN / 32;
   static constexpr int kLoads = kAIters + kBIters + 2 * kScaleDw;  // vector-memory instructions per stage per wave
@@ -108,17 +112,20 @@ struct Cfg {
 };
 
 // Position of logical 16-byte chunk c of row r among the row's NCH stored
-// chunks, chosen so that reads of one chunk by consecutive rows spread over
-// the 64 banks of the LDS:  NCH = 8: c ^ ((r ^ (r >> 3)) & 7);  NCH = 4:
-// c ^ (((r >> 1) ^ (r >> 3)) & 3);  NCH = 6 (96-byte rows, whose bases repeat
-// every 8 rows modulo 64 banks): (c + ((r >> 3) & 1)) % 6, which moves rows
-// 8..15 of every 16 by one 4-bank step.
+// chunks, chosen so that the 16-byte operand reads of one chunk by the 32
+// rows of a wavefront (its two halves reading adjacent chunks) take the
+// minimum four LDS cycles (measured with the bank-conflict counter on
+// gfx950): NCH = 8 (128-byte rows): c ^ ((r ^ (r >> 3)) & 7);  NCH = 4
+// (64-byte rows): c ^ ((r >> 2) & 3) -- a permutation that also depends on
+// row bit 4, or on rows r >> 1, costs twice that;  NCH = 6 (96-byte rows,
+// whose bases repeat every 8 rows modulo 64 banks): (c + ((r >> 3) & 1)) %
+// 6, which moves rows 8..15 of every 16 by one 4-bank step.
 template <int NCH>
 __device__ __forceinline__ int chunk_pos(int r, int c) {
   static_assert(NCH == 4 || NCH == 6 || NCH == 8, "chunks per row");
   if constexpr (NCH == 6) { const int q = c + ((r >> 3) & 1); return q >= 6 ? q - 6 : q; }
   else if constexpr (NCH == 8) return c ^ ((r ^ (r >> 3)) & 7);
-  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+  else return c ^ ((r >> 2) & 3);
 }
 // Inverse: the logical chunk stored at position pos of row r.
 template <int NCH>
@@ -138,6 +145,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 #endif
 }
 
+// Wait for every outstanding LDS read of this wavefront.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt and expcnt unconstrained, lgkmcnt 0
+#endif
+}
+
 // Workgroup barrier without a memory fence (the stage loads are awaited
 // explicitly with vmcnt); the empty asm keeps the compiler from moving LDS
 // accesses across it.
@@ -150,15 +164,35 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // Direct global -> LDS copy of 16 (4) bytes per lane: lane l's bytes land at
-// lds + 16 * l (lds + 4 * l); lds must be the same for the whole wavefront.
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+// LDS byte address lds + 16 * l (lds + 4 * l); lds must be the same for the
+// whole wavefront (it goes to M0, which an LDS DMA needs one wait state
+// after writing).  Written as inline assembly: the compiler models the
+// intrinsic as a flat access to both global memory and the LDS, and while
+// one is in flight it turns every LDS wait it inserts into a wait for all
+// outstanding reads.  Kernels order these loads with explicit vmcnt waits
+// and barriers.
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+}
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 #endif
 }
-__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+#endif
+}
+
+// Materialize a kernel argument in scalar registers at this point.  The
+// epilogue's arguments are pinned before the main loop: a scalar load still
+// in flight there shares the LDS wait counter, and the compiler then turns
+// every LDS wait in the loop into a wait for all outstanding reads.
+template <typename T>
+__device__ __forceinline__ void pin_arg(T v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"s"(v));
 #endif
 }
 
@@ -285,10 +319,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   // ---------------------------------------------------------------- loads
   // Stage slot s (16-byte units, s = i * 256 + t for load i of thread t)
   // holds row s / kChunks, position s % kChunks, i.e. logical chunk
-  // chunk_at(row, position) of the row's stage segment.  Byte 16c of that
-  // segment lies in K group c*16/kGB of the stage, at byte 16c % kGB of the
-  // row's kGB-byte run.  Offsets from the stage's first K group are 32-bit
-  // (operands < 2 GiB).
+  // chunk_at(row, position) of the row's stage segment.  A stage lies inside
+  // one 128-element K group: its segment of a row starts (k0 % 128) * bits/8
+  // bytes into the row's kGB-byte run of that group.  Offsets from the
+  // group's start are 32-bit (operands < 2 GiB).
   constexpr int BK = CF::kBK;
   uint32_t a_off[CF::kAIters], b_off[CF::kBIters];
 #pragma unroll
@@ -296,14 +330,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
     const int rr = r < BM ? r : 0;  // junk slots read a valid chunk
     const int c = chunk_at<CF::kChunks>(rr, pos);
-    a_off[i] = (uint32_t)(((16 * c) / kGB) * a_rows * kGB + (m0 + rr) * kGB + (16 * c) % kGB);
+    a_off[i] = (uint32_t)((m0 + rr) * kGB + 16 * c);
   }
 #pragma unroll
   for (int i = 0; i < CF::kBIters; ++i) {
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
     const int rr = r < BN ? r : 0;
     const int c = chunk_at<CF::kChunks>(rr, pos);
-    b_off[i] = (uint32_t)(b_coff + ((16 * c) / kGB) * b_rows * kGB + (b_row(rr) - b_row0) * kGB + (16 * c) % kGB);
+    b_off[i] = (uint32_t)(b_coff + (b_row(rr) - b_row0) * kGB + 16 * c);
   }
   // scale dwords (4 blocks of 32 along K, blocked layout): slot t and t + 256
   // of [A rows | B rows]; slots past BM + BN load row 0's dword into unused
@@ -318,6 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     s_step[j] = (is_b ? b_rows : a_rows) * 4;
   }
   const int wave_u = wave_uniform(wave);
+  const uint32_t smem_lds = wave_uniform((int)lds_addr(smem));  // LDS byte address of smem
 
   // Load q (0 <= q < kLoads) of stage k into ring buffer buf: A chunks, then
   // B chunks, then scale dwords (K group d, slot half j).  Every use sits in
@@ -326,16 +361,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #define MX_PIECE(k, buf, q)                                                                               \
   do {                                                                                                   \
     const int64_t k0_ = kbeg + (int64_t)(k) * BK;                                                        \
-    uint8_t* st_ = smem + (buf) * CF::kStage;                                                            \
+    const uint32_t st_ = smem_lds + (buf) * CF::kStage;                                                  \
     if ((q) < CF::kAIters) {                                                                             \
       const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
       const bool junk_ = CF::kARem && i_ == CF::kAIters - 1 && wave_u * 64 >= CF::kARem;                 \
-      lds_dma16(p.a_codes + (k0_ / 128) * a_rows * kGB + a_off[i_],                                      \
+      lds_dma16(p.a_codes + (k0_ / 128) * a_rows * kGB + (k0_ % 128) * kBits / 8 + a_off[i_],            \
                 st_ + (junk_ ? CF::kJOff : CF::kAOff + (i_ * 256 + wave_u * 64) * 16));                  \
     } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
       const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
       const bool junk_ = CF::kBRem && i_ == CF::kBIters - 1 && wave_u * 64 >= CF::kBRem;                 \
-      lds_dma16(p.b_codes + (k0_ / 128) * b_rows * kGB + b_off[i_],                                      \
+      lds_dma16(p.b_codes + (k0_ / 128) * b_rows * kGB + (k0_ % 128) * kBits / 8 + b_off[i_],            \
                 st_ + (junk_ ? CF::kJOff : CF::kBOff + (i_ * 256 + wave_u * 64) * 16));                  \
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
@@ -372,80 +407,152 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
   }
 
+  // Software pipeline over K steps of 64 (KS per stage).  The MFMAs of a step
+  // use operand fragments already in registers; the LDS reads of the next
+  // step's fragments are threaded between them, and so are the global -> LDS
+  // loads of a stage S - 1 ahead.  Each A fragment is re-read right after
+  // the last MFMA of the step that uses it; B fragments are double-buffered
+  // by step parity for E2M1 / E2M3, and re-read after their last use like A
+  // for E4M3, whose MFMAs take twice as long (the registers an E4M3 operand
+  // needs do not fit twice).  The last step of stage it first waits for
+  // stage it + 1 to land and passes the one barrier of the stage, so that
+  // its MFMAs overlap the reads of stage it + 1's first fragments and
+  // scales; after that barrier no wave reads buffer it % S any more, and the
+  // loads of stage it + S may refill it.  The loads of a stage are issued
+  // over a window of KS steps: the last step of stage st - S (after its
+  // barrier), then the first KS - 1 steps of stage st - S + 1, so at every
+  // barrier exactly the S - 2 stages after the awaited one may still be in
+  // flight.  Stages past the last one re-load the last stage's K range into
+  // their (free) ring buffers, and the last stage still passes its barrier
+  // and reads "its successor", so the loop has no branches and every wait
+  // count is a constant; the epilogue waits for those extra loads before it
+  // reuses the LDS.
   constexpr int S = CF::kStages;
   constexpr int KS = BK / 64;
-  // Loads of the stage S - 1 ahead are spread over this stage's MFMAs, kPer
-  // per K step, one after every kEvery-th MFMA: issued in one burst they
-  // stall the wavefront at issue while the address units drain them.
-  constexpr int kMf = CF::kMI * CF::kNJ;
-  constexpr int kPer = (CF::kLoads + KS - 1) / KS;
-  constexpr int kEvery = kMf / kPer > 0 ? kMf / kPer : 1;
-  static_assert(kPer <= kMf, "every load needs an MFMA slot");
+  constexpr bool kBDouble = KS == 2;
+  constexpr int kMf = CF::kMI * CF::kNJ;  // MFMAs per step
+  constexpr int kWin = KS * kMf;          // MFMA slots in a stage's load window
+  constexpr int kPart0 = (CF::kLoads + KS - 1) / KS;  // loads in the window's first step
+  static_assert(CF::kLoads <= kWin, "one load per MFMA slot at most");
+  static_assert(KS == 1 || KS == 2, "steps per stage");
+  // fragment reads (and, across a stage boundary, the scale reads) go in
+  // the first three quarters of a step's MFMA slots where the registers
+  // allow, so that they have landed when the next step starts
+  constexpr int kReadSlots = kMf > 4 ? (3 * kMf) / 4 : kMf;
+  // slot of read unit u (issued after that slot's MFMA): spread over the
+  // read slots, but a single-buffered fragment no earlier than the last MFMA
+  // that uses it.  Units: [the scales,] A0, B0 .. B(NJ-1), A1 .. A(MI-1).
+  auto read_slot = [](int u, bool with_scales) constexpr {
+    const int nu = CF::kMI + CF::kNJ + (with_scales ? 1 : 0);
+    const int v = with_scales ? u - 1 : u;
+    const int nominal = u * kReadSlots / nu;
+    int first = 0;
+    if (v == 0 || v > CF::kNJ) first = (v == 0 ? 0 : v - CF::kNJ) * CF::kNJ + CF::kNJ - 1;  // A
+    else if (v > 0 && !kBDouble) first = (CF::kMI - 1) * CF::kNJ + (v - 1);                 // B
+    return nominal > first ? nominal : first;
+  };
+
+  v8i af[CF::kMI], bf[kBDouble ? 2 : 1][CF::kNJ];
+  uint32_t sca[CF::kMI], scb[CF::kNJ];  // this stage's scale dwords, shifted so byte 0 is its block g
+  uint32_t nsa[CF::kMI], nsb[CF::kNJ];  // the next stage's scale dwords as stored
+
+  auto read_scales = [&](const uint8_t* sbuf) __attribute__((always_inline)) {
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (st < nk) MX_ISSUE(st, st);
+    for (int i = 0; i < CF::kMI; ++i) nsa[i] = *reinterpret_cast<const uint32_t*>(sbuf + CF::kSOff + arow[i] * 4);
+#pragma unroll
+    for (int j = 0; j < CF::kNJ; ++j) nsb[j] = *reinterpret_cast<const uint32_t*>(sbuf + CF::kSOff + (BM + brow[j]) * 4);
+  };
+  // fragment v of a step (v = 0: A0, 1 .. NJ: B0 .. B(NJ-1), then A1 ..)
+  auto read_frag = [&](int buf, int v, const uint8_t* sbuf, int ks) __attribute__((always_inline)) {
+    if (v == 0 || v > CF::kNJ) {
+      const int i = v == 0 ? 0 : v - CF::kNJ;
+      af[i] = lds_operand<FMT, CF::kChunks>(sbuf + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], ks, g);
+    } else {
+      const int j = v - 1;
+      bf[kBDouble ? buf : 0][j] =
+          lds_operand<FMT, CF::kChunks>(sbuf + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], ks, g);
+    }
+  };
 
-  // One stage: wait for it, then its MFMAs, with (ISSUE) the loads of stage
-  // it + S - 1 threaded between them.
-#define MX_STAGE(ISSUE)                                                                                   \
-  do {                                                                                                   \
-    if (ISSUE) wait_vmcnt<CF::kLoads * (S - 2)>(); /* stage it landed (this wave's part) */              \
-    else wait_vmcnt<0>();                                                                                \
-    stage_barrier(); /* ... and every wave's; buffer (it - 1) % S is free again */                       \
-    const uint8_t* sb = smem + (it % S) * CF::kStage;                                                    \
-    const int nb_ = (it + S - 1) % S;                                                                    \
-    /* scale dwords of this lane's rows (one per 128 K), read once per stage */                         \
-    uint32_t sda[CF::kScaleDw][CF::kMI], sdb[CF::kScaleDw][CF::kNJ];                                     \
-    _Pragma("unroll") for (int d = 0; d < CF::kScaleDw; ++d) {                                           \
-      _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                                \
-        sda[d][i] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + arow[i]) * 4);       \
-      _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j)                                                \
-        sdb[d][j] = *reinterpret_cast<const uint32_t*>(sb + CF::kSOff + (d * 512 + BM + brow[j]) * 4);  \
-    }                                                                                                    \
-    sched_fence();                                                                                       \
-    /* operand fragments double-buffered in registers: the reads of K step */                           \
-    /* ks + 1 are in flight while the MFMAs of step ks run */                                            \
-    v8i af[2][CF::kMI], bf[2][CF::kNJ];                                                                  \
-    _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                                  \
-      af[0][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], 0, g); \
-    _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j)                                                  \
-      bf[0][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], 0, g); \
-    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                                  \
-      const int cb = ks & 1;                                                                             \
-      if (ks + 1 < KS) {                                                                                 \
-        _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                              \
-          af[cb ^ 1][i] = lds_operand<FMT, CF::kChunks>(sb + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], ks + 1, g); \
-        _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j)                                              \
-          bf[cb ^ 1][j] = lds_operand<FMT, CF::kChunks>(sb + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], ks + 1, g); \
-      }                                                                                                  \
-      sched_fence(); /* the reads above are issued before the MFMAs below */                             \
-      /* E8M0 byte of K block 2 ks + g of the stage (k0 % 128 == 0 at every stage start) */             \
-      const int bi = 2 * ks;                                                                             \
-      int sa[CF::kMI], sbs[CF::kNJ];                                                                     \
-      _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i) sa[i] = (int)(sda[bi >> 2][i] >> (8 * ((bi & 3) + g))); \
-      _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j) sbs[j] = (int)(sdb[bi >> 2][j] >> (8 * ((bi & 3) + g))); \
-      _Pragma("unroll") for (int i = 0; i < CF::kMI; ++i)                                                \
-      _Pragma("unroll") for (int j = 0; j < CF::kNJ; ++j) {                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                     \
-            bf[cb][j], af[cb][i], acc[i][j], MfmaFmt<FMT>::kCode, MfmaFmt<FMT>::kCode, 0, sbs[j], 0, sa[i]); \
-        const int f_ = i * CF::kNJ + j;                                                                  \
-        if (ISSUE && f_ % kEvery == kEvery - 1 && f_ / kEvery < kPer) {                                  \
-          const int q_ = ks * kPer + f_ / kEvery;                                                        \
-          if (q_ < CF::kLoads) {                                                                         \
-            sched_fence();                                                                               \
-            MX_PIECE(it + S - 1, nb_, q_);                                                               \
-            sched_fence();                                                                               \
-          }                                                                                              \
-        }                                                                                                \
-      }                                                                                                  \
-      sched_fence();                                                                                     \
-    }                                                                                                    \
-  } while (0)
+  // one step: stage it, K step ks of the stage
+  auto step = [&](int it, auto ksc) __attribute__((always_inline)) {
+    constexpr int ks = decltype(ksc)::value;
+    constexpr int cur = kBDouble ? ks : 0;  // B fragment buffer of this step
+    constexpr int sel = 2 * ks;             // byte of the shifted scale dwords: block 2 ks + g of the stage
+    constexpr bool last = ks == KS - 1;
+    if (last) {
+      wait_vmcnt<CF::kLoads * (S - 2)>();  // this wave's loads of stage it + 1 landed
+      wait_lgkmcnt0();  // every read of buffer it % S done before the barrier frees it
+      stage_barrier();
+    }
+    const uint8_t* rbuf = smem + ((last ? it + 1 : it) % S) * CF::kStage;  // the next step's stage
+    constexpr int rks = last ? 0 : ks + 1;
+    const int lst = last ? it + S : it + S - 1;  // stage whose loads this step issues
+    constexpr int w = last ? 0 : ks + 1;         // ... and its window step
+    const int lk = lst < nk ? lst : nk - 1;      // its K range (the last stage's past the end)
+    const int lbuf = lst % S;
+    constexpr int U = CF::kMI + CF::kNJ + (last ? 1 : 0);  // read units: [scales,] fragments
+#pragma unroll
+    for (int f = 0; f < kMf; ++f) {
+      const int i = f / CF::kNJ, j = f % CF::kNJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          bf[cur][j], af[i], acc[i][j], MfmaFmt<FMT>::kCode, MfmaFmt<FMT>::kCode, sel, (int)scb[j], sel, (int)sca[i]);
+      sched_fence();
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (read_slot(u, last) == f) {
+          if (last && u == 0) read_scales(rbuf);
+          else read_frag(cur ^ 1, last ? u - 1 : u, rbuf, rks);
+        }
+#pragma unroll
+      for (int q = 0; q < CF::kLoads; ++q)
+        if (q * kWin / CF::kLoads == w * kMf + f) MX_PIECE(lk, lbuf, q);
+      sched_fence();
+    }
+  };
+  auto stage = [&](int it) __attribute__((always_inline)) {
+    // K block of byte 0: g, or 2 (it & 1) + g for 64-element stages (a
+    // dword holds the four blocks of one 128-element group)
+    const int sh = 8 * g + (KS == 1 ? 16 * (it & 1) : 0);
+#pragma unroll
+    for (int i = 0; i < CF::kMI; ++i) sca[i] = nsa[i] >> sh;
+#pragma unroll
+    for (int j = 0; j < CF::kNJ; ++j) scb[j] = nsb[j] >> sh;
+    step(it, std::integral_constant<int, 0>{});
+    if constexpr (KS == 2) step(it, std::integral_constant<int, 1>{});
+  };
 
-  int it = 0;
-  for (; it + S - 1 < nk; ++it) MX_STAGE(true);
-  for (; it < nk; ++it) MX_STAGE(false);
-#undef MX_STAGE
+  pin_arg(p.c);
+  pin_arg(p.ldc);
+  pin_arg(p.c_f32);
+  if constexpr (EPI == kEpiStore) {
+    pin_arg(p.bias);
+    pin_arg(p.bias_f32);
+  } else {
+    pin_arg(p.F);
+    pin_arg(p.R);
+    pin_arg(p.q_mode);
+    pin_arg(p.q_row_codes);
+    pin_arg(p.q_row_scales);
+    pin_arg(p.q_col_codes);
+    pin_arg(p.q_col_scales);
+    if constexpr (EPI == kEpiDSwiglu) pin_arg(p.aux);
+  }
+  if (nk > 0) {  // (a ragged-K group may be empty)
+    // prologue: stages 0 .. S - 2 and the first window step of stage S - 1
+    // in flight; stage 0's scales and first fragments read
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) MX_ISSUE(st < nk ? st : nk - 1, st);
+#pragma unroll
+    for (int q = 0; q < kPart0; ++q) MX_PIECE(S - 1 < nk ? S - 1 : nk - 1, S - 1, q);
+    wait_vmcnt<CF::kLoads * (S - 2) + kPart0>();
+    stage_barrier();
+    read_scales(smem);
+#pragma unroll
+    for (int v = 0; v < CF::kMI + CF::kNJ; ++v) read_frag(0, v, smem, 0);
+    for (int it = 0; it < nk; ++it) stage(it);
+    wait_vmcnt<0>();  // the loads past the last stage, before the LDS is reused
+  }
 #undef MX_PIECE
 #undef MX_ISSUE
   __syncthreads();  // all wavefronts are done with the stage ring before the epilogue reuses LDS
