@@ -19,8 +19,11 @@ Flux-12B block linears at M=16384 and the MXFP8 grouped SwiGLU MLP
 (G=8, D=2048, F=768, R=32768).
 
 The timed steps replay one captured HIP graph per input copy (--no-graph:
-eager launches); per-launch durations come from HIP events around each
-launch in a second loop over the same steps.
+eager launches), on one stream (--two-streams: dgrad and wgrad beside fwd
+-- measured slower).  One launch (mx_quantize_many) packs X, W and dY.
+Per-launch
+device durations come from HIP events around replays of a graph of ten
+back-to-back copies of each launch.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--extra all|none] [--no-cpu-baseline] [--no-graph]
 """
@@ -110,15 +113,37 @@ class LinearStep:
         e16 = lambda *s: torch.empty(s, dtype=torch.int16, device="cuda")
         self.Y, self.dX, self.dW = e16(M, N), e16(M, K), e16(N, K)
 
-    def run(self, i, T):
+    def calls(self, i):
+        """The four launches of one step: (name, fn, args, kwargs)."""
         mx, M, N, K, f, m, h = self.mx, self.M, self.N, self.K, self.fmt, self.mode, self.had
         X, W, dY = self.inp[i % len(self.inp)]
-        T.run("pack_X", mx.quantize, X, M, K, f, m, h, row=self.Xr, col=self.Xc)
-        T.run("pack_W", mx.quantize, W, N, K, f, m, h, row=self.Wr, col=self.Wc)
-        T.run("pack_dY", mx.quantize, dY, M, N, f, m, h, row=self.dYr, col=self.dYc)
-        T.run("gemm_fwd", mx.gemm, self.Xr, self.Wr, M, N, K, f, self.Y)
-        T.run("gemm_dgrad", mx.gemm, self.dYr, self.Wc, M, K, N, f, self.dX)
-        T.run("gemm_wgrad", mx.gemm, self.dYc, self.Xc, N, K, M, f, self.dW)
+        items = [dict(x=X, R=M, C=K, row=self.Xr, col=self.Xc), dict(x=W, R=N, C=K, row=self.Wr, col=self.Wc),
+                 dict(x=dY, R=M, C=N, row=self.dYr, col=self.dYc)]
+        return {"pack_XWdY": (mx.quantize_many, (items, f, m, h), {}),
+                "gemm_fwd": (mx.gemm, (self.Xr, self.Wr, M, N, K, f, self.Y), {}),
+                "gemm_dgrad": (mx.gemm, (self.dYr, self.Wc, M, K, N, f, self.dX), {}),
+                "gemm_wgrad": (mx.gemm, (self.dYc, self.Xc, N, K, M, f, self.dW), {})}
+
+    def run(self, i, T, side=None):
+        """One step: one launch packs X, W and dY (row + column each), then
+        the three GEMMs.  With a side stream, dgrad and wgrad run on it
+        beside fwd; the caller's stream waits for the side stream at the
+        end."""
+        import torch
+        c = self.calls(i)
+        go = lambda n: T.run(n, c[n][0], *c[n][1], **c[n][2])
+        if side is None:
+            for n in ("pack_XWdY", "gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
+                go(n)
+            return
+        main = torch.cuda.current_stream()
+        go("pack_XWdY")
+        side.wait_stream(main)
+        go("gemm_fwd")
+        with torch.cuda.stream(side):
+            go("gemm_dgrad")
+            go("gemm_wgrad")
+        main.wait_stream(side)
 
     def flops(self):
         return 3 * 2.0 * self.M * self.N * self.K
@@ -139,28 +164,59 @@ def time_steps(fn, steps, warmup, T):
     return dt / steps
 
 
-def capture_steps(step, copies):
-    """One HIP graph per input copy, each holding one whole step (the six
-    launches), so that the timed loop replays launches without host work in
-    between.  The captured calls are the same C-ABI entry points, enqueued
-    on torch's capture stream."""
+def capture_steps(step, copies, concurrent=True):
+    """One HIP graph per input copy, each holding one whole step (the four
+    launches; with `concurrent`, the two-stream schedule of LinearStep.run,
+    captured as parallel branches), so that the timed loop replays launches
+    without host work in between.  The captured calls are the same C-ABI
+    entry points, enqueued on torch's capture stream (and a side stream
+    forked from it)."""
     import torch
     T = Timer()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    warm = torch.cuda.Stream()
+    side = torch.cuda.Stream() if concurrent else None
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
         for c in range(copies):
-            step.run(c, T)
-    torch.cuda.current_stream().wait_stream(side)
+            step.run(c, T, side)
+    torch.cuda.current_stream().wait_stream(warm)
     torch.cuda.synchronize()
     graphs = []
     for c in range(copies):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step.run(c, T)
+            step.run(c, T, side)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
+
+
+def graph_time(launch, reps=10, replays=4, warm=None):
+    """Device time of one launch: a graph of `reps` back-to-back calls
+    `launch(r)` (r = 0 .. reps-1) replayed `replays` times between HIP events
+    on the replay stream; the average per call excludes host launch cost.
+    `warm(r)` runs eagerly first (default: `launch`)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(reps):
+            (warm or launch)(r)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(reps):
+            launch(r)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * replays)
 
 
 def time_graph_steps(graphs, steps, warmup):
@@ -175,6 +231,18 @@ def time_graph_steps(graphs, steps, warmup):
         graphs[(warmup + i) % len(graphs)].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def kernel_times(step):
+    """Device time (us) of each of the step's four launches, each repeated
+    back to back over the rotating input copies."""
+    out = {}
+    for name in step.calls(0):
+        def launch(r, name=name):
+            fn, a, kw = step.calls(r)[name]
+            fn(*a, **kw)
+        out[name] = graph_time(launch)
+    return out
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -320,10 +388,8 @@ def only(mx, spec, steps, warmup, T):
         n = int(fbits)
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        sec = time_steps(lambda i: T.run("copy", dst.copy_, src), steps, warmup, T)
-        us = T.summary()["copy"]
-        print(json.dumps({"only": spec, "us": us, "gbs": 2 * n / (us * 1e-6) / 1e9, "ms_per_iter": sec * 1e3}),
-              flush=True)
+        us = graph_time(lambda r: dst.copy_(src), reps=steps)
+        print(json.dumps({"only": spec, "us": us, "gbs": 2 * n / (us * 1e-6) / 1e9}), flush=True)
         return
     fmt = {"4": mx.E2M1, "6": mx.E2M3, "8": mx.E4M3}[fbits]
     mode = mx.RCEIL if fmt == mx.E4M3 else mx.FLOOR
@@ -335,20 +401,15 @@ def only(mx, spec, steps, warmup, T):
         mx.quantize(dev(A), M, K, fmt, mode, had, row=pa)
         mx.quantize(dev(B), N, K, fmt, mode, had, row=pb)
         C = torch.empty((M, N), dtype=torch.int16, device="cuda")
-        sec = time_steps(lambda i: T.run("gemm", mx.gemm, pa, pb, M, N, K, fmt, C), steps, warmup, T)
-        us = T.summary()["gemm"]
-        print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12,
-                          "ms_per_iter": sec * 1e3}), flush=True)
+        us = graph_time(lambda r: mx.gemm(pa, pb, M, N, K, fmt, C), reps=steps)
+        print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
     else:
         R, C = (int(v) for v in dims)
         X = dev(I.bf16_normal(np.random.default_rng(7), (R, C)))
         row, col = mx.alloc_packed(R, C, fmt), mx.alloc_packed(C, R, fmt)
-        sec = time_steps(lambda i: T.run("pack", mx.quantize, X, R, C, fmt, mode, had, row=row, col=col),
-                         steps, warmup, T)
-        us = T.summary()["pack"]
+        us = graph_time(lambda r: mx.quantize(X, R, C, fmt, mode, had, row=row, col=col), reps=steps)
         b = R * C * (2 + 2 * PACK_OUT[int(fbits)])
-        print(json.dumps({"only": spec, "us": us, "gbs": b / (us * 1e-6) / 1e9, "ms_per_iter": sec * 1e3}),
-              flush=True)
+        print(json.dumps({"only": spec, "us": us, "gbs": b / (us * 1e-6) / 1e9}), flush=True)
 
 
 # ------------------------------------------------------------------ main
@@ -360,6 +421,8 @@ def main():
     ap.add_argument("--extra", choices=["all", "none"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="capture the step on two streams (independent launches overlapping) instead of one")
     ap.add_argument("--only", default=None,
                     help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C (FMT = 4, 6 or 8) "
                          "or copy:BYTES (a plain device copy)")
@@ -386,27 +449,27 @@ def main():
     if args.no_graph:
         sec = time_steps(lambda i: step.run(i, T), args.steps, args.warmup, Timer())
     else:
-        graphs = capture_steps(step, len(step.inp))
+        graphs = capture_steps(step, len(step.inp), concurrent=args.two_streams)
         sec = time_graph_steps(graphs, args.steps, args.warmup)
-    # per-launch durations: HIP events around each launch on the launch stream
-    # (separate loop, so that the event records do not stretch the steps)
-    time_steps(lambda i: step.run(i, T), args.steps, 1, T)
-    k = T.summary()
+    # per-launch device durations (graphs of repeated launches, after the
+    # timed steps)
+    k = kernel_times(step)
     value = step.flops() / sec / 1e12
     gemm_us = float(np.mean([k["gemm_fwd"], k["gemm_dgrad"], k["gemm_wgrad"]]))
     gemm_flops = 2.0 * M * N * K
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
-    pack_bytes = M * K * (2 + 2 * PACK_OUT[6])
+    # algorithmic bytes of the fused pack: X [M,K], W [N,K], dY [M,N], each read once (bf16) and written twice
+    pack_bytes = (M * K + N * K + M * N) * (2 + 2 * PACK_OUT[6])
     kernels = {n: {"us": round(v, 2)} for n, v in k.items()}
     for n in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
         kernels[n]["tflops"] = round(gemm_flops / (k[n] * 1e-6) / 1e12, 1)
-    for n, (r, c) in (("pack_X", (M, K)), ("pack_W", (N, K)), ("pack_dY", (M, N))):
-        kernels[n]["gbs"] = round(r * c * (2 + 2 * PACK_OUT[6]) / (k[n] * 1e-6) / 1e9, 1)
+    kernels["pack_XWdY"]["gbs"] = round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp6 (e2m3 x e2m3, fp32 accumulate)", "data": "synthetic",
-        "launch": "eager" if args.no_graph else "hip_graph (one captured step per input copy)",
+        "launch": "eager" if args.no_graph else ("hip_graph (one captured step per input copy, "
+                                                 + ("two streams)" if args.two_streams else "one stream)")),
         "config": {"workload": "MXFP6 linear (E2M3, FLOOR, Hadamard-32) X[4096,3072] W[3072,3072]: dual packs "
                                "of X, W, dY + fwd, dgrad, wgrad GEMMs, bf16 out",
                    "M": M, "N": N, "K": K, "format": "mxfp6", "gemm_flops_per_step": step.flops()},
@@ -414,9 +477,9 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp6"], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": gemm_traffic(),
                      "traffic_unit": "bytes per launch (HBM read + write)"},
-        "quantizer": {"kernel": "pack_kernel<E2M3, Hadamard> dual pack of X", "achieved_gbs":
-                      round(pack_bytes / (k["pack_X"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
-                      "frac": round(pack_bytes / (k["pack_X"] * 1e-6) / 1e9 / HBM_GBS, 4)},
+        "quantizer": {"kernel": "pack_many_kernel<E2M3, Hadamard>: dual packs of X, W and dY in one launch",
+                      "achieved_gbs": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
+                      "frac": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9 / HBM_GBS, 4)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

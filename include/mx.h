@@ -159,6 +159,41 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
                 void* col_codes, void* col_scales, float* colsum_partials, float* colsum,
                 void* stream);
 
+/*
+ * mx_quantize_many -- several packs of one format, scale mode, rotation and
+ * prologue in a single launch, with the results of n mx_quantize calls made
+ * with each item's arguments.  For callers that pack several tensors at
+ * once (a linear layer's activation, weight and output gradient before its
+ * forward, data-gradient and weight-gradient GEMMs, [P1] description): one
+ * launch keeps every compute unit busy where n small launches each leave
+ * the GPU idle while they start and drain.
+ *
+ *  items        host array of n items; each item's fields have the meaning
+ *               and rules of the mx_quantize arguments of the same names
+ *               (row / col: {codes, scales}, either pair {NULL, NULL}).  The
+ *               outputs of distinct items must not overlap.
+ *  n            1 <= n <= MX_QUANTIZE_MANY_MAX.
+ *  fmt, scale_mode, hadamard, prologue   as for mx_quantize, shared by all
+ *               items.
+ * Items with R = 0 or C = 0 are skipped.  The colsum of an item that asks
+ * for one is finished by one extra small launch per such item.
+ * Errors: MX_ERR_NULL (items NULL, or an item's pointers as for
+ * mx_quantize), MX_ERR_SHAPE (n out of range, or an item's sizes), then as
+ * mx_quantize for the first failing item; nothing is enqueued on an error.
+ */
+#define MX_QUANTIZE_MANY_MAX 8
+typedef struct {
+  const void* x;
+  const void* aux;
+  int64_t batch, R, C;
+  mx_packed row, col;
+  float* colsum_partials;
+  float* colsum;
+} mx_quantize_item;
+
+int mx_quantize_many(const mx_quantize_item* items, int n, int fmt, int scale_mode, int hadamard, int prologue,
+                     void* stream);
+
 /* ---------------------------------------------------------------- GEMM */
 /*
  * mx_gemm -- C[m][n] = sum_k A[m][k] * B[n][k] (+ bias[n]) on packed

@@ -171,6 +171,50 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
                          col_codes, col_scales, colsum_partials, colsum, static_cast<hipStream_t>(stream));
 }
 
+int mx_quantize_many(const mx_quantize_item* items, int n, int fmt, int scale_mode, int hadamard, int prologue,
+                     void* stream) {
+  if (!items) return MX_ERR_NULL;
+  if (n < 1 || n > MX_QUANTIZE_MANY_MAX) return MX_ERR_SHAPE;
+  static_assert(MX_QUANTIZE_MANY_MAX == mx::kPackManyMax, "item limit");
+  mx::PackMany m;
+  memset(&m, 0, sizeof m);
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const mx_quantize_item& it = items[i];
+    int st = validate_quantize(it.x, it.aux, it.batch, it.R, it.C, fmt, scale_mode, hadamard, prologue,
+                               it.row.codes, it.row.scales, it.col.codes, it.col.scales, it.colsum_partials,
+                               it.colsum);
+    if (st != MX_OK) return st;
+    PackParams& p = m.p[i];
+    p.x = static_cast<const uint16_t*>(it.x);
+    p.aux = static_cast<const uint16_t*>(it.aux);
+    p.R = it.R;
+    p.C = it.C;
+    p.row_codes = static_cast<uint8_t*>(it.row.codes);
+    p.row_scales = static_cast<uint8_t*>(it.row.scales);
+    p.col_codes = static_cast<uint8_t*>(it.col.codes);
+    p.col_scales = static_cast<uint8_t*>(it.col.scales);
+    p.partials = it.colsum_partials;
+    m.first[i] = tiles;
+    tiles += ((it.C + 127) / 128) * ((it.R + 127) / 128) * it.batch;
+  }
+  m.first[n] = tiles;
+  m.n = n;
+  if (!grid_fits(tiles, 1, 1)) return MX_ERR_INDEX_OVERFLOW;
+  int st = check_device();
+  if (st != MX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launched(mx::launch_pack_many(m, fmt, scale_mode, hadamard, prologue, s))) != MX_OK) return st;
+  for (int i = 0; i < n; ++i) {
+    const mx_quantize_item& it = items[i];
+    if (it.colsum && it.R > 0 && it.C > 0)
+      if ((st = launched(mx::launch_colsum_finish(it.colsum_partials, it.R / 32, it.C, it.colsum, it.batch, s))) !=
+          MX_OK)
+        return st;
+  }
+  return MX_OK;
+}
+
 int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
             int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
             void* stream) {

@@ -123,7 +123,7 @@ __device__ __forceinline__ void hadamard32(float (&y)[32]) {
 // codes.
 template <int FMT, int MODE>
 __device__ __forceinline__ uint32_t quant_block(const float (&v)[32], uint32_t (&w)[FmtTraits<FMT>::kBits]) {
-  constexpr int B = FmtTraits<FMT>::kBits;
+  [[maybe_unused]] constexpr int B = FmtTraits<FMT>::kBits;
   uint32_t amax = 0u;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {

@@ -48,9 +48,19 @@ struct PackParams {
   float* partials;      // [R/32][C] or nullptr
 };
 
+// Up to kPackManyMax tensors packed in one launch: item i owns workgroups
+// first[i] .. first[i + 1] - 1 (ceil(C/128) * ceil(R/128) * batch of them).
+constexpr int kPackManyMax = 8;
+struct PackMany {
+  PackParams p[kPackManyMax];
+  int64_t first[kPackManyMax + 1];
+  int n;
+};
+
 bool pack_supported(int fmt, int mode, int had, int pro);
 hipError_t launch_pack(const PackParams& p, int fmt, int mode, int had, int pro, int64_t batch,
                        hipStream_t stream);
+hipError_t launch_pack_many(const PackMany& m, int fmt, int mode, int had, int pro, hipStream_t stream);
 hipError_t launch_colsum_finish(const float* partials, int64_t nb, int64_t C, float* out, int64_t batch,
                                 hipStream_t stream);
 

@@ -120,14 +120,14 @@ __device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<
   }
 }
 
-// One workgroup packs one 128 x 128 tile of one batch entry.
+// One workgroup packs one 128 x 128 tile (column tile bx, row tile by) of
+// batch entry z.
 template <int FMT, int MODE, int HAD, int PRO>
-__global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
+__device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64_t by, int64_t z,
+                                          uint8_t* tile) {
   constexpr int B = FmtTraits<FMT>::kBits;
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * kTileR, c0 = (int64_t)blockIdx.x * kTileC;
-  const int64_t z = blockIdx.z;
+  const int64_t r0 = by * kTileR, c0 = bx * kTileC;
   const int64_t in_cols = (PRO == kSwiglu) ? 2 * p.C : (PRO == kDSwiglu ? p.C / 2 : p.C);
   const uint16_t* xb = p.x + z * p.R * in_cols;
   const uint16_t* ab = p.aux ? p.aux + z * p.R * p.C : nullptr;
@@ -215,6 +215,26 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   }
 }
 
+template <int FMT, int MODE, int HAD, int PRO>
+__global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
+  pack_tile<FMT, MODE, HAD, PRO>(p, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+}
+
+// Several tensors in one launch: workgroup w packs tile w - first[i] of
+// item i, with first[i] <= w < first[i + 1]; an item's tiles are ordered
+// column tile fastest, then row tile, then batch entry.
+template <int FMT, int MODE, int HAD, int PRO>
+__global__ __launch_bounds__(256) void pack_many_kernel(PackMany m) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
+  const int64_t w = blockIdx.x;
+  int i = 0;
+  while (i + 1 < m.n && w >= m.first[i + 1]) ++i;
+  const int64_t local = w - m.first[i];
+  const int64_t tx = (m.p[i].C + kTileC - 1) / kTileC, ty = (m.p[i].R + kTileR - 1) / kTileR;
+  pack_tile<FMT, MODE, HAD, PRO>(m.p[i], local % tx, (local / tx) % ty, local / (tx * ty), tile);
+}
+
 // db[c] = sum over blocks b (increasing) of partials[b][c], from +0.
 __global__ __launch_bounds__(256) void colsum_finish_kernel(const float* partials, int64_t nb, int64_t C,
                                                             float* out) {
@@ -228,38 +248,63 @@ __global__ __launch_bounds__(256) void colsum_finish_kernel(const float* partial
 }
 
 using PackFn = void (*)(PackParams);
+using PackManyFn = void (*)(PackMany);
 
-template <int FMT, int MODE, int HAD>
-PackFn pick_pro(int pro) {
+// The kernel of one (format, scale mode, rotation, prologue) combination,
+// for one tensor per launch (PackKernels) or several (ManyAsOne).
+template <int FMT, int MODE, int HAD, int PRO>
+struct PackKernels {
+  static constexpr PackFn one = pack_kernel<FMT, MODE, HAD, PRO>;
+};
+
+template <template <int, int, int, int> class K, int FMT, int MODE, int HAD>
+auto pick_pro(int pro) -> decltype(K<FMT, MODE, HAD, kIdentity>::one) {
   switch (pro) {
-    case kIdentity: return pack_kernel<FMT, MODE, HAD, kIdentity>;
-    case kGelu: return pack_kernel<FMT, MODE, HAD, kGelu>;
-    case kDGelu: return pack_kernel<FMT, MODE, HAD, kDGelu>;
-    case kSwiglu: return pack_kernel<FMT, MODE, HAD, kSwiglu>;
-    case kDSwiglu: return pack_kernel<FMT, MODE, HAD, kDSwiglu>;
+    case kIdentity: return K<FMT, MODE, HAD, kIdentity>::one;
+    case kGelu: return K<FMT, MODE, HAD, kGelu>::one;
+    case kDGelu: return K<FMT, MODE, HAD, kDGelu>::one;
+    case kSwiglu: return K<FMT, MODE, HAD, kSwiglu>::one;
+    case kDSwiglu: return K<FMT, MODE, HAD, kDSwiglu>::one;
     default: return nullptr;
   }
 }
 
-PackFn pick(int fmt, int mode, int had, int pro) {
-  if (fmt == kE2M1 && mode == kFloor && !had) return pick_pro<kE2M1, kFloor, 0>(pro);
-  if (fmt == kE2M3 && mode == kFloor && !had) return pick_pro<kE2M3, kFloor, 0>(pro);
-  if (fmt == kE2M3 && mode == kFloor && had) return pick_pro<kE2M3, kFloor, 1>(pro);
-  if (fmt == kE4M3 && mode == kRceil && !had) return pick_pro<kE4M3, kRceil, 0>(pro);
-  if (fmt == kE4M3 && mode == kFloor && !had) return pick_pro<kE4M3, kFloor, 0>(pro);
+template <int FMT, int MODE, int HAD, int PRO>
+struct ManyAsOne {
+  static constexpr PackManyFn one = pack_many_kernel<FMT, MODE, HAD, PRO>;
+};
+
+// The served combinations (FLOOR for every format, RCEIL for E4M3, the
+// rotation for E2M3), through kernel family K.
+template <template <int, int, int, int> class K>
+auto pick(int fmt, int mode, int had, int pro) -> decltype(K<kE2M1, kFloor, 0, kIdentity>::one) {
+  if (fmt == kE2M1 && mode == kFloor && !had) return pick_pro<K, kE2M1, kFloor, 0>(pro);
+  if (fmt == kE2M3 && mode == kFloor && !had) return pick_pro<K, kE2M3, kFloor, 0>(pro);
+  if (fmt == kE2M3 && mode == kFloor && had) return pick_pro<K, kE2M3, kFloor, 1>(pro);
+  if (fmt == kE4M3 && mode == kRceil && !had) return pick_pro<K, kE4M3, kRceil, 0>(pro);
+  if (fmt == kE4M3 && mode == kFloor && !had) return pick_pro<K, kE4M3, kFloor, 0>(pro);
   return nullptr;
 }
 
 }  // namespace
 
-bool pack_supported(int fmt, int mode, int had, int pro) { return pick(fmt, mode, had, pro) != nullptr; }
+bool pack_supported(int fmt, int mode, int had, int pro) { return pick<PackKernels>(fmt, mode, had, pro) != nullptr; }
 
 hipError_t launch_pack(const PackParams& p, int fmt, int mode, int had, int pro, int64_t batch,
                        hipStream_t stream) {
-  PackFn fn = pick(fmt, mode, had, pro);
+  PackFn fn = pick<PackKernels>(fmt, mode, had, pro);
   if (!fn) return hipErrorInvalidValue;
   dim3 grid((unsigned)((p.C + kTileC - 1) / kTileC), (unsigned)((p.R + kTileR - 1) / kTileR), (unsigned)batch);
   hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_many(const PackMany& m, int fmt, int mode, int had, int pro, hipStream_t stream) {
+  PackManyFn fn = pick<ManyAsOne>(fmt, mode, had, pro);
+  if (!fn || m.n < 1 || m.n > kPackManyMax) return hipErrorInvalidValue;
+  const int64_t tiles = m.first[m.n];
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 

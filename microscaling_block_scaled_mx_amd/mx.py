@@ -64,6 +64,14 @@ class GroupedArgs(ctypes.Structure):
                 ("aux", ctypes.c_void_p), ("out_row", Packed), ("out_col", Packed)]
 
 
+class QuantizeItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("aux", ctypes.c_void_p), ("batch", ctypes.c_int64),
+                ("R", ctypes.c_int64), ("C", ctypes.c_int64), ("row", Packed), ("col", Packed),
+                ("colsum_partials", ctypes.c_void_p), ("colsum", ctypes.c_void_p)]
+
+
+QUANTIZE_MANY_MAX = 8
+
 _lib = None
 
 
@@ -78,6 +86,8 @@ def lib():
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.mx_quantize.restype = ci
         L.mx_quantize.argtypes = [vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.mx_quantize_many.restype = ci
+        L.mx_quantize_many.argtypes = [ctypes.POINTER(QuantizeItem), ci, ci, ci, ci, ci, vp]
         L.mx_gemm.restype = ci
         L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_fused_mlp_fwd.restype = ci
@@ -178,6 +188,30 @@ def quantize(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = Fals
                            _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
                            _ptr(colsum_partials), _ptr(colsum), _stream(stream))
     _check(st, "mx_quantize")
+
+
+def quantize_many(items, fmt, scale_mode, hadamard=False, prologue=PRO_IDENTITY, stream=None):
+    """mx_quantize_many: each item is a dict with the mx_quantize arguments
+    x, R, C and optionally aux, batch (1), row=(codes, scales),
+    col=(codes, scales), colsum_partials, colsum -- all packed in one launch."""
+    n = len(items)
+    arr = (QuantizeItem * max(n, 1))()
+    for i, it in enumerate(items):
+        R, C, batch = it["R"], it["C"], it.get("batch", 1)
+        pro = prologue
+        in_cols = 2 * C if pro == PRO_SWIGLU else (C // 2 if pro == PRO_DSWIGLU else C)
+        what = f"quantize_many item {i}"
+        _need(it["x"], 2 * batch * R * in_cols, what + " input")
+        if pro in (PRO_DGELU_TANH, PRO_DSWIGLU):
+            _need(it.get("aux"), 2 * batch * R * C, what + " aux")
+        _need_packed(it.get("row"), R, C, fmt, what + " row", batch)
+        _need_packed(it.get("col"), C, R, fmt, what + " col", batch)
+        _need(it.get("colsum_partials"), 4 * batch * (R // 32) * C, what + " colsum partials")
+        _need(it.get("colsum"), 4 * batch * C, what + " colsum")
+        arr[i] = QuantizeItem(_ptr(it["x"]), _ptr(it.get("aux")), batch, R, C, _packed(it.get("row")),
+                              _packed(it.get("col")), _ptr(it.get("colsum_partials")), _ptr(it.get("colsum")))
+    st = lib().mx_quantize_many(arr, n, fmt, scale_mode, int(hadamard), prologue, _stream(stream))
+    _check(st, "mx_quantize_many")
 
 
 def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16, c_dtype: int = BF16,

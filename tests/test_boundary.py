@@ -90,6 +90,39 @@ def test_quantize_valid_args_need_the_device():
             assert st == DEVICE
 
 
+
+def qmany(items, n=None, fmt=mx.E2M1, mode=mx.FLOOR, had=0, pro=mx.PRO_IDENTITY):
+    arr = (mx.QuantizeItem * max(len(items), 1))()
+    for k, it in enumerate(items):
+        a = dict(x=P, aux=None, batch=1, R=64, C=128, row=(P2, P3), col=(P4, P5), part=None, sum=None)
+        a.update(it)
+        arr[k] = mx.QuantizeItem(a["x"], a["aux"], a["batch"], a["R"], a["C"], mx.Packed(*a["row"]),
+                                 mx.Packed(*a["col"]), a["part"], a["sum"])
+    return mx.lib().mx_quantize_many(arr, len(items) if n is None else n, fmt, mode, had, pro, None)
+
+
+def test_quantize_many_rejections():
+    L = mx.lib()
+    assert L.mx_quantize_many(None, 1, mx.E2M1, mx.FLOOR, 0, 0, None) == NULL
+    assert qmany([{}], n=0) == SHAPE
+    assert qmany([{}] * 9) == SHAPE  # more than MX_QUANTIZE_MANY_MAX
+    # each item is validated as mx_quantize validates its arguments
+    assert qmany([{}, dict(R=48)]) == SHAPE
+    assert qmany([{}, dict(x=None)]) == NULL
+    assert qmany([dict(row=(P2, None))]) == NULL
+    assert qmany([{}, dict(x=P + 8)]) == ALIGN
+    assert qmany([{}], fmt=mx.E2M1, had=1) == FORMAT
+    assert qmany([{}], pro=mx.PRO_DGELU_TANH) == NULL  # aux required
+
+
+def test_quantize_many_valid_args_need_the_device():
+    for items, kw in (([{}], {}), ([{}, dict(R=160, C=96), dict(R=0)], dict(fmt=mx.E2M3, had=1)),
+                      ([dict(batch=8)] * 8, dict(fmt=mx.E4M3, mode=mx.RCEIL))):
+        st = qmany(items, **kw)
+        assert st in (OK, DEVICE)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
 def g(**kw):
     a = dict(ac=P, as_=P2, bc=P3, bs=P4, M=256, N=512, K=768, fmt=mx.E2M3, bias=None, bt=mx.BF16, c=P5,
              ct=mx.BF16, ldc=512)

@@ -155,6 +155,42 @@ def test_quantize_batched(mxl, orc):
             assert np.array_equal(got[k][b], want[k]), (b, k)
 
 
+@pytest.mark.parametrize("fmt,mode,had,pro", [(1, 0, False, 0), (2, 0, True, 0), (3, 1, False, 0), (2, 0, True, 1)])
+def test_quantize_many_matches_quantize_and_oracle(mxl, orc, fmt, mode, had, pro):
+    # three tensors of different shapes (one ragged against the 128 x 128
+    # tile, one batched) in one launch: every byte equals what separate
+    # mx_quantize calls write, and the ragged one matches the oracle
+    rng = np.random.default_rng(300 + 10 * fmt + pro)
+    items = [(256, 384, 1), (160, 96, 1), (128, 256, 2)]
+    xs = [with_specials(I.bf16_normal(rng, (R, C), 2.0), rng) if b == 1 else I.bf16_normal(rng, (b, R, C), 2.0)
+          for R, C, b in items]
+    bits = mxl.BITS[fmt]
+
+    def bufs(R, C, b):
+        bb = None if b == 1 else b
+        return [torch.full(tiled_shape(R, C, bits, bb), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(blocked_shape(R, C, bb), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(tiled_shape(C, R, bits, bb), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(blocked_shape(C, R, bb), 0xA5, dtype=torch.uint8, device="cuda")]
+
+    many = [bufs(*it) for it in items]
+    one = [bufs(*it) for it in items]
+    xd = [dev(x) for x in xs]
+    mxl.quantize_many([dict(x=xd[i], R=R, C=C, batch=b, row=(many[i][0], many[i][1]), col=(many[i][2], many[i][3]))
+                       for i, (R, C, b) in enumerate(items)], fmt, mode, had, pro)
+    for i, (R, C, b) in enumerate(items):
+        mxl.quantize(xd[i], R, C, fmt, mode, had, pro, row=(one[i][0], one[i][1]), col=(one[i][2], one[i][3]),
+                     batch=b)
+    for i in range(len(items)):
+        for k in range(4):
+            assert torch.equal(many[i][k], one[i][k]), (items[i], k)
+    R, C, _ = items[1]
+    want = orc.quantize(xs[1], R, C, fmt, mode, had, pro=pro, row=True, col=True)
+    got = {"row_codes": untiled(host(many[1][0]), C, bits), "row_scales": unblocked(host(many[1][1]), C // 32),
+           "col_codes": untiled(host(many[1][2]), R, bits), "col_scales": unblocked(host(many[1][3]), R // 32)}
+    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+
+
 def test_quantize_zero_size_is_a_noop(mxl):
     x = torch.zeros(1, dtype=torch.int16, device="cuda")
     rc = torch.full((4,), 7, dtype=torch.uint8, device="cuda")
