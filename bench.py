@@ -18,8 +18,8 @@ MXFP6 MLP at M=8192 (3072 -> 12288 -> 3072), the MXFP4 sweep over the five
 Flux-12B block linears at M=16384 and the MXFP8 grouped SwiGLU MLP
 (G=8, D=2048, F=768, R=32768).
 
-The timed steps replay one captured HIP graph per input copy (--no-graph:
-eager launches), on one stream (--two-streams: dgrad and wgrad beside fwd
+The timed steps replay a captured HIP graph of four consecutive steps (one
+per input copy; --no-graph: eager launches), on one stream (--two-streams: dgrad and wgrad beside fwd
 -- measured slower).  One launch (mx_quantize_many) packs X, W and dY.
 Per-launch
 device durations come from HIP events around replays of a graph of ten
@@ -164,13 +164,15 @@ def time_steps(fn, steps, warmup, T):
     return dt / steps
 
 
-def capture_steps(step, copies, concurrent=True):
-    """One HIP graph per input copy, each holding one whole step (the four
-    launches; with `concurrent`, the two-stream schedule of LinearStep.run,
-    captured as parallel branches), so that the timed loop replays launches
-    without host work in between.  The captured calls are the same C-ABI
-    entry points, enqueued on torch's capture stream (and a side stream
-    forked from it)."""
+def capture_steps(step, copies, concurrent=False):
+    """HIP graphs of whole steps, so that the timed loop replays launches
+    without host work in between: graphs[0] holds `copies` consecutive steps
+    (input copies 0 .. copies-1, so one replay launches once for that many
+    steps), graphs[1 + c] one step on input copy c (for step counts that are
+    not a multiple of `copies`).  With `concurrent`, each step uses the
+    two-stream schedule of LinearStep.run, captured as parallel branches.
+    The captured calls are the same C-ABI entry points, enqueued on torch's
+    capture stream (and a side stream forked from it)."""
     import torch
     T = Timer()
     warm = torch.cuda.Stream()
@@ -182,13 +184,31 @@ def capture_steps(step, copies, concurrent=True):
     torch.cuda.current_stream().wait_stream(warm)
     torch.cuda.synchronize()
     graphs = []
-    for c in range(copies):
+    for group in [list(range(copies))] + [[c] for c in range(copies)]:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step.run(c, T, side)
+            for c in group:
+                step.run(c, T, side)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
+
+
+def time_graph_steps(graphs, copies, steps, warmup):
+    """Wall time per step of exactly `steps` steps (whole `copies`-step
+    graphs, then single-step graphs for the remainder), between two device
+    synchronizations, after `warmup` single steps."""
+    import torch
+    for i in range(warmup):
+        graphs[1 + i % copies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // copies):
+        graphs[0].replay()
+    for i in range(steps % copies):
+        graphs[1 + i].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
 
 
 def graph_time(launch, reps=10, replays=4, warm=None):
@@ -217,20 +237,6 @@ def graph_time(launch, reps=10, replays=4, warm=None):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (reps * replays)
-
-
-def time_graph_steps(graphs, steps, warmup):
-    """Wall time per step of `steps` replays (rotating input copies), between
-    two device synchronizations."""
-    import torch
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[(warmup + i) % len(graphs)].replay()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
 
 
 def kernel_times(step):
@@ -450,7 +456,7 @@ def main():
         sec = time_steps(lambda i: step.run(i, T), args.steps, args.warmup, Timer())
     else:
         graphs = capture_steps(step, len(step.inp), concurrent=args.two_streams)
-        sec = time_graph_steps(graphs, args.steps, args.warmup)
+        sec = time_graph_steps(graphs, len(step.inp), args.steps, args.warmup)
     # per-launch device durations (graphs of repeated launches, after the
     # timed steps)
     k = kernel_times(step)
@@ -468,7 +474,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp6 (e2m3 x e2m3, fp32 accumulate)", "data": "synthetic",
-        "launch": "eager" if args.no_graph else ("hip_graph (one captured step per input copy, "
+        "launch": "eager" if args.no_graph else ("hip_graph (4 consecutive steps per graph, "
                                                  + ("two streams)" if args.two_streams else "one stream)")),
         "config": {"workload": "MXFP6 linear (E2M3, FLOOR, Hadamard-32) X[4096,3072] W[3072,3072]: dual packs "
                                "of X, W, dY + fwd, dgrad, wgrad GEMMs, bf16 out",

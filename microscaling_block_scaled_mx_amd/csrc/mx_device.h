@@ -124,20 +124,31 @@ __device__ __forceinline__ void hadamard32(float (&y)[32]) {
 template <int FMT, int MODE>
 __device__ __forceinline__ uint32_t quant_block(const float (&v)[32], uint32_t (&w)[FmtTraits<FMT>::kBits]) {
   [[maybe_unused]] constexpr int B = FmtTraits<FMT>::kBits;
-  uint32_t amax = 0u;
+  // amax of |v| on the bit patterns: positive values (and +NaN / +Inf)
+  // order as signed integers, negative ones as unsigned integers above
+  // every positive one, so the signed maximum (from 0) finds the largest
+  // positive pattern and the unsigned maximum, sign cleared, the largest
+  // negative one (or the same positive one if there is none)
+  int32_t mpos = 0;
+  uint32_t mneg = 0u;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
-    amax = amax > b ? amax : b;
+    const uint32_t b = __float_as_uint(v[i]);
+    mpos = mpos > (int32_t)b ? mpos : (int32_t)b;
+    mneg = mneg > b ? mneg : b;
   }
+  const uint32_t amax = (uint32_t)mpos > (mneg & 0x7fffffffu) ? (uint32_t)mpos : (mneg & 0x7fffffffu);
   const uint32_t s = scale_byte<FMT, MODE>(amax);
 #if defined(__HIP_DEVICE_COMPILE__)
   const bool tiny = s == 0u;
-  const float pre = tiny ? 0x1p64f : 1.0f;
   const float sc = __uint_as_float((tiny ? 64u : (s == 0xffu ? 127u : s)) << 23);  // 2^X (2^-63 if tiny)
   float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = v[i] * pre;
+  for (int i = 0; i < 32; ++i) x[i] = v[i];
+  if (__builtin_amdgcn_ballot_w64(tiny) != 0) {  // rare: only a wavefront holding a tiny block pays
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = tiny ? v[i] * 0x1p64f : v[i];
+  }
   if constexpr (FMT == kE4M3 && MODE == kFloor) {
     const float bound = 448.0f * sc;
 #pragma unroll
