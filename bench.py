@@ -44,18 +44,25 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a plain copy
 # (profiles/mxfp6_gemm_pack_hbm_traffic.md); valid only for the GEMM sources
 # they were taken with
-GEMM_TRAFFIC = {"bytes_per_launch": 79.0e6, "sources_sha1": "36972c0dfe31d95f38bbc21d1cd97ff28dc20f99"}
-GEMM_SOURCES = ("mx_gemm.hip", "mx_device.h", "mx_kernels.h")
+# HBM traffic per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+# (scaled by what they read for a plain copy), valid while the kernel
+# sources are those the counters were taken with
+GEMM_TRAFFIC = {"bytes_per_launch": 79.0e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
+                "sources_sha1": "a3757de7c953527a58cd7e84942787d90e167d52"}
+PACK_TRAFFIC = {"bytes_per_launch": 123.6e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
+                "sources_sha1": "9de046d67417af520ee3265b4f5672279cf3178b"}
 
 
-def gemm_traffic():
-    """The measured traffic if the GEMM sources are unchanged since, else None."""
+def measured_traffic(rec):
+    """rec's traffic if its kernel sources are unchanged since, else None."""
     import hashlib
     h = hashlib.sha1()
-    for f in GEMM_SOURCES:
+    for f in rec["sources"]:
         with open(os.path.join(ROOT, "microscaling_block_scaled_mx_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    return GEMM_TRAFFIC["bytes_per_launch"] if h.hexdigest() == GEMM_TRAFFIC["sources_sha1"] else None
+    return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha1"] else None
+
+
 PEAK_TFLOPS = {"fp4": 10100.0, "fp6": 10100.0, "fp8": 5000.0}  # MI355X dense MFMA
 HBM_GBS = 8000.0
 # algorithmic bytes per element of a pack: 2 B bf16 in + (bits/8 + 1/32) per output axis
@@ -385,8 +392,9 @@ def bench_cfg5(mx, T, iters=5):
 
 
 def only(mx, spec, steps, warmup, T):
-    """One kernel configuration, for profilers: gemm:FMT:M:N:K or pack:FMT:R:C
-    (dual pack).  Prints one JSON line with its average time."""
+    """One kernel configuration, for profilers: gemm:FMT:M:N:K, pack:FMT:R:C
+    (dual pack), packs:FMT:M:N:K (the linear step's fused dual packs of X,
+    W and dY) or copy:BYTES.  Prints one JSON line with its average time."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     kind, fbits, *dims = spec.split(":")
@@ -409,6 +417,16 @@ def only(mx, spec, steps, warmup, T):
         C = torch.empty((M, N), dtype=torch.int16, device="cuda")
         us = graph_time(lambda r: mx.gemm(pa, pb, M, N, K, fmt, C), reps=steps)
         print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
+    elif kind == "packs":  # the linear step's fused pack: X [M,K], W [N,K], dY [M,N] in one launch
+        M, N, K = (int(v) for v in dims)
+        rng = np.random.default_rng(7)
+        shapes = ((M, K), (N, K), (M, N))
+        xs = [dev(I.bf16_normal(rng, sh)) for sh in shapes]
+        items = [dict(x=x, R=r, C=c, row=mx.alloc_packed(r, c, fmt), col=mx.alloc_packed(c, r, fmt))
+                 for x, (r, c) in zip(xs, shapes)]
+        us = graph_time(lambda r: mx.quantize_many(items, fmt, mode, had), reps=steps)
+        b = sum(r * c for r, c in shapes) * (2 + 2 * PACK_OUT[int(fbits)])
+        print(json.dumps({"only": spec, "us": us, "gbs": b / (us * 1e-6) / 1e9}), flush=True)
     else:
         R, C = (int(v) for v in dims)
         X = dev(I.bf16_normal(np.random.default_rng(7), (R, C)))
@@ -430,8 +448,8 @@ def main():
     ap.add_argument("--two-streams", action="store_true",
                     help="capture the step on two streams (independent launches overlapping) instead of one")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C (FMT = 4, 6 or 8) "
-                         "or copy:BYTES (a plain device copy)")
+                    help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C, packs:FMT:M:N:K "
+                         "(FMT = 4, 6 or 8) or copy:BYTES (a plain device copy)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
@@ -481,11 +499,12 @@ def main():
                    "M": M, "N": N, "K": K, "format": "mxfp6", "gemm_flops_per_step": step.flops()},
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel<E2M3> (fwd/dgrad/wgrad launches, 77.3 GFLOP each)",
                      "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp6"], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": gemm_traffic(),
+                     "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": measured_traffic(GEMM_TRAFFIC),
                      "traffic_unit": "bytes per launch (HBM read + write)"},
         "quantizer": {"kernel": "pack_many_kernel<E2M3, Hadamard>: dual packs of X, W and dY in one launch",
                       "achieved_gbs": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
-                      "frac": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9 / HBM_GBS, 4)},
+                      "frac": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9 / HBM_GBS, 4),
+                      "algorithmic_bytes": pack_bytes, "traffic": measured_traffic(PACK_TRAFFIC)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
