@@ -89,13 +89,22 @@ struct Cfg {
   static constexpr int kARem = (BM * kChunks) % kThreads;  // slots of a partial last load (0: none)
   static constexpr int kBRem = (BN * kChunks) % kThreads;
   static_assert(kARem % 64 == 0 && kBRem % 64 == 0, "partial loads cover whole wavefronts");
-  static constexpr int kAOff = 0;
-  static constexpr int kBOff = BM * kRowBytes;
-  static constexpr int kSOff = kBOff + BN * kRowBytes;   // scale dwords: [dword][A rows, then B rows] (512 slots)
-  static constexpr int kJOff = kSOff + kScaleDw * 512 * 4;
-  static constexpr int kStage = kJOff + ((kARem || kBRem) ? 1024 : 0);
-  static constexpr int kStages = (4 * kStage <= 160 * 1024) ? 4 : 3;
-  static_assert(kStages * kStage <= 160 * 1024, "three stages fit the LDS");
+  // The ring of kStages stage buffers is laid out region by region: the A
+  // rows of buffers 0 .. S-1, then their B rows, then their scale dwords
+  // ([A rows, then B rows], 512 slots), then a junk area for idle load
+  // slots.  Every read of one operand from any buffer is then within the
+  // 16-bit offset of a ds_read from one per-lane base.
+  static constexpr int kARegion = BM * kRowBytes;
+  static constexpr int kBRegion = BN * kRowBytes;
+  static constexpr int kSRegion = kScaleDw * 512 * 4;
+  static constexpr int kJunk = (kARem || kBRem) ? 1024 : 0;
+  static constexpr int kStage = kARegion + kBRegion + kSRegion;  // bytes per stage
+  static constexpr int kStages = (4 * kStage + kJunk <= 160 * 1024) ? 4 : 3;
+  static_assert(kStages * kStage + kJunk <= 160 * 1024, "three stages fit the LDS");
+  static constexpr int aoff(int b) { return b * kARegion; }
+  static constexpr int boff(int b) { return kStages * kARegion + b * kBRegion; }
+  static constexpr int soff(int b) { return kStages * (kARegion + kBRegion) + b * kSRegion; }
+  static constexpr int kJOff = kStages * kStage;
   static constexpr int kWM = BM / 2, kWN = BN / 2;
   static constexpr int kMI = kWM / 32, kNJ = kWN / 32;
   static constexpr int kLoads = kAIters + kBIters + 2 * kScaleDw;  // vector-memory instructions per stage per wave
@@ -107,7 +116,7 @@ struct Cfg {
   static constexpr int kEpiBytes = EPI == kEpiSwiglu    ? BM * kZPitch
                                    : EPI == kEpiDSwiglu ? 2 * BM * kDPitch
                                                         : 4 * kWM * kCPitch;
-  static constexpr int kSmem = (kStages * kStage > kEpiBytes) ? kStages * kStage : kEpiBytes;
+  static constexpr int kSmem = (kJOff + kJunk > kEpiBytes) ? kJOff + kJunk : kEpiBytes;
   static_assert(kSmem <= 163840, "LDS budget");
 };
 
@@ -177,6 +186,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+#endif
+}
+// The same from a wavefront-uniform base (scalar registers) plus a per-lane
+// 32-bit byte offset, so that the per-lane part stays fixed across stages.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 #endif
 }
 __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
@@ -361,22 +377,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #define MX_PIECE(k, buf, q)                                                                               \
   do {                                                                                                   \
     const int64_t k0_ = kbeg + (int64_t)(k) * BK;                                                        \
-    const uint32_t st_ = smem_lds + (buf) * CF::kStage;                                                  \
+    const uint32_t st_ = smem_lds;                                                                       \
     if ((q) < CF::kAIters) {                                                                             \
       const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
       const bool junk_ = CF::kARem && i_ == CF::kAIters - 1 && wave_u * 64 >= CF::kARem;                 \
-      lds_dma16(p.a_codes + (k0_ / 128) * a_rows * kGB + (k0_ % 128) * kBits / 8 + a_off[i_],            \
-                st_ + (junk_ ? CF::kJOff : CF::kAOff + (i_ * 256 + wave_u * 64) * 16));                  \
+      lds_dma16_s(p.a_codes + (k0_ / 128) * a_rows * kGB + (k0_ % 128) * kBits / 8, a_off[i_],          \
+                  st_ + (junk_ ? CF::kJOff : CF::aoff(buf) + (i_ * 256 + wave_u * 64) * 16));            \
     } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
       const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
       const bool junk_ = CF::kBRem && i_ == CF::kBIters - 1 && wave_u * 64 >= CF::kBRem;                 \
-      lds_dma16(p.b_codes + (k0_ / 128) * b_rows * kGB + (k0_ % 128) * kBits / 8 + b_off[i_],            \
-                st_ + (junk_ ? CF::kJOff : CF::kBOff + (i_ * 256 + wave_u * 64) * 16));                  \
+      lds_dma16_s(p.b_codes + (k0_ / 128) * b_rows * kGB + (k0_ % 128) * kBits / 8, b_off[i_],          \
+                  st_ + (junk_ ? CF::kJOff : CF::boff(buf) + (i_ * 256 + wave_u * 64) * 16));            \
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
       const int d_ = e_ / 2, j_ = e_ % 2;                                                                \
       lds_dma4(s_src[j_] + (k0_ / 128 + d_) * s_step[j_],                                               \
-               st_ + CF::kSOff + (d_ * 512 + j_ * 256 + wave_u * 64) * 4);                              \
+               st_ + CF::soff(buf) + (d_ * 512 + j_ * 256 + wave_u * 64) * 4);                          \
     }                                                                                                    \
   } while (0)
 #define MX_ISSUE(k, buf)                                                                                  \
@@ -456,27 +472,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   uint32_t sca[CF::kMI], scb[CF::kNJ];  // this stage's scale dwords, shifted so byte 0 is its block g
   uint32_t nsa[CF::kMI], nsb[CF::kNJ];  // the next stage's scale dwords as stored
 
-  auto read_scales = [&](const uint8_t* sbuf) __attribute__((always_inline)) {
+  // scale dwords and operand fragments of ring buffer b (a constant)
+  auto read_scales = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CF::kMI; ++i) nsa[i] = *reinterpret_cast<const uint32_t*>(sbuf + CF::kSOff + arow[i] * 4);
+    for (int i = 0; i < CF::kMI; ++i) nsa[i] = *reinterpret_cast<const uint32_t*>(smem + CF::soff(b) + arow[i] * 4);
 #pragma unroll
-    for (int j = 0; j < CF::kNJ; ++j) nsb[j] = *reinterpret_cast<const uint32_t*>(sbuf + CF::kSOff + (BM + brow[j]) * 4);
+    for (int j = 0; j < CF::kNJ; ++j)
+      nsb[j] = *reinterpret_cast<const uint32_t*>(smem + CF::soff(b) + (BM + brow[j]) * 4);
   };
   // fragment v of a step (v = 0: A0, 1 .. NJ: B0 .. B(NJ-1), then A1 ..)
-  auto read_frag = [&](int buf, int v, const uint8_t* sbuf, int ks) __attribute__((always_inline)) {
+  auto read_frag = [&](int reg, int v, int b, int ks) __attribute__((always_inline)) {
     if (v == 0 || v > CF::kNJ) {
       const int i = v == 0 ? 0 : v - CF::kNJ;
-      af[i] = lds_operand<FMT, CF::kChunks>(sbuf + CF::kAOff + arow[i] * CF::kRowBytes, arow[i], ks, g);
+      af[i] = lds_operand<FMT, CF::kChunks>(smem + CF::aoff(b) + arow[i] * CF::kRowBytes, arow[i], ks, g);
     } else {
       const int j = v - 1;
-      bf[kBDouble ? buf : 0][j] =
-          lds_operand<FMT, CF::kChunks>(sbuf + CF::kBOff + brow[j] * CF::kRowBytes, brow[j], ks, g);
+      bf[kBDouble ? reg : 0][j] =
+          lds_operand<FMT, CF::kChunks>(smem + CF::boff(b) + brow[j] * CF::kRowBytes, brow[j], ks, g);
     }
   };
 
-  // one step: stage it, K step ks of the stage
-  auto step = [&](int it, auto ksc) __attribute__((always_inline)) {
-    constexpr int ks = decltype(ksc)::value;
+  // one step: stage it (in ring buffer B = it % S, a constant), K step ks
+  auto step = [&](int it, auto ksc, auto bc) __attribute__((always_inline)) {
+    constexpr int ks = decltype(ksc)::value, B = decltype(bc)::value;
     constexpr int cur = kBDouble ? ks : 0;  // B fragment buffer of this step
     constexpr int sel = 2 * ks;             // byte of the shifted scale dwords: block 2 ks + g of the stage
     constexpr bool last = ks == KS - 1;
@@ -485,12 +503,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       wait_lgkmcnt0();  // every read of buffer it % S done before the barrier frees it
       stage_barrier();
     }
-    const uint8_t* rbuf = smem + ((last ? it + 1 : it) % S) * CF::kStage;  // the next step's stage
+    constexpr int rbuf = last ? (B + 1) % S : B;  // the next step's stage buffer
     constexpr int rks = last ? 0 : ks + 1;
     const int lst = last ? it + S : it + S - 1;  // stage whose loads this step issues
     constexpr int w = last ? 0 : ks + 1;         // ... and its window step
     const int lk = lst < nk ? lst : nk - 1;      // its K range (the last stage's past the end)
-    const int lbuf = lst % S;
+    constexpr int lbuf = last ? B : (B + S - 1) % S;
     constexpr int U = CF::kMI + CF::kNJ + (last ? 1 : 0);  // read units: [scales,] fragments
 #pragma unroll
     for (int f = 0; f < kMf; ++f) {
@@ -510,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       sched_fence();
     }
   };
-  auto stage = [&](int it) __attribute__((always_inline)) {
+  auto stage = [&](int it, auto bc) __attribute__((always_inline)) {
     // K block of byte 0: g, or 2 (it & 1) + g for 64-element stages (a
     // dword holds the four blocks of one 128-element group)
     const int sh = 8 * g + (KS == 1 ? 16 * (it & 1) : 0);
@@ -518,8 +536,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     for (int i = 0; i < CF::kMI; ++i) sca[i] = nsa[i] >> sh;
 #pragma unroll
     for (int j = 0; j < CF::kNJ; ++j) scb[j] = nsb[j] >> sh;
-    step(it, std::integral_constant<int, 0>{});
-    if constexpr (KS == 2) step(it, std::integral_constant<int, 1>{});
+    step(it, std::integral_constant<int, 0>{}, bc);
+    if constexpr (KS == 2) step(it, std::integral_constant<int, 1>{}, bc);
   };
 
   pin_arg(p.c);
@@ -547,10 +565,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     for (int q = 0; q < kPart0; ++q) MX_PIECE(S - 1 < nk ? S - 1 : nk - 1, S - 1, q);
     wait_vmcnt<CF::kLoads * (S - 2) + kPart0>();
     stage_barrier();
-    read_scales(smem);
+    read_scales(0);
 #pragma unroll
-    for (int v = 0; v < CF::kMI + CF::kNJ; ++v) read_frag(0, v, smem, 0);
-    for (int it = 0; it < nk; ++it) stage(it);
+    for (int v = 0; v < CF::kMI + CF::kNJ; ++v) read_frag(0, v, 0, 0);
+    // unrolled by S so that every stage's ring buffer is a constant
+    for (int it0 = 0; it0 < nk; it0 += S) {
+      stage(it0, std::integral_constant<int, 0>{});
+      if (it0 + 1 < nk) stage(it0 + 1, std::integral_constant<int, 1>{});
+      if (it0 + 2 < nk) stage(it0 + 2, std::integral_constant<int, 2>{});
+      if constexpr (S > 3) {
+        if (it0 + 3 < nk) stage(it0 + 3, std::integral_constant<int, 3 % S>{});
+      }
+    }
     wait_vmcnt<0>();  // the loads past the last stage, before the LDS is reused
   }
 #undef MX_PIECE
