@@ -19,8 +19,8 @@ Flux-12B block linears at M=16384 and the MXFP8 grouped SwiGLU MLP
 (G=8, D=2048, F=768, R=32768).
 
 The timed steps replay a captured HIP graph of four consecutive steps (one
-per input copy; --no-graph: eager launches), on one stream (--two-streams: dgrad and wgrad beside fwd
--- measured slower).  One launch (mx_quantize_many) packs X, W and dY.
+per input copy; --no-graph: eager launches).  A step is two launches:
+mx_quantize_many packs X, W and dY, mx_gemm_many computes the three GEMMs.
 Per-launch
 device durations come from HIP events around replays of a graph of ten
 back-to-back copies of each launch.
@@ -121,36 +121,23 @@ class LinearStep:
         self.Y, self.dX, self.dW = e16(M, N), e16(M, K), e16(N, K)
 
     def calls(self, i):
-        """The four launches of one step: (name, fn, args, kwargs)."""
+        """The two launches of one step: name -> (fn, args, kwargs)."""
         mx, M, N, K, f, m, h = self.mx, self.M, self.N, self.K, self.fmt, self.mode, self.had
         X, W, dY = self.inp[i % len(self.inp)]
         items = [dict(x=X, R=M, C=K, row=self.Xr, col=self.Xc), dict(x=W, R=N, C=K, row=self.Wr, col=self.Wc),
                  dict(x=dY, R=M, C=N, row=self.dYr, col=self.dYc)]
+        gemms = [dict(a=self.Xr, b=self.Wr, M=M, N=N, K=K, c=self.Y),      # forward
+                 dict(a=self.dYr, b=self.Wc, M=M, N=K, K=N, c=self.dX),    # data gradient
+                 dict(a=self.dYc, b=self.Xc, M=N, N=K, K=M, c=self.dW)]    # weight gradient (K = tokens)
         return {"pack_XWdY": (mx.quantize_many, (items, f, m, h), {}),
-                "gemm_fwd": (mx.gemm, (self.Xr, self.Wr, M, N, K, f, self.Y), {}),
-                "gemm_dgrad": (mx.gemm, (self.dYr, self.Wc, M, K, N, f, self.dX), {}),
-                "gemm_wgrad": (mx.gemm, (self.dYc, self.Xc, N, K, M, f, self.dW), {})}
+                "gemm_fwd_dgrad_wgrad": (mx.gemm_many, (gemms, f), {})}
 
-    def run(self, i, T, side=None):
-        """One step: one launch packs X, W and dY (row + column each), then
-        the three GEMMs.  With a side stream, dgrad and wgrad run on it
-        beside fwd; the caller's stream waits for the side stream at the
-        end."""
-        import torch
-        c = self.calls(i)
-        go = lambda n: T.run(n, c[n][0], *c[n][1], **c[n][2])
-        if side is None:
-            for n in ("pack_XWdY", "gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
-                go(n)
-            return
-        main = torch.cuda.current_stream()
-        go("pack_XWdY")
-        side.wait_stream(main)
-        go("gemm_fwd")
-        with torch.cuda.stream(side):
-            go("gemm_dgrad")
-            go("gemm_wgrad")
-        main.wait_stream(side)
+    def run(self, i, T):
+        """One step: one launch packs X, W and dY (row + column each), one
+        launch computes the forward, data-gradient and weight-gradient
+        GEMMs."""
+        for n, (fn, a, kw) in self.calls(i).items():
+            T.run(n, fn, *a, **kw)
 
     def flops(self):
         return 3 * 2.0 * self.M * self.N * self.K
@@ -171,23 +158,20 @@ def time_steps(fn, steps, warmup, T):
     return dt / steps
 
 
-def capture_steps(step, copies, concurrent=False):
+def capture_steps(step, copies):
     """HIP graphs of whole steps, so that the timed loop replays launches
     without host work in between: graphs[0] holds `copies` consecutive steps
     (input copies 0 .. copies-1, so one replay launches once for that many
     steps), graphs[1 + c] one step on input copy c (for step counts that are
-    not a multiple of `copies`).  With `concurrent`, each step uses the
-    two-stream schedule of LinearStep.run, captured as parallel branches.
-    The captured calls are the same C-ABI entry points, enqueued on torch's
-    capture stream (and a side stream forked from it)."""
+    not a multiple of `copies`).  The captured calls are the same C-ABI
+    entry points, enqueued on torch's capture stream."""
     import torch
     T = Timer()
     warm = torch.cuda.Stream()
-    side = torch.cuda.Stream() if concurrent else None
     warm.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(warm):
         for c in range(copies):
-            step.run(c, T, side)
+            step.run(c, T)
     torch.cuda.current_stream().wait_stream(warm)
     torch.cuda.synchronize()
     graphs = []
@@ -195,7 +179,7 @@ def capture_steps(step, copies, concurrent=False):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for c in group:
-                step.run(c, T, side)
+                step.run(c, T)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
@@ -336,15 +320,15 @@ def bench_cfg4(mx, T, iters=3):
     tot_fl = tot_gemm_us = tot_us = 0.0
     for i, (name, K, N) in enumerate(I.FLUX_LINEARS):
         st = LinearStep(mx, 16384, N, K, mx.E2M1, mx.FLOOR, False, 401 + i, copies=1)
-        sec = time_steps(lambda j: st.run(j, T), iters, 1, T)
-        k = T.summary()
-        g = k["gemm_fwd"] + k["gemm_dgrad"] + k["gemm_wgrad"]
+        k = kernel_times(st)  # device time of the step's two launches
+        g = k["gemm_fwd_dgrad_wgrad"]
+        step_us = g + k["pack_XWdY"]
         fl = st.flops()
-        out["linears"][name] = {"K": K, "N": N, "gemm_us": g, "step_us": sec * 1e6,
+        out["linears"][name] = {"K": K, "N": N, "gemm_us": g, "step_us": step_us,
                                 "gemm_tflops": fl / (g * 1e-6) / 1e12}
         tot_fl += fl
         tot_gemm_us += g
-        tot_us += sec * 1e6
+        tot_us += step_us
         del st
         torch.cuda.empty_cache()
     out["gemm_tflops"] = tot_fl / (tot_gemm_us * 1e-6) / 1e12
@@ -394,7 +378,8 @@ def bench_cfg5(mx, T, iters=5):
 def only(mx, spec, steps, warmup, T):
     """One kernel configuration, for profilers: gemm:FMT:M:N:K, pack:FMT:R:C
     (dual pack), packs:FMT:M:N:K (the linear step's fused dual packs of X,
-    W and dY) or copy:BYTES.  Prints one JSON line with its average time."""
+    W and dY), gemms:FMT:M:N:K (its three GEMMs in one launch; random
+    codes) or copy:BYTES.  Prints one JSON line with its average time."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     kind, fbits, *dims = spec.split(":")
@@ -417,6 +402,17 @@ def only(mx, spec, steps, warmup, T):
         C = torch.empty((M, N), dtype=torch.int16, device="cuda")
         us = graph_time(lambda r: mx.gemm(pa, pb, M, N, K, fmt, C), reps=steps)
         print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
+    elif kind == "gemms":  # the linear step's three GEMMs in one launch (FMT:M:N:K as the step)
+        M, N, K = (int(v) for v in dims)
+        g = torch.Generator(device="cuda").manual_seed(7)
+        P = lambda r, k: tuple(torch.randint(118 if i else 0, 130 if i else 256, t.shape, dtype=torch.uint8,
+                                             device="cuda", generator=g)
+                               for i, t in enumerate(mx.alloc_packed(r, k, fmt)))
+        trio = [(P(M, K), P(N, K), M, N, K), (P(M, N), P(K, N), M, K, N), (P(N, M), P(K, M), N, K, M)]
+        items = [dict(a=a, b=b, M=m, N=n, K=k, c=torch.empty((m, n), dtype=torch.int16, device="cuda"))
+                 for a, b, m, n, k in trio]
+        us = graph_time(lambda r: mx.gemm_many(items, fmt), reps=steps)
+        print(json.dumps({"only": spec, "us": us, "tflops": 3 * 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
     elif kind == "packs":  # the linear step's fused pack: X [M,K], W [N,K], dY [M,N] in one launch
         M, N, K = (int(v) for v in dims)
         rng = np.random.default_rng(7)
@@ -445,10 +441,9 @@ def main():
     ap.add_argument("--extra", choices=["all", "none"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    ap.add_argument("--two-streams", action="store_true",
-                    help="capture the step on two streams (independent launches overlapping) instead of one")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C, packs:FMT:M:N:K "
+                    help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C, packs:FMT:M:N:K, "
+                         "gemms:FMT:M:N:K "
                          "(FMT = 4, 6 or 8) or copy:BYTES (a plain device copy)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -473,31 +468,30 @@ def main():
     if args.no_graph:
         sec = time_steps(lambda i: step.run(i, T), args.steps, args.warmup, Timer())
     else:
-        graphs = capture_steps(step, len(step.inp), concurrent=args.two_streams)
+        graphs = capture_steps(step, len(step.inp))
         sec = time_graph_steps(graphs, len(step.inp), args.steps, args.warmup)
     # per-launch device durations (graphs of repeated launches, after the
     # timed steps)
     k = kernel_times(step)
     value = step.flops() / sec / 1e12
-    gemm_us = float(np.mean([k["gemm_fwd"], k["gemm_dgrad"], k["gemm_wgrad"]]))
-    gemm_flops = 2.0 * M * N * K
+    gemm_us = k["gemm_fwd_dgrad_wgrad"]
+    gemm_flops = step.flops()  # the three GEMMs of the one launch
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
     # algorithmic bytes of the fused pack: X [M,K], W [N,K], dY [M,N], each read once (bf16) and written twice
     pack_bytes = (M * K + N * K + M * N) * (2 + 2 * PACK_OUT[6])
     kernels = {n: {"us": round(v, 2)} for n, v in k.items()}
-    for n in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad"):
-        kernels[n]["tflops"] = round(gemm_flops / (k[n] * 1e-6) / 1e12, 1)
+    kernels["gemm_fwd_dgrad_wgrad"]["tflops"] = round(achieved, 1)
     kernels["pack_XWdY"]["gbs"] = round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp6 (e2m3 x e2m3, fp32 accumulate)", "data": "synthetic",
-        "launch": "eager" if args.no_graph else ("hip_graph (4 consecutive steps per graph, "
-                                                 + ("two streams)" if args.two_streams else "one stream)")),
+        "launch": "eager" if args.no_graph else "hip_graph (4 consecutive steps per graph)",
         "config": {"workload": "MXFP6 linear (E2M3, FLOOR, Hadamard-32) X[4096,3072] W[3072,3072]: dual packs "
                                "of X, W, dY + fwd, dgrad, wgrad GEMMs, bf16 out",
                    "M": M, "N": N, "K": K, "format": "mxfp6", "gemm_flops_per_step": step.flops()},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<E2M3> (fwd/dgrad/wgrad launches, 77.3 GFLOP each)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_many_kernel<E2M3, 256x192 | 192x192> (fwd, dgrad and wgrad "
+                                                "in one launch, 231.9 GFLOP)",
                      "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp6"], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": measured_traffic(GEMM_TRAFFIC),
                      "traffic_unit": "bytes per launch (HBM read + write)"},

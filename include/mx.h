@@ -225,6 +225,40 @@ int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, cons
             int64_t M, int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c,
             int c_dtype, int64_t ldc, void* stream);
 
+/*
+ * mx_gemm_many -- several GEMMs of one format in a single launch, with the
+ * results of n mx_gemm calls made with each item's arguments (each GEMM
+ * takes the tile shape mx_gemm would give it, so the results are bitwise
+ * those of mx_gemm).  For a linear layer's forward, data-gradient and
+ * weight-gradient GEMMs, which are independent once the operands are packed
+ * ([P1] description): one launch lets the compute units that finish one
+ * GEMM's tiles start the next GEMM's instead of idling until every tile of
+ * the launch is done.  Items whose tile shapes are all one shape, or are
+ * 256x192 and 192x192, share one launch; other mixes take one launch per
+ * shape.
+ *
+ *  items        host array of n items; each item's fields have the meaning
+ *               and rules of the mx_gemm arguments of the same names.  No
+ *               item's C may overlap another item's A, B or C.
+ *  n            1 <= n <= MX_GEMM_MANY_MAX.
+ *  fmt          element format of every operand.
+ * Items with M = 0 or N = 0 are skipped.
+ * Errors: MX_ERR_NULL (items NULL), MX_ERR_SHAPE (n out of range), then as
+ * mx_gemm for the first failing item; nothing is enqueued on an error.
+ */
+#define MX_GEMM_MANY_MAX 4
+typedef struct {
+  mx_packed A, B;
+  int64_t M, N, K;
+  const void* bias;
+  int32_t bias_dtype;
+  int32_t c_dtype;
+  void* C;
+  int64_t ldc;
+} mx_gemm_item;
+
+int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream);
+
 /* ---------------------------------------------------------------- fused MLP */
 /*
  * Fused MX MLP, Y = fc2(GELU_tanh(fc1(X) + b1)) ([P1] description and

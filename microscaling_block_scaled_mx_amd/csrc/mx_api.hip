@@ -225,6 +225,39 @@ int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, cons
                      static_cast<hipStream_t>(stream));
 }
 
+int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream) {
+  if (!items) return MX_ERR_NULL;
+  if (n < 1 || n > MX_GEMM_MANY_MAX) return MX_ERR_SHAPE;
+  static_assert(MX_GEMM_MANY_MAX == mx::kGemmManyMax, "item limit");
+  mx::GemmMany m;
+  memset(&m, 0, sizeof m);
+  for (int i = 0; i < n; ++i) {
+    const mx_gemm_item& it = items[i];
+    int st = validate_gemm(it.A.codes, it.A.scales, it.B.codes, it.B.scales, it.M, it.N, it.K, fmt, it.bias,
+                           it.bias_dtype, it.C, it.c_dtype, it.ldc);
+    if (st != MX_OK) return st;
+    if (it.M == 0 || it.N == 0) continue;
+    GemmParams& p = m.p[m.n++];
+    p.a_codes = static_cast<const uint8_t*>(it.A.codes);
+    p.a_scales = static_cast<const uint8_t*>(it.A.scales);
+    p.b_codes = static_cast<const uint8_t*>(it.B.codes);
+    p.b_scales = static_cast<const uint8_t*>(it.B.scales);
+    p.M = it.M;
+    p.N = it.N;
+    p.K = it.K;
+    p.ktot = it.K;
+    p.bias = it.bias;
+    p.bias_f32 = it.bias_dtype == MX_F32;
+    p.c = it.C;
+    p.ldc = it.ldc;
+    p.c_f32 = it.c_dtype == MX_F32;
+  }
+  int st = check_device();
+  if (st != MX_OK) return st;
+  if (m.n == 0) return MX_OK;
+  return launched(mx::launch_gemm_many(m, fmt, static_cast<hipStream_t>(stream)));
+}
+
 int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
   if (!a) return MX_ERR_NULL;
   if (!a->X || !a->W1 || !a->W2 || !a->h || !a->Y) return MX_ERR_NULL;

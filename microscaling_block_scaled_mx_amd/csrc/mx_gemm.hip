@@ -49,6 +49,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "mx_device.h"
@@ -269,10 +270,9 @@ __device__ __forceinline__ void dense_tile(int bid, int tiles_m, int tiles_n, in
 }
 
 template <int FMT, int BM, int BN, int MODE, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, int bz, uint8_t* smem) {
   using CF = Cfg<FMT, BM, BN, MODE, EPI>;
   constexpr int kBits = CF::kBits;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[CF::kSmem];
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -282,10 +282,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   // ---------------------------------------------------------------- tile
   int tm, tn;
   if constexpr (MODE == kDense) {
-    dense_tile(blockIdx.x, (int)(p.M / BM), (int)(p.N / BN), tm, tn);
+    dense_tile(bx, (int)(p.M / BM), (int)(p.N / BN), tm, tn);
   } else {
-    tn = blockIdx.x;
-    tm = blockIdx.y;
+    tn = bx;
+    tm = by;
   }
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;  // SwiGLU: tile tn covers z columns [tn*BN/2, (tn+1)*BN/2)
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     b_coff = (int64_t)gi * code_bytes(p.b_group_rows, p.ktot, kBits);
   }
   if constexpr (MODE == kRaggedK) {
-    const int gi = blockIdx.z;
+    const int gi = bz;
     kbeg = gi ? p.offsets[gi - 1] : 0;
     kend = p.offsets[gi];
     kbeg = (kbeg < 0 ? 0 : (kbeg > p.R ? p.R : kbeg)) & ~(int64_t)127;
@@ -783,6 +783,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   }
 }
 
+// One launch, one GEMM (or one grouped GEMM): workgroup (x, y, z) computes
+// tile (x, y) of group z.
+template <int FMT, int BM, int BN, int MODE, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg<FMT, BM, BN, MODE, EPI>::kSmem];
+  gemm_tile<FMT, BM, BN, MODE, EPI>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+}
+
+// The dense tile shapes, in the order of GemmMany::shape.
+constexpr int kDenseShapes[5][2] = {{256, 256}, {256, 192}, {192, 256}, {192, 192}, {256, 128}};
+
+template <int FMT, int SH>
+using DenseCfg = Cfg<FMT, kDenseShapes[SH][0], kDenseShapes[SH][1], kDense, kEpiStore>;
+
+template <int FMT, int SH>
+__device__ __forceinline__ void dense_tile_sh(const GemmParams& p, int local, uint8_t* smem) {
+  gemm_tile<FMT, kDenseShapes[SH][0], kDenseShapes[SH][1], kDense, kEpiStore>(p, local, 0, 0, smem);
+}
+
+// Several dense GEMMs in one launch: workgroup w computes tile
+// w - first[i] of GEMM i (first[i] <= w < first[i + 1]) with that GEMM's
+// tile shape, SA or SB (indices into kDenseShapes); the branch is uniform
+// across the workgroup.
+template <int FMT, int SA, int SB>
+__global__ __launch_bounds__(kThreads, 1) void gemm_many_kernel(GemmMany m) {
+  constexpr int kA = DenseCfg<FMT, SA>::kSmem, kB = DenseCfg<FMT, SB>::kSmem;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kA > kB ? kA : kB];
+  const int w = blockIdx.x;
+  int i = 0;
+  while (i + 1 < m.n && w >= m.first[i + 1]) ++i;
+  const int local = w - m.first[i];
+  if (SA == SB || m.shape[i] == SA) dense_tile_sh<FMT, SA>(m.p[i], local, smem);
+  else dense_tile_sh<FMT, SB>(m.p[i], local, smem);
+}
+
 template <int FMT, int BM, int BN, int MODE, int EPI>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   dim3 grid;
@@ -814,37 +849,40 @@ int cu_count() {
   return n;
 }
 
-// Dense tile shape: the one whose rounds of one tile per compute unit cost
-// the least output area (rounds x BM x BN), larger tiles first on ties --
-// e.g. 4096 x 3072 takes 256 tiles of 256 x 192 in one round instead of 192
-// tiles of 256 x 256 on 192 of the 256 compute units.
-template <int FMT>
-hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
-  static constexpr int kShapes[5][2] = {{256, 256}, {256, 192}, {192, 256}, {192, 192}, {256, 128}};
+// Dense tile shape (index into kDenseShapes): the one whose rounds of one
+// tile per compute unit cost the least output area (rounds x BM x BN),
+// larger tiles first on ties -- e.g. 4096 x 3072 takes 256 tiles of
+// 256 x 192 in one round instead of 192 tiles of 256 x 256 on 192 of the 256
+// compute units.  MX_DENSE_TILE=<BM>x<BN> restricts the choice to that shape
+// (tests use it to cover every shape at small sizes); unset, or not dividing
+// M x N, it has no effect.  -1: no shape divides M x N.
+int dense_shape(int64_t M, int64_t N) {
   const int64_t cus = cu_count();
-  // MX_DENSE_TILE=<BM>x<BN> restricts the choice to that shape (tests use it
-  // to cover every shape at small sizes); unset, or not dividing M x N, it
-  // has no effect
   int force = -1;
   if (const char* env = getenv("MX_DENSE_TILE")) {
     int fm = 0, fn = 0;
     if (sscanf(env, "%dx%d", &fm, &fn) == 2)
       for (int i = 0; i < 5; ++i)
-        if (kShapes[i][0] == fm && kShapes[i][1] == fn && p.M % fm == 0 && p.N % fn == 0) force = i;
+        if (kDenseShapes[i][0] == fm && kDenseShapes[i][1] == fn && M % fm == 0 && N % fn == 0) force = i;
   }
   int best = -1;
   int64_t best_cost = 0;
   for (int i = 0; i < 5; ++i) {
-    const int bm = kShapes[i][0], bn = kShapes[i][1];
-    if (p.M % bm || p.N % bn || (force >= 0 && i != force)) continue;
-    const int64_t tiles = (p.M / bm) * (p.N / bn);
+    const int bm = kDenseShapes[i][0], bn = kDenseShapes[i][1];
+    if (M % bm || N % bn || (force >= 0 && i != force)) continue;
+    const int64_t tiles = (M / bm) * (N / bn);
     const int64_t cost = ((tiles + cus - 1) / cus) * bm * bn;
     if (best < 0 || cost < best_cost) {
       best = i;
       best_cost = cost;
     }
   }
-  switch (best) {
+  return best;
+}
+
+template <int FMT>
+hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
+  switch (dense_shape(p.M, p.N)) {
     case 0: return launch_one<FMT, 256, 256, kDense, kEpiStore>(p, stream);
     case 1: return launch_one<FMT, 256, 192, kDense, kEpiStore>(p, stream);
     case 2: return launch_one<FMT, 192, 256, kDense, kEpiStore>(p, stream);
@@ -865,7 +903,77 @@ hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream
   return launch_one<FMT, 256, 256, kRaggedK, kEpiStore>(p, stream);
 }
 
+// Workgroup ranges of a many-launch whose shapes are set.
+bool plan_many(GemmMany& m) {
+  int64_t tiles = 0;
+  for (int i = 0; i < m.n; ++i) {
+    const int sh = m.shape[i];
+    m.first[i] = (int)tiles;
+    tiles += (m.p[i].M / kDenseShapes[sh][0]) * (m.p[i].N / kDenseShapes[sh][1]);
+  }
+  m.first[m.n] = (int)tiles;
+  return tiles < (1ll << 31);
+}
+
+template <int FMT, int SA, int SB>
+hipError_t launch_many_k(GemmMany m, hipStream_t stream) {
+  if (!plan_many(m)) return hipErrorInvalidValue;
+  const unsigned tiles = (unsigned)m.first[m.n];
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_many_kernel<FMT, SA, SB>), dim3(tiles), dim3(kThreads), 0, stream, m);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_many_single(const GemmMany& m, int sh, hipStream_t stream) {
+  switch (sh) {
+    case 0: return launch_many_k<FMT, 0, 0>(m, stream);
+    case 1: return launch_many_k<FMT, 1, 1>(m, stream);
+    case 2: return launch_many_k<FMT, 2, 2>(m, stream);
+    case 3: return launch_many_k<FMT, 3, 3>(m, stream);
+    default: return launch_many_k<FMT, 4, 4>(m, stream);
+  }
+}
+
+// One launch when every GEMM takes the same tile shape, or the shapes are
+// 256 x 192 and 192 x 192 (a linear layer's forward / data-gradient and
+// weight-gradient GEMMs at the Flux shapes); otherwise one launch per shape.
+template <int FMT>
+hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
+  bool used[5] = {false, false, false, false, false};
+  for (int i = 0; i < all.n; ++i) used[all.shape[i]] = true;
+  int nused = 0;
+  for (int k = 0; k < 5; ++k) nused += used[k];
+  if (nused == 2 && used[1] && used[3]) return launch_many_k<FMT, 1, 3>(all, stream);
+  for (int k = 0; k < 5; ++k) {
+    if (!used[k]) continue;
+    GemmMany m;
+    memset(&m, 0, sizeof m);
+    for (int i = 0; i < all.n; ++i)
+      if (all.shape[i] == k) {
+        m.p[m.n] = all.p[i];
+        m.shape[m.n] = k;
+        ++m.n;
+      }
+    const hipError_t e = launch_many_single<FMT>(m, k, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_gemm_many(GemmMany m, int fmt, hipStream_t stream) {
+  if (m.n < 1 || m.n > kGemmManyMax) return hipErrorInvalidValue;
+  for (int i = 0; i < m.n; ++i)
+    if ((m.shape[i] = dense_shape(m.p[i].M, m.p[i].N)) < 0) return hipErrorInvalidValue;
+  switch (fmt) {
+    case kE2M1: return launch_many_fmt<kE2M1>(m, stream);
+    case kE2M3: return launch_many_fmt<kE2M3>(m, stream);
+    case kE4M3: return launch_many_fmt<kE4M3>(m, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream) {
   switch (fmt) {

@@ -97,4 +97,16 @@ struct GemmParams {
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream);
 
+// Up to kGemmManyMax dense GEMMs (kDense, kEpiStore) of one format in one
+// launch; each takes the tile shape launch_gemm would give it.  shape and
+// first are filled in by the launch.
+constexpr int kGemmManyMax = 4;
+struct GemmMany {
+  GemmParams p[kGemmManyMax];
+  int shape[kGemmManyMax];
+  int first[kGemmManyMax + 1];
+  int n;
+};
+hipError_t launch_gemm_many(GemmMany m, int fmt, hipStream_t stream);
+
 }  // namespace mx

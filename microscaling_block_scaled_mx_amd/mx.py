@@ -72,6 +72,15 @@ class QuantizeItem(ctypes.Structure):
 
 QUANTIZE_MANY_MAX = 8
 
+
+class GemmItem(ctypes.Structure):
+    _fields_ = [("A", Packed), ("B", Packed), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int32), ("c_dtype", ctypes.c_int32),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
+
+
+GEMM_MANY_MAX = 4
+
 _lib = None
 
 
@@ -88,6 +97,8 @@ def lib():
         L.mx_quantize.argtypes = [vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
         L.mx_quantize_many.restype = ci
         L.mx_quantize_many.argtypes = [ctypes.POINTER(QuantizeItem), ci, ci, ci, ci, ci, vp]
+        L.mx_gemm_many.restype = ci
+        L.mx_gemm_many.argtypes = [ctypes.POINTER(GemmItem), ci, ci, vp]
         L.mx_gemm.restype = ci
         L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_fused_mlp_fwd.restype = ci
@@ -224,6 +235,27 @@ def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int =
     st = lib().mx_gemm(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
                        _ptr(c), c_dtype, N if ldc is None else ldc, _stream(stream))
     _check(st, "mx_gemm")
+
+
+def gemm_many(items, fmt, stream=None):
+    """mx_gemm_many: each item is a dict with the mx_gemm arguments a, b
+    (packed operands), M, N, K, c and optionally c_dtype (BF16), ldc (N),
+    bias, bias_dtype (BF16) -- all computed in one launch where the tile
+    shapes allow."""
+    n = len(items)
+    arr = (GemmItem * max(n, 1))()
+    for i, it in enumerate(items):
+        M, N, K = it["M"], it["N"], it["K"]
+        c_dtype, bias_dtype = it.get("c_dtype", BF16), it.get("bias_dtype", BF16)
+        ldc = it.get("ldc") or N
+        what = f"gemm_many item {i}"
+        _need_packed(it["a"], M, K, fmt, what + " A")
+        _need_packed(it["b"], N, K, fmt, what + " B")
+        _need(it["c"], (4 if c_dtype == F32 else 2) * M * ldc, what + " C")
+        _need(it.get("bias"), (4 if bias_dtype == F32 else 2) * N, what + " bias")
+        arr[i] = GemmItem(_packed(it["a"]), _packed(it["b"]), M, N, K, _ptr(it.get("bias")), bias_dtype, c_dtype,
+                          _ptr(it["c"]), ldc)
+    _check(lib().mx_gemm_many(arr, n, fmt, _stream(stream)), "mx_gemm_many")
 
 
 def fused_mlp_fwd(M, D, F, X, W1, b1, W2, h, Y, Xr, Xc, W1r, W1c, W2r, W2c, ar, ac, fmt=E2M3,

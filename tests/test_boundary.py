@@ -227,3 +227,36 @@ def test_binding_rejects_short_buffers_before_the_call():
     off = torch.tensor([M], dtype=torch.int32)
     with pytest.raises(mx.MXError, match="grouped A codes"):
         mx.grouped_gemm(mx.RAGGED_M, 1, M, off, small, b, C, N=N, K=K)
+
+
+def gmany(items, n=None, fmt=mx.E2M1):
+    arr = (mx.GemmItem * max(len(items), 1))()
+    for k, it in enumerate(items):
+        a = dict(A=(P, P2), B=(P3, P4), M=256, N=256, K=256, bias=None, bias_dtype=mx.BF16, c_dtype=mx.BF16, C=P5,
+                 ldc=256)
+        a.update(it)
+        arr[k] = mx.GemmItem(mx.Packed(*a["A"]), mx.Packed(*a["B"]), a["M"], a["N"], a["K"], a["bias"],
+                             a["bias_dtype"], a["c_dtype"], a["C"], a["ldc"])
+    return mx.lib().mx_gemm_many(arr, len(items) if n is None else n, fmt, None)
+
+
+def test_gemm_many_rejections():
+    assert mx.lib().mx_gemm_many(None, 1, mx.E2M1, None) == NULL
+    assert gmany([{}], n=0) == SHAPE
+    assert gmany([{}] * 5) == SHAPE  # more than MX_GEMM_MANY_MAX
+    assert gmany([{}, dict(M=100)]) == SHAPE
+    assert gmany([{}, dict(ldc=128)]) == SHAPE
+    assert gmany([{}, dict(C=None)]) == NULL
+    assert gmany([dict(B=(P3, None))]) == NULL
+    assert gmany([{}, dict(C=P5 + 2)]) == ALIGN
+    assert gmany([{}], fmt=5) == FORMAT
+    assert gmany([dict(c_dtype=7)]) == FORMAT
+
+
+def test_gemm_many_valid_args_need_the_device():
+    for items, fmt in (([{}], mx.E2M1), ([{}, dict(M=4096, N=3072, K=3072, ldc=3072), dict(M=0)], mx.E2M3),
+                       ([dict(bias=P6, bias_dtype=mx.F32, c_dtype=mx.F32)] * 4, mx.E4M3)):
+        st = gmany(items, fmt=fmt)
+        assert st in (OK, DEVICE)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE

@@ -276,6 +276,68 @@ def test_gemm_exact_products_bitwise(mxl, orc, fmt):
     assert np.array_equal(host(c32).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
+def test_gemm_many_matches_gemm_and_oracle(mxl, orc, fmt, mode, had):
+    # four GEMMs of different shapes, K, bias and output types in one call:
+    # every output equals the separate mx_gemm result bit for bit, and one
+    # matches the oracle
+    rng = np.random.default_rng(500 + fmt)
+    cases = [dict(M=512, N=768, K=768), dict(M=256, N=512, K=256, bias="bf16"),
+             dict(M=768, N=256, K=512, c_dtype=mxl.F32, bias="f32"), dict(M=256, N=256, K=1024, ldc=320)]
+    items, ref = [], []
+    for c in cases:
+        M, N, K = c["M"], c["N"], c["K"]
+        A, B = I.bf16_normal(rng, (M, K)), I.bf16_normal(rng, (N, K), 0.05)
+        pa, pb = mxl.alloc_packed(M, K, fmt), mxl.alloc_packed(N, K, fmt)
+        mxl.quantize(dev(A), M, K, fmt, mode, had, row=pa)
+        mxl.quantize(dev(B), N, K, fmt, mode, had, row=pb)
+        c_dtype, ldc = c.get("c_dtype", mxl.BF16), c.get("ldc", N)
+        bias = bias_dtype = None
+        if c.get("bias") == "bf16":
+            bias, bias_dtype = dev(I.bf16_normal(rng, (N,), 0.5)), mxl.BF16
+        elif c.get("bias") == "f32":
+            bias, bias_dtype = torch.from_numpy(rng.normal(size=N).astype(np.float32)).cuda(), mxl.F32
+        mk = lambda: torch.full((M, ldc), 0x5A5A if c_dtype == mxl.BF16 else 0,
+                                dtype=torch.int16 if c_dtype == mxl.BF16 else torch.float32, device="cuda")
+        C1, C2 = mk(), mk()
+        it = dict(a=pa, b=pb, M=M, N=N, K=K, c=C1, c_dtype=c_dtype, ldc=ldc)
+        if bias is not None:
+            it.update(bias=bias, bias_dtype=bias_dtype)
+        items.append(it)
+        mxl.gemm(pa, pb, M, N, K, fmt, C2, bias=bias, bias_dtype=bias_dtype if bias is not None else mxl.BF16,
+                 c_dtype=c_dtype, ldc=ldc)
+        ref.append((C2, A, B))
+    mxl.gemm_many(items, fmt)
+    for it, (C2, A, B) in zip(items, ref):
+        assert torch.equal(it["c"], C2), (it["M"], it["N"], it["K"])
+    M, N, K = cases[0]["M"], cases[0]["N"], cases[0]["K"]
+    A, B = ref[0][1], ref[0][2]
+    qa = orc.quantize(A, M, K, fmt, mode, had, row=True)
+    qb = orc.quantize(B, N, K, fmt, mode, had, row=True)
+    want = orc.gemm(qa["row_codes"], qa["row_scales"], qb["row_codes"], qb["row_scales"], M, N, K, fmt)
+    assert bf16_close(host(items[0]["c"]), want)
+
+
+def test_gemm_many_linear_trio_matches_gemm(mxl):
+    # the Flux linear step's forward, data-gradient and weight-gradient GEMMs
+    # (tile shapes 256x192, 256x192, 192x192: one launch of both shapes)
+    fmt = 2
+    M, N, K = 4096, 3072, 3072
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    rnd = lambda *s: torch.randint(0, 256, s, dtype=torch.uint8, device="cuda", generator=gen)
+    sc = lambda *s: torch.randint(118, 130, s, dtype=torch.uint8, device="cuda", generator=gen)
+    P = lambda r, k: (rnd(*mxl.alloc_packed(r, k, fmt)[0].shape), sc(*mxl.alloc_packed(r, k, fmt)[1].shape))
+    xr, wr, dyr, wc, dyc, xc = P(M, K), P(N, K), P(M, N), P(K, N), P(N, M), P(K, M)
+    shapes = [(xr, wr, M, N, K), (dyr, wc, M, K, N), (dyc, xc, N, K, M)]
+    outs = [torch.empty((m, n), dtype=torch.int16, device="cuda") for _, _, m, n, _ in shapes]
+    refs = [torch.empty((m, n), dtype=torch.int16, device="cuda") for _, _, m, n, _ in shapes]
+    mxl.gemm_many([dict(a=a, b=b, M=m, N=n, K=k, c=c) for (a, b, m, n, k), c in zip(shapes, outs)], fmt)
+    for (a, b, m, n, k), c in zip(shapes, refs):
+        mxl.gemm(a, b, m, n, k, fmt, c)
+    for c1, c2 in zip(outs, refs):
+        assert torch.equal(c1, c2)
+
+
 def test_gemm_determinism(mxl, orc):
     rng = np.random.default_rng(3)
     M, N, K = 512, 512, 1024
