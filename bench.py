@@ -47,10 +47,10 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # HBM traffic per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE counters
 # (scaled by what they read for a plain copy), valid while the kernel
 # sources are those the counters were taken with
-GEMM_TRAFFIC = {"bytes_per_launch": 79.0e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "a3757de7c953527a58cd7e84942787d90e167d52"}
+GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
+                "sources_sha1": "ef27be76101b9ce922fac3c4d0dfb8245a78263a"}
 PACK_TRAFFIC = {"bytes_per_launch": 123.6e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "9de046d67417af520ee3265b4f5672279cf3178b"}
+                "sources_sha1": "f691e4c7e40566e0e5bced1b3448250272ffd74f"}
 
 
 def measured_traffic(rec):
