@@ -40,10 +40,6 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quantizer GB/s"
-# HBM bytes per GEMM launch of the headline step (mean of its three launches),
-# from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a plain copy
-# (profiles/mxfp6_gemm_pack_hbm_traffic.md); valid only for the GEMM sources
-# they were taken with
 # HBM traffic per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE counters
 # (scaled by what they read for a plain copy), valid while the kernel
 # sources are those the counters were taken with
@@ -231,8 +227,8 @@ def graph_time(launch, reps=10, replays=4, warm=None):
 
 
 def kernel_times(step):
-    """Device time (us) of each of the step's four launches, each repeated
-    back to back over the rotating input copies."""
+    """Device time (us) of each of the step's launches, each repeated back to
+    back over the rotating input copies."""
     out = {}
     for name in step.calls(0):
         def launch(r, name=name):
