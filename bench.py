@@ -371,13 +371,39 @@ def bench_cfg5(mx, T, iters=5):
     return out
 
 
+def bench_main_grad(mx, T):
+    """The headline weight gradient (MXFP6, dW [3072,3072] = dY^T X over
+    4096 tokens) stored into a bf16 main_grad (mx_gemm, beta = 0) and added
+    into it (mx_gemm_accumulate, beta = 1), device time per launch."""
+    import torch
+    M, N, K = 4096, 3072, 3072
+    g = torch.Generator(device="cuda").manual_seed(9)
+    P = lambda r, k: tuple(torch.randint(118 if i else 0, 130 if i else 256, t.shape, dtype=torch.uint8,
+                                         device="cuda", generator=g)
+                           for i, t in enumerate(mx.alloc_packed(r, k, mx.E2M3)))
+    dyc, xc = P(N, M), P(K, M)
+    main_grad = torch.zeros((N, K), dtype=torch.int16, device="cuda")
+    fl = 2.0 * M * N * K
+    store = graph_time(lambda r: mx.gemm(dyc, xc, N, K, M, mx.E2M3, main_grad))
+    accum = graph_time(lambda r: mx.gemm_accumulate(dyc, xc, N, K, M, mx.E2M3, main_grad))
+    return {"workload": "MXFP6 wgrad dW[3072,3072] (K = 4096 tokens) into a bf16 main_grad",
+            "store_us": store, "accumulate_us": accum, "store_tflops": fl / (store * 1e-6) / 1e12,
+            "accumulate_tflops": fl / (accum * 1e-6) / 1e12}
+
+
 def only(mx, spec, steps, warmup, T):
     """One kernel configuration, for profilers: gemm:FMT:M:N:K, pack:FMT:R:C
     (dual pack), packs:FMT:M:N:K (the linear step's fused dual packs of X,
     W and dY), gemms:FMT:M:N:K (its three GEMMs in one launch; random
-    codes) or copy:BYTES.  Prints one JSON line with its average time."""
+    codes) or copy:BYTES; or one whole other workload: linear256, mlp,
+    sweep, grouped or main_grad.  Prints one JSON line with its average time."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
+    workloads = {"linear256": bench_cfg1, "mlp": bench_cfg3, "sweep": bench_cfg4, "grouped": bench_cfg5,
+                 "main_grad": bench_main_grad}
+    if spec in workloads:  # one of the other workloads, as in the full run
+        print(json.dumps({"only": spec, **workloads[spec](mx, T)}), flush=True)
+        return
     kind, fbits, *dims = spec.split(":")
     if kind == "copy":  # plain device copy of fbits bytes: the reference for the traffic counters
         n = int(fbits)
@@ -440,7 +466,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C, packs:FMT:M:N:K, "
                          "gemms:FMT:M:N:K "
-                         "(FMT = 4, 6 or 8) or copy:BYTES (a plain device copy)")
+                         "(FMT = 4, 6 or 8), copy:BYTES (a plain device copy), or one workload: "
+                         "linear256, mlp, sweep, grouped, main_grad")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
@@ -503,7 +530,7 @@ def main():
     if args.extra == "all":
         extra = {}
         for name, fn in (("mxfp4_256", bench_cfg1), ("fused_mlp_mxfp6", bench_cfg3), ("mxfp4_flux_sweep", bench_cfg4),
-                         ("grouped_mxfp8", bench_cfg5)):
+                         ("grouped_mxfp8", bench_cfg5), ("wgrad_main_grad", bench_main_grad)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = fn(mx, T)
             torch.cuda.empty_cache()

@@ -226,6 +226,26 @@ int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, cons
             int c_dtype, int64_t ldc, void* stream);
 
 /*
+ * mx_gemm_accumulate -- C[m][n] += sum_k A[m][k] * B[n][k] (+ bias[n]): the
+ * weight gradient added into a caller-owned main_grad buffer in the GEMM's
+ * own store epilogue, so no separate add pass reads and writes it again.
+ * [P1] commit messages (the MXFP6 wgrad written straight into main_grad by
+ * the GEMM): the page's GEMM stores with beta = 0, which overwrites, and so
+ * needs one microbatch per optimizer step; mx_gemm into main_grad is that
+ * store.  This call is beta = 1, for several microbatches per step.
+ *
+ * Arguments, tiling and errors are those of mx_gemm; c is read and written
+ * (bf16 or binary32, dtype c_dtype).  Arithmetic per element: the binary32
+ * accumulator plus the bias, plus the previous c converted exactly to
+ * binary32, then one rounding to c_dtype (nearest even for bf16).  The
+ * result is bitwise round(fl32(fl32(acc + bias) + c_old)) where
+ * fl32(acc + bias) is what mx_gemm stores with c_dtype = MX_F32.
+ */
+int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                       int64_t M, int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c,
+                       int c_dtype, int64_t ldc, void* stream);
+
+/*
  * mx_gemm_many -- several GEMMs of one format in a single launch, with the
  * results of n mx_gemm calls made with each item's arguments (each GEMM
  * takes the tile shape mx_gemm would give it, so the results are bitwise
@@ -242,7 +262,9 @@ int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, cons
  *               item's C may overlap another item's A, B or C.
  *  n            1 <= n <= MX_GEMM_MANY_MAX.
  *  fmt          element format of every operand.
- * Items with M = 0 or N = 0 are skipped.
+ * Items with M = 0 or N = 0 are skipped.  An item with accumulate = 1 adds
+ * into its C as mx_gemm_accumulate does, in a launch of its own after the
+ * others (any other value than 0 or 1 is MX_ERR_FORMAT).
  * Errors: MX_ERR_NULL (items NULL), MX_ERR_SHAPE (n out of range), then as
  * mx_gemm for the first failing item; nothing is enqueued on an error.
  */
@@ -255,6 +277,8 @@ typedef struct {
   int32_t c_dtype;
   void* C;
   int64_t ldc;
+  int32_t accumulate;     /* 0: C = A . B^T (mx_gemm); 1: C += A . B^T (mx_gemm_accumulate) */
+  int32_t reserved;       /* 0 */
 } mx_gemm_item;
 
 int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream);
@@ -268,6 +292,10 @@ int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream);
  * assembled; the fc1 bias gradient comes back as a per-column sum).
  * All packs use fmt / scale_mode / hadamard (MXFP6: MX_E2M3, FLOOR, 1).
  * M, D, F multiples of 256.  Packed buffers: rows x K as named.
+ * The backward's weight gradients may be the caller's main_grad buffers
+ * ([P1] commit messages: the gradient lands in main_grad for both MLP
+ * matrices): accumulate_wgrad = 0 overwrites them, 1 adds into them (any
+ * other value is MX_ERR_FORMAT).
  */
 typedef struct {
   int64_t M, D, F;        /* tokens; fc1 in = fc2 out width; fc1 out = fc2 in width */
@@ -290,7 +318,9 @@ typedef struct {
 
 typedef struct {
   int64_t M, D, F;
-  int32_t fmt, scale_mode, hadamard, reserved;
+  int32_t fmt, scale_mode, hadamard;
+  int32_t accumulate_wgrad; /* 0: dW1, dW2 are overwritten; 1: the weight gradients are added into them
+                               (main_grad buffers accumulated over microbatches, as mx_gemm_accumulate) */
   const void* dY;         /* bf16 [M][D] */
   const void* h;          /* bf16 [M][F] from the forward */
   mx_packed Xc, W1c, W2c, ac; /* from the forward */

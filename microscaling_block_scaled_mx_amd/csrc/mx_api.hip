@@ -133,7 +133,8 @@ int validate_gemm(const void* ac, const void* as, const void* bc, const void* bs
 }
 
 int gemm_launch(const void* ac, const void* as, const void* bc, const void* bs, int64_t M, int64_t N, int64_t K,
-                int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc, hipStream_t s) {
+                int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc, int accumulate,
+                hipStream_t s) {
   if (M == 0 || N == 0) return MX_OK;
   GemmParams p;
   memset(&p, 0, sizeof p);
@@ -150,7 +151,7 @@ int gemm_launch(const void* ac, const void* as, const void* bc, const void* bs, 
   p.c = c;
   p.ldc = ldc;
   p.c_f32 = c_dtype == MX_F32;
-  return launched(mx::launch_gemm(p, fmt, mx::kDense, mx::kEpiStore, s));
+  return launched(mx::launch_gemm(p, fmt, mx::kDense, accumulate ? mx::kEpiAccum : mx::kEpiStore, s));
 }
 
 bool packed_ok(const mx_packed& q) { return q.codes && q.scales; }
@@ -221,7 +222,17 @@ int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, cons
   int st = validate_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc);
   if (st != MX_OK) return st;
   if ((st = check_device()) != MX_OK) return st;
-  return gemm_launch(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc,
+  return gemm_launch(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc, 0,
+                     static_cast<hipStream_t>(stream));
+}
+
+int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
+                       int64_t M, int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c,
+                       int c_dtype, int64_t ldc, void* stream) {
+  int st = validate_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc);
+  if (st != MX_OK) return st;
+  if ((st = check_device()) != MX_OK) return st;
+  return gemm_launch(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc, 1,
                      static_cast<hipStream_t>(stream));
 }
 
@@ -236,7 +247,8 @@ int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream) {
     int st = validate_gemm(it.A.codes, it.A.scales, it.B.codes, it.B.scales, it.M, it.N, it.K, fmt, it.bias,
                            it.bias_dtype, it.C, it.c_dtype, it.ldc);
     if (st != MX_OK) return st;
-    if (it.M == 0 || it.N == 0) continue;
+    if (it.accumulate != 0 && it.accumulate != 1) return MX_ERR_FORMAT;
+    if (it.M == 0 || it.N == 0 || it.accumulate) continue;  // accumulating items: a launch each, below
     GemmParams& p = m.p[m.n++];
     p.a_codes = static_cast<const uint8_t*>(it.A.codes);
     p.a_scales = static_cast<const uint8_t*>(it.A.scales);
@@ -254,8 +266,16 @@ int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream) {
   }
   int st = check_device();
   if (st != MX_OK) return st;
-  if (m.n == 0) return MX_OK;
-  return launched(mx::launch_gemm_many(m, fmt, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m.n > 0 && (st = launched(mx::launch_gemm_many(m, fmt, s))) != MX_OK) return st;
+  for (int i = 0; i < n; ++i) {
+    const mx_gemm_item& it = items[i];
+    if (!it.accumulate) continue;
+    if ((st = gemm_launch(it.A.codes, it.A.scales, it.B.codes, it.B.scales, it.M, it.N, it.K, fmt, it.bias,
+                          it.bias_dtype, it.C, it.c_dtype, it.ldc, 1, s)) != MX_OK)
+      return st;
+  }
+  return MX_OK;
 }
 
 int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
@@ -290,7 +310,7 @@ int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
     return st;
   // fc1: h = X W1^T + b1 (bias in the fp32 accumulator, one rounding)
   if ((st = gemm_launch(a->Xr.codes, a->Xr.scales, a->W1r.codes, a->W1r.scales, M, F, D, fmt, a->b1, MX_BF16,
-                        a->h, MX_BF16, F, s)))
+                        a->h, MX_BF16, F, 0, s)))
     return st;
   // a = GELU(h) exists only inside the packer: packed rows for fc2, columns for dW2
   if ((st = quantize_launch(a->h, nullptr, 1, M, F, fmt, mode, had, MX_PRO_GELU_TANH, a->ar.codes, a->ar.scales,
@@ -298,7 +318,7 @@ int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
     return st;
   // fc2: Y = a W2^T
   return gemm_launch(a->ar.codes, a->ar.scales, a->W2r.codes, a->W2r.scales, M, D, F, fmt, nullptr, MX_BF16, a->Y,
-                     MX_BF16, D, s);
+                     MX_BF16, D, 0, s);
 }
 
 int mx_fused_mlp_bwd(const mx_mlp_bwd_args* a, void* stream) {
@@ -309,6 +329,7 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* a, void* stream) {
   for (const mx_packed* q : packs)
     if (!packed_ok(*q)) return MX_ERR_NULL;
   if (!combo_ok(a->fmt, a->scale_mode, a->hadamard)) return MX_ERR_FORMAT;
+  if (a->accumulate_wgrad != 0 && a->accumulate_wgrad != 1) return MX_ERR_FORMAT;
   const int64_t M = a->M, D = a->D, F = a->F;
   if (M < 0 || D < 0 || F < 0 || M % 256 || D % 256 || F % 256) return MX_ERR_SHAPE;
   const void* ptrs[] = {a->dY, a->h, a->da, a->dX, a->dW1, a->dW2, a->db1, a->db1_partials};
@@ -327,7 +348,7 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* a, void* stream) {
     return st;
   // fc2 dgrad: da = dY W2 (K = D), materialised
   if ((st = gemm_launch(a->dYr.codes, a->dYr.scales, a->W2c.codes, a->W2c.scales, M, F, D, fmt, nullptr, MX_BF16,
-                        a->da, MX_BF16, F, s)))
+                        a->da, MX_BF16, F, 0, s)))
     return st;
   // dh = dGELU(da, h) exists only inside the packer; bias gradient from its column sums
   if ((st = quantize_launch(a->da, a->h, 1, M, F, fmt, mode, had, MX_PRO_DGELU_TANH, a->dhr.codes, a->dhr.scales,
@@ -335,15 +356,15 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* a, void* stream) {
     return st;
   // fc1 dgrad: dX = dh W1 (K = F)
   if ((st = gemm_launch(a->dhr.codes, a->dhr.scales, a->W1c.codes, a->W1c.scales, M, D, F, fmt, nullptr, MX_BF16,
-                        a->dX, MX_BF16, D, s)))
+                        a->dX, MX_BF16, D, 0, s)))
     return st;
   // fc1 wgrad: dW1 = dh^T X (K = M)
   if ((st = gemm_launch(a->dhc.codes, a->dhc.scales, a->Xc.codes, a->Xc.scales, F, D, M, fmt, nullptr, MX_BF16,
-                        a->dW1, MX_BF16, D, s)))
+                        a->dW1, MX_BF16, D, a->accumulate_wgrad, s)))
     return st;
   // fc2 wgrad: dW2 = dY^T a (K = M)
   return gemm_launch(a->dYc.codes, a->dYc.scales, a->ac.codes, a->ac.scales, D, F, M, fmt, nullptr, MX_BF16,
-                     a->dW2, MX_BF16, F, s);
+                     a->dW2, MX_BF16, F, a->accumulate_wgrad, s);
 }
 
 int mx_grouped_gemm(const mx_grouped_args* a, void* stream) {

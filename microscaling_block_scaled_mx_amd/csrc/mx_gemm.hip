@@ -283,11 +283,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   int tm, tn;
   if constexpr (MODE == kDense) {
     dense_tile(bx, (int)(p.M / BM), (int)(p.N / BN), tm, tn);
+  } else if constexpr (MODE == kRaggedM) {
+    // 1-D grid of (row tile, column tile) pairs, column tiles fastest.  Each
+    // XCD takes a contiguous range, so the tiles of one row panel (and of
+    // one group's weights) share that XCD's L2 -- except under dSwiGLU,
+    // whose epilogue reads H rows scattered over its tile and measured 17%
+    // faster with consecutive tiles spread over the XCDs (the other
+    // epilogues 3-7% slower that way).
+    const int nt = (int)(EPI == kEpiSwiglu ? 2 * p.F / BN : p.N / BN);
+    const int T = (int)gridDim.x;
+    int bid = bx;
+    if (EPI != kEpiDSwiglu && (T & 7) == 0) bid = (bid & 7) * (T >> 3) + (bid >> 3);
+    tn = bid % nt;
+    tm = bid / nt;
   } else {
     tn = bx;
     tm = by;
   }
-  const int64_t m0 = (int64_t)tm * BM;
+  int64_t m0 = (int64_t)tm * BM;
+  int64_t m_end = 0;  // ragged-M: end of this tile's group (rows of C it may write)
   const int64_t n0 = (int64_t)tn * BN;  // SwiGLU: tile tn covers z columns [tn*BN/2, (tn+1)*BN/2)
   int64_t kbeg = 0, kend = p.K;
   int64_t b_row0 = 0;  // first B row of this tile's group
@@ -295,13 +309,30 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   int64_t b_coff = 0;  // byte offset of this tile's group in the B codes (one K-group-major array per group)
   int64_t c_off = 0;   // element offset of this tile's group in C
   if constexpr (MODE == kRaggedM) {
-    // offsets are a caller invariant; clamping keeps every access inside the
-    // buffers even if it is broken
-    int64_t end = p.offsets[p.G - 1];
-    end = end < p.R ? end : p.R;
-    if (m0 >= end) return;  // rows at or past the last group end: untouched
-    int gi = 0;
-    while (p.offsets[gi] <= m0) ++gi;
+    // Group gi's rows [start, end) are cut into ceil((end - start) / BM)
+    // tiles (counts are multiples of 128, so a 256-row tile at a group's
+    // end may hold 128 rows); row tile tm walks the groups in order.  Rows
+    // of a tile past its group's end are loaded as the group's last row and
+    // never stored, so nothing at or past the last end is read or written.
+    // Offsets are a caller invariant; clamping them into [start, R] and down
+    // to a multiple of 128 keeps every access inside the buffers (and every
+    // 32-row column block inside one tile) even if they are broken.
+    int64_t start = 0;
+    int rem = tm, gi = -1;
+    for (int q = 0; q < p.G; ++q) {
+      int64_t e = p.offsets[q];
+      e = (e < start ? start : (e > p.R ? p.R : e)) & ~(int64_t)127;
+      const int64_t nt = (e - start + BM - 1) / BM;
+      if (rem < nt) {
+        gi = q;
+        m0 = start + (int64_t)rem * BM;
+        m_end = e;
+        break;
+      }
+      rem -= (int)nt;
+      start = e;
+    }
+    if (gi < 0) return;  // past the last group's tiles
     b_row0 = (int64_t)gi * p.b_group_rows;
     b_soff = (int64_t)gi * scale_bytes(p.b_group_rows, p.ktot);
     b_coff = (int64_t)gi * code_bytes(p.b_group_rows, p.ktot, kBits);
@@ -346,7 +377,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     const int q = t + kThreads * i, r = q / CF::kChunks, pos = q % CF::kChunks;
     const int rr = r < BM ? r : 0;  // junk slots read a valid chunk
     const int c = chunk_at<CF::kChunks>(rr, pos);
-    a_off[i] = (uint32_t)((m0 + rr) * kGB + 16 * c);
+    const int64_t ar = MODE == kRaggedM && m0 + rr >= m_end ? m_end - 1 : m0 + rr;
+    a_off[i] = (uint32_t)(ar * kGB + 16 * c);
   }
 #pragma unroll
   for (int i = 0; i < CF::kBIters; ++i) {
@@ -364,7 +396,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   for (int j = 0; j < 2; ++j) {
     const int r = t + 256 * j;
     const bool is_b = r >= BM && r < BM + BN;
-    s_src[j] = is_b ? p.b_scales + b_soff + (b_row(r - BM) - b_row0) * 4 : p.a_scales + (m0 + (r < BM ? r : 0)) * 4;
+    const int64_t ar = MODE == kRaggedM && m0 + (r < BM ? r : 0) >= m_end ? m_end - 1 : m0 + (r < BM ? r : 0);
+    s_src[j] = is_b ? p.b_scales + b_soff + (b_row(r - BM) - b_row0) * 4 : p.a_scales + ar * 4;
     s_step[j] = (is_b ? b_rows : a_rows) * 4;
   }
   const int wave_u = wave_uniform(wave);
@@ -543,7 +576,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   pin_arg(p.c);
   pin_arg(p.ldc);
   pin_arg(p.c_f32);
-  if constexpr (EPI == kEpiStore) {
+  if constexpr (EPI == kEpiStore || EPI == kEpiAccum) {
     pin_arg(p.bias);
     pin_arg(p.bias_f32);
   } else {
@@ -586,7 +619,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   // ---------------------------------------------------------------- epilogues
   // Lane (row lrow, column group q = 8 * (e / 4) + 4 * g) of MFMA tile (i, j)
   // holds acc[i][j][4 * (e / 4) + 0..3] = C[row][col + 0..3].
-  if constexpr (EPI == kEpiStore) {
+  if constexpr (EPI == kEpiStore || EPI == kEpiAccum) {
     // bias of this lane's columns, read once (one uniform branch)
     float bv[CF::kNJ][16];
     if (p.bias == nullptr) {
@@ -619,37 +652,138 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
           bv[j][4 * e4 + 3] = bf16_hi(q.y);
         }
     }
-    if (p.c_f32) {
-      float* C = reinterpret_cast<float*>(p.c) + c_off;
+    // C += A . B^T (mx_gemm_accumulate: a weight gradient added into a
+    // caller-owned main_grad): the previous C joins the binary32 result
+    // after the bias, before the store's one rounding.  The old values of
+    // one 32-row block of MFMA tiles are loaded together (no load sits under
+    // a per-element branch); the accumulators themselves are never
+    // rewritten.  A kernel of its own, so that the plain store's register
+    // allocation is not touched.
+    constexpr bool accumulate = EPI == kEpiAccum;
+    auto load_old = [&](int i, float (&o)[CF::kNJ][16]) {
+      const int64_t m = m0 + wm * CF::kWM + 32 * i + lrow;
+      if (p.c_f32) {
+        const float* Co = reinterpret_cast<const float*>(p.c) + m * p.ldc;
+        float4 w[CF::kNJ][4];
 #pragma unroll
-      for (int i = 0; i < CF::kMI; ++i)
+        for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+            w[j][e4] = *reinterpret_cast<const float4*>(Co + n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g);
 #pragma unroll
         for (int j = 0; j < CF::kNJ; ++j)
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
-            const int64_t m = m0 + wm * CF::kWM + 32 * i + lrow;
-            const int64_t n = n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
-            const v16f& a = acc[i][j];
-            *reinterpret_cast<float4*>(C + m * p.ldc + n) =
-                make_float4(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1],
-                            a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]);
+            o[j][4 * e4 + 0] = w[j][e4].x;
+            o[j][4 * e4 + 1] = w[j][e4].y;
+            o[j][4 * e4 + 2] = w[j][e4].z;
+            o[j][4 * e4 + 3] = w[j][e4].w;
           }
+      } else {
+        const uint16_t* Co = reinterpret_cast<const uint16_t*>(p.c) + m * p.ldc;
+        uint2 w[CF::kNJ][4];
+#pragma unroll
+        for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+            w[j][e4] = *reinterpret_cast<const uint2*>(Co + n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g);
+#pragma unroll
+        for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            o[j][4 * e4 + 0] = bf16_lo(w[j][e4].x);
+            o[j][4 * e4 + 1] = bf16_hi(w[j][e4].x);
+            o[j][4 * e4 + 2] = bf16_lo(w[j][e4].y);
+            o[j][4 * e4 + 3] = bf16_hi(w[j][e4].y);
+          }
+      }
+    };
+    // value of element e of MFMA tile (i, j): fl32(acc + bias) (+ old)
+    if (p.c_f32) {
+      float* C = reinterpret_cast<float*>(p.c) + c_off;
+      auto store_f32 = [&](auto with_old) {
+        constexpr bool kOld = decltype(with_old)::value;
+#pragma unroll
+        for (int i = 0; i < CF::kMI; ++i) {
+          float o[CF::kNJ][16];
+          if constexpr (kOld) load_old(i, o);
+          const int64_t m = m0 + wm * CF::kWM + 32 * i + lrow;
+          if (MODE == kRaggedM && m >= m_end) continue;
+#pragma unroll
+          for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int64_t n = n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = acc[i][j][4 * e4 + q] + bv[j][4 * e4 + q];
+                if constexpr (kOld) v[q] = v[q] + o[j][4 * e4 + q];
+              }
+              *reinterpret_cast<float4*>(C + m * p.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+      };
+      if constexpr (accumulate) {
+        store_f32(std::true_type{});
+      } else {
+#pragma unroll
+        for (int i = 0; i < CF::kMI; ++i)
+#pragma unroll
+          for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int64_t m = m0 + wm * CF::kWM + 32 * i + lrow;
+              const int64_t n = n0 + wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
+              const v16f& a = acc[i][j];
+              if (MODE == kRaggedM && m >= m_end) continue;
+              *reinterpret_cast<float4*>(C + m * p.ldc + n) =
+                  make_float4(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1],
+                              a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]);
+            }
+      }
     } else {
       // bf16: stage the wavefront's tile in LDS with 8-byte writes, then
       // write 16-byte row chunks
       uint8_t* wt = smem + wave * CF::kWM * CF::kCPitch;
+      auto stage_bf16 = [&](auto with_old) {
+        constexpr bool kOld = decltype(with_old)::value;
 #pragma unroll
-      for (int i = 0; i < CF::kMI; ++i)
+        for (int i = 0; i < CF::kMI; ++i) {
+          float o[CF::kNJ][16];
+          if constexpr (kOld) load_old(i, o);
 #pragma unroll
-        for (int j = 0; j < CF::kNJ; ++j)
+          for (int j = 0; j < CF::kNJ; ++j)
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const int r = 32 * i + lrow, cl = 32 * j + 8 * e4 + 4 * g;
-            const v16f& a = acc[i][j];
-            *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) =
-                make_uint2(pack_bf16x2(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1]),
-                           pack_bf16x2(a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]));
-          }
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int r = 32 * i + lrow, cl = 32 * j + 8 * e4 + 4 * g;
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = acc[i][j][4 * e4 + q] + bv[j][4 * e4 + q];
+                if constexpr (kOld) v[q] = v[q] + o[j][4 * e4 + q];
+              }
+              *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) =
+                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+        }
+      };
+      if constexpr (accumulate) {
+        stage_bf16(std::true_type{});
+      } else {
+#pragma unroll
+        for (int i = 0; i < CF::kMI; ++i)
+#pragma unroll
+          for (int j = 0; j < CF::kNJ; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int r = 32 * i + lrow, cl = 32 * j + 8 * e4 + 4 * g;
+              const v16f& a = acc[i][j];
+              *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) =
+                  make_uint2(pack_bf16x2(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1]),
+                             pack_bf16x2(a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]));
+            }
+      }
       __syncthreads();
       uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + c_off;
       constexpr int kRowChunks = CF::kWN / 8;
@@ -659,6 +793,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
         const uint2 lo = *reinterpret_cast<const uint2*>(wt + r * CF::kCPitch + ch * 16);
         const uint2 hi = *reinterpret_cast<const uint2*>(wt + r * CF::kCPitch + ch * 16 + 8);
         const int64_t m = m0 + wm * CF::kWM + r;
+        if (MODE == kRaggedM && m >= m_end) continue;
         *reinterpret_cast<uint4*>(C + m * p.ldc + n0 + wn * CF::kWN + ch * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     }
@@ -687,9 +822,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
             hu[q] = __float_as_uint(u0) >> 16;
             z[q] = __float_as_uint(swiglu_bf16(g0, u0)) >> 16;
           }
-          *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + zb + zc) = make_uint2(hg[0] | (hg[1] << 16), hg[2] | (hg[3] << 16));
-          *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + p.F + zb + zc) =
-              make_uint2(hu[0] | (hu[1] << 16), hu[2] | (hu[3] << 16));
+          if (m < m_end) {
+            *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + zb + zc) =
+                make_uint2(hg[0] | (hg[1] << 16), hg[2] | (hg[3] << 16));
+            *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + p.F + zb + zc) =
+                make_uint2(hu[0] | (hu[1] << 16), hu[2] | (hu[3] << 16));
+          }
           *reinterpret_cast<uint2*>(zt + ml * CF::kZPitch + zc * 2) = make_uint2(z[0] | (z[1] << 16), z[2] | (z[3] << 16));
         }
     __syncthreads();
@@ -697,6 +835,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     constexpr int ZC = BN / 2;  // z columns in the tile
     for (int q = t; q < BM * (ZC / 32); q += kThreads) {
       const int row = q / (ZC / 32), blk = q % (ZC / 32);
+      if (m0 + row >= m_end) continue;
       float v[32];
       lds_row_block(zt, CF::kZPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = zb + 32 * blk;
@@ -709,6 +848,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     }
     for (int q = t; q < ZC * (BM / 32); q += kThreads) {
       const int col = q % ZC, rb2 = q / ZC;
+      if (m0 + 32 * rb2 >= m_end) continue;
       float v[32];
       lds_col_block(zt, CF::kZPitch, rb2 * 32, col, v);
       const int64_t cz = zb + col, m = m0 + 32 * rb2;
@@ -733,8 +873,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
           const int ml = wm * CF::kWM + 32 * i + lrow;
           const int nl = wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
           const int64_t m = m0 + ml, n = n0 + nl;
-          const uint2 gw = *reinterpret_cast<const uint2*>(H + m * 2 * p.F + n);
-          const uint2 uw = *reinterpret_cast<const uint2*>(H + m * 2 * p.F + p.F + n);
+          // rows past the group's end read the group's last row (loads stay
+          // unconditional, so the compiler need not wait for each at a join)
+          const bool live = m < m_end;
+          const int64_t mh = live ? m : m_end - 1;
+          const uint2 gw = *reinterpret_cast<const uint2*>(H + mh * 2 * p.F + n);
+          const uint2 uw = *reinterpret_cast<const uint2*>(H + mh * 2 * p.F + p.F + n);
           const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
           const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
           uint32_t dzb[4], dg[4], du[4];
@@ -745,7 +889,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
             dg[q] = __float_as_uint(dswiglu_gate_bf16(dz, gv[q], uv[q])) >> 16;
             du[q] = __float_as_uint(dswiglu_up_bf16(dz, gv[q])) >> 16;
           }
-          if (p.c)
+          if (p.c && live)
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.F + n) =
                 make_uint2(dzb[0] | (dzb[1] << 16), dzb[2] | (dzb[3] << 16));
           *reinterpret_cast<uint2*>(tg + ml * CF::kDPitch + nl * 2) = make_uint2(dg[0] | (dg[1] << 16), dg[2] | (dg[3] << 16));
@@ -757,6 +901,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     for (int q = t; q < 2 * BM * (BN / 32); q += kThreads) {
       const int half = q / (BM * (BN / 32)), rq = q % (BM * (BN / 32));
       const int row = rq / (BN / 32), blk = rq % (BN / 32);
+      if (m0 + row >= m_end) continue;
       float v[32];
       lds_row_block(half ? tu : tg, CF::kDPitch, row, blk * 32, v);
       const int64_t m = m0 + row, col = (half ? p.F : 0) + n0 + 32 * blk;
@@ -770,6 +915,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     for (int q = t; q < 2 * BN * (BM / 32); q += kThreads) {
       const int half = q / (BN * (BM / 32)), cq = q % (BN * (BM / 32));
       const int col = cq % BN, rb2 = cq / BN;
+      if (m0 + 32 * rb2 >= m_end) continue;
       float v[32];
       lds_col_block(half ? tu : tg, CF::kDPitch, rb2 * 32, col, v);
       const int64_t cw = (half ? p.F : 0) + n0 + col, m = m0 + 32 * rb2;
@@ -824,8 +970,12 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   if (MODE == kDense) {
     grid = dim3((unsigned)((p.M / BM) * (p.N / BN)), 1, 1);
   } else if (MODE == kRaggedM) {
-    const unsigned nt = EPI == kEpiSwiglu ? (unsigned)(2 * p.F / BN) : (unsigned)(p.N / BN);
-    grid = dim3(nt, (unsigned)(p.R / BM), 1);
+    // column tiles x an upper bound on the row tiles: sum over groups of
+    // ceil(count / BM) <= R / BM + G; the surplus workgroups exit at once
+    const int64_t nt = EPI == kEpiSwiglu ? 2 * p.F / BN : p.N / BN;
+    const int64_t rows = p.R > 0 ? (p.R + BM - 1) / BM + p.G : 0;
+    if (nt * rows >= (1ll << 31)) return hipErrorInvalidValue;
+    grid = dim3((unsigned)(nt * rows), 1, 1);
   } else {
     grid = dim3((unsigned)(p.N / BN), (unsigned)(p.M / BM), (unsigned)p.G);
   }
@@ -880,25 +1030,28 @@ int dense_shape(int64_t M, int64_t N) {
   return best;
 }
 
-template <int FMT>
+template <int FMT, int EPI>
 hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
   switch (dense_shape(p.M, p.N)) {
-    case 0: return launch_one<FMT, 256, 256, kDense, kEpiStore>(p, stream);
-    case 1: return launch_one<FMT, 256, 192, kDense, kEpiStore>(p, stream);
-    case 2: return launch_one<FMT, 192, 256, kDense, kEpiStore>(p, stream);
-    case 3: return launch_one<FMT, 192, 192, kDense, kEpiStore>(p, stream);
-    case 4: return launch_one<FMT, 256, 128, kDense, kEpiStore>(p, stream);
+    case 0: return launch_one<FMT, 256, 256, kDense, EPI>(p, stream);
+    case 1: return launch_one<FMT, 256, 192, kDense, EPI>(p, stream);
+    case 2: return launch_one<FMT, 192, 256, kDense, EPI>(p, stream);
+    case 3: return launch_one<FMT, 192, 192, kDense, EPI>(p, stream);
+    case 4: return launch_one<FMT, 256, 128, kDense, EPI>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int FMT>
 hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream) {
-  if (mode == kDense) return launch_dense<FMT>(p, stream);
+  if (mode == kDense)
+    return epi == kEpiAccum ? launch_dense<FMT, kEpiAccum>(p, stream) : launch_dense<FMT, kEpiStore>(p, stream);
   if (mode == kRaggedM) {
-    if (epi == kEpiSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiSwiglu>(p, stream);
+    // 256-row tiles; dSwiGLU keeps 128 rows, its two bf16 LDS tiles of the
+    // epilogue would not fit at 256 x 256
+    if (epi == kEpiSwiglu) return launch_one<FMT, 256, 256, kRaggedM, kEpiSwiglu>(p, stream);
     if (epi == kEpiDSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiDSwiglu>(p, stream);
-    return launch_one<FMT, 128, 256, kRaggedM, kEpiStore>(p, stream);
+    return launch_one<FMT, 256, 256, kRaggedM, kEpiStore>(p, stream);
   }
   return launch_one<FMT, 256, 256, kRaggedK, kEpiStore>(p, stream);
 }

@@ -65,7 +65,8 @@ hipError_t launch_colsum_finish(const float* partials, int64_t nb, int64_t C, fl
                                 hipStream_t stream);
 
 enum GemmMode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
-enum Epilogue { kEpiStore = 0, kEpiSwiglu = 1, kEpiDSwiglu = 2 };
+// kEpiAccum (dense only): the store of kEpiStore, adding into the previous C
+enum Epilogue { kEpiStore = 0, kEpiSwiglu = 1, kEpiDSwiglu = 2, kEpiAccum = 3 };
 
 struct GemmParams {
   const uint8_t* a_codes;

@@ -48,7 +48,7 @@ class MlpFwdArgs(ctypes.Structure):
 class MlpBwdArgs(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("D", ctypes.c_int64), ("F", ctypes.c_int64),
                 ("fmt", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("hadamard", ctypes.c_int32),
-                ("reserved", ctypes.c_int32),
+                ("accumulate_wgrad", ctypes.c_int32),
                 ("dY", ctypes.c_void_p), ("h", ctypes.c_void_p),
                 ("Xc", Packed), ("W1c", Packed), ("W2c", Packed), ("ac", Packed),
                 ("da", ctypes.c_void_p), ("dX", ctypes.c_void_p), ("dW1", ctypes.c_void_p),
@@ -76,7 +76,8 @@ QUANTIZE_MANY_MAX = 8
 class GemmItem(ctypes.Structure):
     _fields_ = [("A", Packed), ("B", Packed), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int32), ("c_dtype", ctypes.c_int32),
-                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("accumulate", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 GEMM_MANY_MAX = 4
@@ -101,6 +102,8 @@ def lib():
         L.mx_gemm_many.argtypes = [ctypes.POINTER(GemmItem), ci, ci, vp]
         L.mx_gemm.restype = ci
         L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
+        L.mx_gemm_accumulate.restype = ci
+        L.mx_gemm_accumulate.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_fused_mlp_fwd.restype = ci
         L.mx_fused_mlp_fwd.argtypes = [ctypes.POINTER(MlpFwdArgs), vp]
         L.mx_fused_mlp_bwd.restype = ci
@@ -237,11 +240,23 @@ def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int =
     _check(st, "mx_gemm")
 
 
+def gemm_accumulate(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16,
+                    c_dtype: int = BF16, ldc: int | None = None, stream=None):
+    """mx_gemm_accumulate: c [M][ldc] += A . B^T (+ bias); a, b = (codes, scales)."""
+    _need_packed(a, M, K, fmt, "gemm_accumulate A")
+    _need_packed(b, N, K, fmt, "gemm_accumulate B")
+    _need(c, (4 if c_dtype == F32 else 2) * M * (N if ldc is None else ldc), "gemm_accumulate C")
+    _need(bias, (4 if bias_dtype == F32 else 2) * N, "gemm_accumulate bias")
+    st = lib().mx_gemm_accumulate(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias),
+                                  bias_dtype, _ptr(c), c_dtype, N if ldc is None else ldc, _stream(stream))
+    _check(st, "mx_gemm_accumulate")
+
+
 def gemm_many(items, fmt, stream=None):
     """mx_gemm_many: each item is a dict with the mx_gemm arguments a, b
     (packed operands), M, N, K, c and optionally c_dtype (BF16), ldc (N),
-    bias, bias_dtype (BF16) -- all computed in one launch where the tile
-    shapes allow."""
+    bias, bias_dtype (BF16), accumulate (False: c = A.B^T; True: c += A.B^T)
+    -- all computed in one launch where the tile shapes allow."""
     n = len(items)
     arr = (GemmItem * max(n, 1))()
     for i, it in enumerate(items):
@@ -254,7 +269,7 @@ def gemm_many(items, fmt, stream=None):
         _need(it["c"], (4 if c_dtype == F32 else 2) * M * ldc, what + " C")
         _need(it.get("bias"), (4 if bias_dtype == F32 else 2) * N, what + " bias")
         arr[i] = GemmItem(_packed(it["a"]), _packed(it["b"]), M, N, K, _ptr(it.get("bias")), bias_dtype, c_dtype,
-                          _ptr(it["c"]), ldc)
+                          _ptr(it["c"]), ldc, int(it.get("accumulate", 0)), 0)
     _check(lib().mx_gemm_many(arr, n, fmt, _stream(stream)), "mx_gemm_many")
 
 
@@ -273,7 +288,7 @@ def fused_mlp_fwd(M, D, F, X, W1, b1, W2, h, Y, Xr, Xc, W1r, W1c, W2r, W2c, ar, 
 
 
 def fused_mlp_bwd(M, D, F, dY, h, Xc, W1c, W2c, ac, da, dX, dW1, dW2, db1, db1_partials, dYr, dYc, dhr, dhc,
-                  fmt=E2M3, scale_mode=FLOOR, hadamard=True, stream=None):
+                  fmt=E2M3, scale_mode=FLOOR, hadamard=True, accumulate_wgrad=False, stream=None):
     for t, n, what in ((dY, 2 * M * D, "dY"), (h, 2 * M * F, "h"), (da, 2 * M * F, "da"), (dX, 2 * M * D, "dX"),
                        (dW1, 2 * F * D, "dW1"), (dW2, 2 * D * F, "dW2"), (db1, 4 * F, "db1"),
                        (db1_partials, 4 * (M // 32) * F, "db1 partials")):
@@ -281,7 +296,7 @@ def fused_mlp_bwd(M, D, F, dY, h, Xc, W1c, W2c, ac, da, dX, dW1, dW2, db1, db1_p
     for p, r, k, what in ((Xc, D, M, "Xc"), (W1c, D, F, "W1c"), (W2c, F, D, "W2c"), (ac, F, M, "ac"),
                           (dYr, M, D, "dYr"), (dYc, D, M, "dYc"), (dhr, M, F, "dhr"), (dhc, F, M, "dhc")):
         _need_packed(p, r, k, fmt, "fused bwd " + what)
-    a = MlpBwdArgs(M, D, F, fmt, scale_mode, int(hadamard), 0, _ptr(dY), _ptr(h), _packed(Xc), _packed(W1c),
+    a = MlpBwdArgs(M, D, F, fmt, scale_mode, int(hadamard), int(accumulate_wgrad), _ptr(dY), _ptr(h), _packed(Xc), _packed(W1c),
                    _packed(W2c), _packed(ac), _ptr(da), _ptr(dX), _ptr(dW1), _ptr(dW2), _ptr(db1),
                    _ptr(db1_partials), _packed(dYr), _packed(dYc), _packed(dhr), _packed(dhc))
     _check(lib().mx_fused_mlp_bwd(ctypes.byref(a), _stream(stream)), "mx_fused_mlp_bwd")

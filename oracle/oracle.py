@@ -218,6 +218,19 @@ def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: int,
     return out
 
 
+def gemm_accumulate(c_old, a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: int,
+                    bias=None) -> np.ndarray:
+    """C_old + A . B^T (+ bias), binary64: the weight gradient added into a
+    caller-owned main_grad ([P1] commit messages: the MXFP6 GEMM writes the
+    weight gradient into main_grad itself instead of a separate add).
+    ``c_old`` is bf16 bits (uint16) or float32, [M][N]; its values are exact
+    in binary64.  The GPU rounds the sum once to c_old's dtype."""
+    c_old = np.asarray(c_old)
+    old = bf16_to_f32(c_old).astype(np.float64) if c_old.dtype == np.uint16 else c_old.astype(np.float64)
+    assert old.shape == (M, N)
+    return old + gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias=bias)
+
+
 def unpack_codes(codes: np.ndarray, fmt: int, k: int) -> np.ndarray:
     """Element codes [rows][k] from a packed [rows][k*bits/8] array."""
     codes = np.ascontiguousarray(codes, np.uint8)

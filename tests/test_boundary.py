@@ -123,12 +123,12 @@ def test_quantize_many_valid_args_need_the_device():
         if not mx.lib().mx_device_supported(0):
             assert st == DEVICE
 
-def g(**kw):
+def g(fn="mx_gemm", **kw):
     a = dict(ac=P, as_=P2, bc=P3, bs=P4, M=256, N=512, K=768, fmt=mx.E2M3, bias=None, bt=mx.BF16, c=P5,
              ct=mx.BF16, ldc=512)
     a.update(kw)
-    return mx.lib().mx_gemm(a["ac"], a["as_"], a["bc"], a["bs"], a["M"], a["N"], a["K"], a["fmt"], a["bias"],
-                            a["bt"], a["c"], a["ct"], a["ldc"], None)
+    return getattr(mx.lib(), fn)(a["ac"], a["as_"], a["bc"], a["bs"], a["M"], a["N"], a["K"], a["fmt"], a["bias"],
+                                 a["bt"], a["c"], a["ct"], a["ldc"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -138,13 +138,15 @@ def g(**kw):
     (dict(ldc=256), SHAPE), (dict(ldc=516), SHAPE),
     (dict(ac=P + 4), ALIGN), (dict(c=P5 + 2), ALIGN), (dict(bias=P6 + 8), ALIGN),
 ])
-def test_gemm_rejections(kw, want):
-    assert g(**kw) == want
+@pytest.mark.parametrize("fn", ["mx_gemm", "mx_gemm_accumulate"])
+def test_gemm_rejections(fn, kw, want):
+    assert g(fn, **kw) == want
 
 
-def test_gemm_valid_args_need_the_device():
+@pytest.mark.parametrize("fn", ["mx_gemm", "mx_gemm_accumulate"])
+def test_gemm_valid_args_need_the_device(fn):
     for kw in (dict(), dict(bias=P6, bt=mx.F32, ct=mx.F32, ldc=1024), dict(M=0), dict(K=0)):
-        st = g(**kw)
+        st = g(fn, **kw)
         assert st in (OK, DEVICE)
         if not mx.lib().mx_device_supported(0):
             assert st == DEVICE
@@ -233,10 +235,10 @@ def gmany(items, n=None, fmt=mx.E2M1):
     arr = (mx.GemmItem * max(len(items), 1))()
     for k, it in enumerate(items):
         a = dict(A=(P, P2), B=(P3, P4), M=256, N=256, K=256, bias=None, bias_dtype=mx.BF16, c_dtype=mx.BF16, C=P5,
-                 ldc=256)
+                 ldc=256, accumulate=0)
         a.update(it)
         arr[k] = mx.GemmItem(mx.Packed(*a["A"]), mx.Packed(*a["B"]), a["M"], a["N"], a["K"], a["bias"],
-                             a["bias_dtype"], a["c_dtype"], a["C"], a["ldc"])
+                             a["bias_dtype"], a["c_dtype"], a["C"], a["ldc"], a["accumulate"], 0)
     return mx.lib().mx_gemm_many(arr, len(items) if n is None else n, fmt, None)
 
 
@@ -251,11 +253,13 @@ def test_gemm_many_rejections():
     assert gmany([{}, dict(C=P5 + 2)]) == ALIGN
     assert gmany([{}], fmt=5) == FORMAT
     assert gmany([dict(c_dtype=7)]) == FORMAT
+    assert gmany([{}, dict(accumulate=2)]) == FORMAT
 
 
 def test_gemm_many_valid_args_need_the_device():
     for items, fmt in (([{}], mx.E2M1), ([{}, dict(M=4096, N=3072, K=3072, ldc=3072), dict(M=0)], mx.E2M3),
-                       ([dict(bias=P6, bias_dtype=mx.F32, c_dtype=mx.F32)] * 4, mx.E4M3)):
+                       ([dict(bias=P6, bias_dtype=mx.F32, c_dtype=mx.F32)] * 4, mx.E4M3),
+                       ([{}, dict(accumulate=1)], mx.E2M1)):
         st = gmany(items, fmt=fmt)
         assert st in (OK, DEVICE)
         if not mx.lib().mx_device_supported(0):

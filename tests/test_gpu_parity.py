@@ -508,3 +508,101 @@ def test_grouped_inactive_tail_untouched(mxl, orc):
     assert np.all(zrs[:, 640:] == 0xAB) and not np.any(zrs[:, :640] == 0xAB)
     assert np.all(zcs[640 // 128:] == 0xAB) and not np.any(zcs[:640 // 128] == 0xAB)
     assert not np.any(np.isnan(I.bf16_bits_to_f32(Hh[:640])))
+
+
+# ------------------------------------------------------------------ wgrad into main_grad (C += A . B^T)
+@pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_gemm_accumulate_parity(mxl, orc, fmt, mode, had, c_dtype):
+    # C += A . B^T (+ bias) on a C that already holds values: bitwise one
+    # rounding of fl32(fl32(acc + bias) + C_old), where fl32(acc + bias) is
+    # the same kernel's binary32 store, and within the GEMM bar of the
+    # oracle's C_old + A . B^T
+    rng = np.random.default_rng(700 + fmt)
+    M, N, K = 512, 768, 1024
+    A, B = I.bf16_normal(rng, (M, K)), I.bf16_normal(rng, (N, K), 0.02)
+    bias = I.bf16_normal(rng, (N,), 0.01)
+    pa, pb = mxl.alloc_packed(M, K, fmt), mxl.alloc_packed(N, K, fmt)
+    mxl.quantize(dev(A), M, K, fmt, mode, had, row=pa)
+    mxl.quantize(dev(B), N, K, fmt, mode, had, row=pb)
+    f32 = c_dtype == "f32"
+    cd = mxl.F32 if f32 else mxl.BF16
+    old = rng.standard_normal((M, N)).astype(np.float32) * 0.5
+    old_dev = dev(old) if f32 else dev(I.f32_to_bf16_bits(old))
+    c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mxl.gemm(pa, pb, M, N, K, fmt, c32, bias=dev(bias), c_dtype=mxl.F32)
+    c = old_dev.clone()
+    mxl.gemm_accumulate(pa, pb, M, N, K, fmt, c, bias=dev(bias), c_dtype=cd)
+    old_f = old if f32 else I.bf16_bits_to_f32(I.f32_to_bf16_bits(old))
+    want32 = (host(c32) + old_f).astype(np.float32)  # one binary32 add, nearest even
+    got = host(c)
+    if f32:
+        assert_f32_bitwise(got, want32)
+    else:
+        assert np.array_equal(got, I.f32_to_bf16_bits(want32))
+    qa = orc.quantize(A, M, K, fmt, mode, had, row=True)
+    qb = orc.quantize(B, N, K, fmt, mode, had, row=True)
+    old_bits = old if f32 else I.f32_to_bf16_bits(old)
+    ref = orc.gemm_accumulate(old_bits, qa["row_codes"], qa["row_scales"], qb["row_codes"], qb["row_scales"], M, N,
+                              K, fmt, bias=bias)
+    inc = ref - old_f.astype(np.float64)  # the GEMM's own contribution sets the error scale
+    g = got.astype(np.float64) if f32 else I.bf16_bits_to_f32(got).astype(np.float64)
+    half_ulp = 0.0 if f32 else np.abs(ref) * 2.0 ** -8
+    assert np.all(np.abs(g - ref) <= REL * np.max(np.abs(inc)) + half_ulp)
+
+
+def test_wgrad_accumulates_microbatches_into_main_grad(mxl, orc):
+    # two microbatches' weight gradients into one bf16 main_grad: the first
+    # stores (beta = 0, mx_gemm), the second adds (beta = 1); one linear
+    # step's trio in one launch with the wgrad item accumulating gives the
+    # same bits as the separate call
+    fmt, mode, had = 2, 0, True
+    M, N, K = 1024, 512, 768  # tokens per microbatch, out, in
+    rng = np.random.default_rng(710)
+    mbs = [(I.bf16_normal(rng, (M, K)), I.bf16_normal(rng, (M, N))) for _ in range(2)]
+    main_grad = torch.full((N, K), 0x7FC0, dtype=torch.int16, device="cuda")  # stale NaNs: overwritten by beta = 0
+    ref = np.zeros((N, K))
+    for i, (X, dY) in enumerate(mbs):
+        xc, dyc = mxl.alloc_packed(K, M, fmt), mxl.alloc_packed(N, M, fmt)
+        mxl.quantize(dev(X), M, K, fmt, mode, had, col=xc)
+        mxl.quantize(dev(dY), M, N, fmt, mode, had, col=dyc)
+        (mxl.gemm if i == 0 else mxl.gemm_accumulate)(dyc, xc, N, K, M, fmt, main_grad)
+        qx = orc.quantize(X, M, K, fmt, mode, had, row=False, col=True)
+        qd = orc.quantize(dY, M, N, fmt, mode, had, row=False, col=True)
+        ref += orc.gemm(qd["col_codes"], qd["col_scales"], qx["col_codes"], qx["col_scales"], N, K, M, fmt)
+    g = I.bf16_bits_to_f32(host(main_grad)).astype(np.float64)
+    # two bf16 roundings (the first store and the accumulated store)
+    assert np.all(np.abs(g - ref) <= REL * np.max(np.abs(ref)) + np.abs(ref) * 2.0 ** -7)
+    # the same accumulation as an item of mx_gemm_many
+    X, dY = mbs[1]
+    xc, dyc, xr, wr = (mxl.alloc_packed(K, M, fmt), mxl.alloc_packed(N, M, fmt), mxl.alloc_packed(M, K, fmt),
+                       mxl.alloc_packed(N, K, fmt))
+    mxl.quantize(dev(X), M, K, fmt, mode, had, row=xr, col=xc)
+    mxl.quantize(dev(dY), M, N, fmt, mode, had, col=dyc)
+    mxl.quantize(dev(I.bf16_normal(rng, (N, K), 0.02)), N, K, fmt, mode, had, row=wr)
+    start = dev(I.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32)))
+    c1, c2 = start.clone(), start.clone()
+    y = bf16_empty(M, N)
+    mxl.gemm_many([dict(a=xr, b=wr, M=M, N=N, K=K, c=y), dict(a=dyc, b=xc, M=N, N=K, K=M, c=c1, accumulate=True)],
+                  fmt)
+    mxl.gemm_accumulate(dyc, xc, N, K, M, fmt, c2)
+    assert torch.equal(c1, c2)
+
+
+def test_fused_mlp_bwd_accumulates_weight_gradients(mxl):
+    # accumulate_wgrad = 1 adds both weight gradients into dW1 / dW2 (the
+    # main_grad buffers), exactly as mx_gemm_accumulate on the backward's own
+    # packed operands; dX, da and db1 do not change
+    M, D, F = 256, 256, 512
+    X, W1, b1, W2, dY = I.mlp(304, M, D, F)
+    t = run_mlp(mxl, X, W1, b1, W2, dY, M, D, F)
+    first = {k: t[k].clone() for k in ("dW1", "dW2", "dX", "da", "db1")}
+    mxl.fused_mlp_bwd(M, D, F, t["dY"], t["h"], t["Xc"], t["W1c"], t["W2c"], t["ac"], t["da"], t["dX"], t["dW1"],
+                      t["dW2"], t["db1"], t["part"], t["dYr"], t["dYc"], t["dhr"], t["dhc"], accumulate_wgrad=True)
+    w1, w2 = first["dW1"].clone(), first["dW2"].clone()
+    mxl.gemm_accumulate(t["dhc"], t["Xc"], F, D, M, 2, w1)
+    mxl.gemm_accumulate(t["dYc"], t["ac"], D, F, M, 2, w2)
+    assert torch.equal(t["dW1"], w1) and torch.equal(t["dW2"], w2)
+    assert not torch.equal(t["dW1"], first["dW1"])
+    for k in ("dX", "da", "db1"):
+        assert torch.equal(t[k], first[k]), k

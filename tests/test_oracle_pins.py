@@ -518,3 +518,33 @@ def test_grouped_chain_empty_expert_and_shapes(orc):
     dense = orc.gemm(q["row_codes"][s:e], q["row_scales"][s:e], w["row_codes"], w["row_scales"], e - s, 2 * F,
                      D, orc.E4M3)
     assert np.array_equal(dense, fwd["H64"][s:e])
+
+
+def test_gemm_accumulate_is_linear_in_k_and_exact_on_grid_values(orc):
+    # Operands whose values lie on the E2M1 grid quantize exactly under any
+    # FLOOR scale, and their dot products are small multiples of 1/4: every
+    # partial sum is exact in binary32.  Splitting K into two halves and
+    # accumulating the second GEMM into the first one's binary32 result must
+    # then give the whole-K GEMM exactly; a zero C_old gives the plain GEMM.
+    rng = np.random.default_rng(77)
+    M, N, K = 64, 96, 128
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    vals = lambda shape: (rng.choice(grid, shape) * rng.choice([-1, 1], shape)).astype(np.float32)
+    X = I.f32_to_bf16_bits(vals((M, K)))
+    W = I.f32_to_bf16_bits(vals((N, K)))
+    fmt = orc.E2M1
+    qx, qw = orc.quantize(X, M, K, fmt, orc.FLOOR), orc.quantize(W, N, K, fmt, orc.FLOOR)
+    whole = orc.gemm(qx["row_codes"], qx["row_scales"], qw["row_codes"], qw["row_scales"], M, N, K, fmt)
+    exact = I.bf16_bits_to_f32(X).astype(np.float64) @ I.bf16_bits_to_f32(W).astype(np.float64).T
+    assert np.array_equal(whole, exact)
+    half = lambda q: orc._kslice(q["row_codes"], q["row_scales"], fmt, 0, K // 2)
+    rest = lambda q: orc._kslice(q["row_codes"], q["row_scales"], fmt, K // 2, K)
+    first = orc.gemm(*half(qx), *half(qw), M, N, K // 2, fmt)
+    acc = orc.gemm_accumulate(first.astype(np.float32), *rest(qx), *rest(qw), M, N, K // 2, fmt)
+    assert np.array_equal(acc, whole)
+    zero = orc.gemm_accumulate(np.zeros((M, N), np.uint16), *rest(qx), *rest(qw), M, N, K // 2, fmt)
+    assert np.array_equal(zero, orc.gemm(*rest(qx), *rest(qw), M, N, K // 2, fmt))
+    # a bf16 C_old enters with its exact value
+    old = I.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    got = orc.gemm_accumulate(old, *rest(qx), *rest(qw), M, N, K // 2, fmt)
+    assert np.array_equal(got - I.bf16_bits_to_f32(old).astype(np.float64), zero)
