@@ -496,6 +496,142 @@ int orc_quantize(const uint16_t* x, const uint16_t* aux, int64_t R, int64_t C, i
 }
 
 /* ------------------------------------------------------------------ */
+/* Stochastic rounding of MXFP4 gradient packs.                           */
+/* [P3 Overview, configuration table]: the MXFP4 recipe has one numerics  */
+/* switch, stochastic rounding (SR) of the FP4 quantization of gradients. */
+/* The page gives neither the rounding rule nor the random source; the    */
+/* readings taken here:                                                   */
+/*  - the block scale is the FLOOR scale of round-to-nearest packing;     */
+/*  - v = x * 2^-X is exact; |v| >= 6 saturates to 6 (no SR there);       */
+/*    otherwise with grid neighbours lo <= |v| < hi and                   */
+/*    t = (|v| - lo) / (hi - lo), the magnitude is hi iff                 */
+/*    (r >> 8) < floor(t * 2^24), for a 32-bit random word r, else lo;    */
+/*    the sign is kept (-0 included).  E[result] = v up to 2^-24 of the   */
+/*    grid spacing, and values on the grid never move;                    */
+/*  - r is a word of Philox4x32-10 (Salmon, Moraes, Dror and Shaw,         */
+/*    "Parallel random numbers: as easy as 1, 2, 3", SC 2011), keyed by   */
+/*    the 64-bit seed (low word first) with counter                        */
+/*    (q mod 2^32, q div 2^32, axis, 0), q = i div 4, where i is the      */
+/*    element's index in its packed operand, i = (batch entry * rows +    */
+/*    operand row) * K + k, and axis is 0 for the rowwise operand and 1    */
+/*    for the columnwise one; the element takes output word i mod 4.      */
+/* ------------------------------------------------------------------ */
+
+/* Philox4x32 with 10 rounds.  One round: the two 32x32 -> 64-bit products
+ * of counter words 0 and 2 with the round multipliers, counter words
+ * recombined as (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1,
+ * lo(M0*c0)); the key is bumped by the Weyl constants between rounds. */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint64_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    uint64_t p0 = M0 * (uint64_t)c0, p1 = M1 * (uint64_t)c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The random word of element i of a packed operand (see above). */
+uint32_t orc_sr_word(uint64_t seed, int axis, uint64_t i) {
+  uint64_t q = i / 4;
+  uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)axis, 0u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return out[i % 4];
+}
+
+/* E2M1 code of the exact value v with the random word r (rule above). */
+unsigned orc_encode_e2m1_sr(double v, uint32_t r) {
+  unsigned sign = signbit(v) ? 0x8u : 0u;
+  double a = fabs(v);
+  if (a >= 6.0) return sign | 7u;
+  double lo, hi;
+  unsigned clo; /* code of lo: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are codes 0..7 */
+  if (a < 2.0) {
+    clo = (unsigned)floor(a * 2.0);
+    lo = 0.5 * clo;
+    hi = lo + 0.5;
+  } else if (a < 4.0) {
+    lo = floor(a);
+    hi = lo + 1.0;
+    clo = 4u + (unsigned)(lo - 2.0);
+  } else {
+    lo = 4.0;
+    hi = 6.0;
+    clo = 6u;
+  }
+  double t = (a - lo) / (hi - lo); /* exact: a has 24 significant bits */
+  uint64_t k = (uint64_t)floor(t * 16777216.0);
+  return sign | (clo + ((uint64_t)(r >> 8) < k ? 1u : 0u));
+}
+
+static void quant_block_sr(const float* v, uint64_t seed, int axis, uint64_t i0, unsigned* codes,
+                           unsigned* scale) {
+  float amax = 0.0f;
+  int has_nan = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (isnan(v[i])) has_nan = 1;
+    float a = fabsf(v[i]);
+    if (a > amax) amax = a;
+  }
+  if (has_nan) amax = NAN;
+  unsigned s = orc_scale_floor(ORC_E2M1, amax);
+  *scale = s;
+  if (s == 0xffu) {
+    for (int i = 0; i < 32; ++i) codes[i] = 0u;
+    return;
+  }
+  int e = (int)s - 127;
+  for (int i = 0; i < 32; ++i)
+    codes[i] = orc_encode_e2m1_sr(ldexp((double)v[i], -e), orc_sr_word(seed, axis, i0 + (uint64_t)i));
+}
+
+/* MXFP4 (E2M1, FLOOR scale) pack of the bf16 tensor x [R][C] with
+ * stochastic rounding, rowwise ([R] x K=C) and/or columnwise ([C] x K=R,
+ * transposed); index_base = batch entry * R * C (the operand index of its
+ * first element).  NULL outputs are skipped. */
+int orc_quantize_sr(const uint16_t* x, int64_t R, int64_t C, uint64_t seed, uint64_t index_base,
+                    uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales) {
+  if (R % 32 || C % 32 || R < 0 || C < 0) return 1;
+  int64_t rb = orc_row_bytes(ORC_E2M1, C), cb = orc_row_bytes(ORC_E2M1, R);
+  if (row_codes) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+      for (int64_t b = 0; b < C / 32; ++b) {
+        float blk[32];
+        unsigned codes[32], s;
+        for (int i = 0; i < 32; ++i) blk[i] = orc_bf16_to_f32(x[r * C + b * 32 + i]);
+        quant_block_sr(blk, seed, 0, index_base + (uint64_t)(r * C + b * 32), codes, &s);
+        row_scales[r * (C / 32) + b] = (uint8_t)s;
+        for (int i = 0; i < 32; ++i) orc_put_code(row_codes + r * rb, ORC_E2M1, b * 32 + i, codes[i]);
+      }
+    }
+  }
+  if (col_codes) {
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+      for (int64_t b = 0; b < R / 32; ++b) {
+        float blk[32];
+        unsigned codes[32], s;
+        for (int i = 0; i < 32; ++i) blk[i] = orc_bf16_to_f32(x[(b * 32 + i) * C + c]);
+        quant_block_sr(blk, seed, 1, index_base + (uint64_t)(c * R + b * 32), codes, &s);
+        col_scales[c * (R / 32) + b] = (uint8_t)s;
+        for (int i = 0; i < 32; ++i) orc_put_code(col_codes + c * cb, ORC_E2M1, b * 32 + i, codes[i]);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Block-scaled GEMM, C = A . B^T (NT layout [P3 Troubleshooting]).       */
 /* Both operands are K-major packed codes + [rows][K/32] scales.          */
 /* Dequantized values code * 2^(scale-127) are exact in binary64; the     */

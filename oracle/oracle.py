@@ -75,6 +75,15 @@ def lib():
         L.orc_gemm.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, ctypes.c_int, u16p, i64p, i64, f64p]
         L.orc_get_code.restype = ctypes.c_uint
         L.orc_get_code.argtypes = [u8p, ctypes.c_int, i64]
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        L.orc_philox4x32_10.restype = None
+        L.orc_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        L.orc_sr_word.restype = ctypes.c_uint32
+        L.orc_sr_word.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_uint64]
+        L.orc_encode_e2m1_sr.restype = ctypes.c_uint
+        L.orc_encode_e2m1_sr.argtypes = [ctypes.c_double, ctypes.c_uint32]
+        L.orc_quantize_sr.restype = ctypes.c_int
+        L.orc_quantize_sr.argtypes = [u16p, i64, i64, ctypes.c_uint64, ctypes.c_uint64, u8p, u8p, u8p, u8p]
         _lib = L
     return _lib
 
@@ -190,6 +199,46 @@ def quantize(x: np.ndarray, R: int, C: int, fmt: int, mode: int, hadamard: bool 
         out["col_codes"], out["col_scales"] = cc, cs
     if colsum:
         out["colsum_partials"], out["colsum"] = cp, csum
+    return out
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon et al., SC 2011) of four counter words and two
+    key words -> four output words."""
+    c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib().orc_philox4x32_10(c, k, o)
+    return list(o)
+
+
+def sr_word(seed: int, axis: int, i: int) -> int:
+    return lib().orc_sr_word(seed, axis, i)
+
+
+def encode_e2m1_sr(v: float, r: int) -> int:
+    return lib().orc_encode_e2m1_sr(float(v), r)
+
+
+def quantize_sr(x: np.ndarray, R: int, C: int, seed: int, row: bool = True, col: bool = False,
+                index_base: int = 0) -> dict:
+    """MXFP4 (E2M1, FLOOR) pack with stochastic rounding of the elements
+    [P3 Overview: SR of FP4 gradient quantization] -- see orc_quantize_sr."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rc = rs = cc = cs = None
+    if row:
+        rc, rs = np.zeros((R, row_bytes(E2M1, C)), np.uint8), np.zeros((R, C // 32), np.uint8)
+    if col:
+        cc, cs = np.zeros((C, row_bytes(E2M1, R)), np.uint8), np.zeros((C, R // 32), np.uint8)
+    st = lib().orc_quantize_sr(_p(x, ctypes.c_uint16), R, C, seed, index_base, _p(rc, ctypes.c_uint8),
+                               _p(rs, ctypes.c_uint8), _p(cc, ctypes.c_uint8), _p(cs, ctypes.c_uint8))
+    if st != 0:
+        raise ValueError(f"orc_quantize_sr rejected the arguments (status {st})")
+    out = {}
+    if row:
+        out["row_codes"], out["row_scales"] = rc, rs
+    if col:
+        out["col_codes"], out["col_scales"] = cc, cs
     return out
 
 

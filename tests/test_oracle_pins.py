@@ -548,3 +548,96 @@ def test_gemm_accumulate_is_linear_in_k_and_exact_on_grid_values(orc):
     old = I.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
     got = orc.gemm_accumulate(old, *rest(qx), *rest(qw), M, N, K // 2, fmt)
     assert np.array_equal(got - I.bf16_bits_to_f32(old).astype(np.float64), zero)
+
+
+# ------------------------------------------------------------------ stochastic rounding (MXFP4 gradients)
+def test_philox_known_answer_vectors(orc):
+    kat = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")))
+    for v in kat["vectors"]:
+        h = lambda xs: [int(t, 16) for t in xs]
+        assert orc.philox4x32_10(h(v["ctr"]), h(v["key"])) == h(v["out"])
+
+
+def test_sr_word_counter_layout(orc):
+    # element i takes word i % 4 of the Philox block with counter
+    # (i // 4 low, i // 4 high, axis, 0) and key (seed low, seed high)
+    seed = 0x0123456789ABCDEF
+    for axis in (0, 1):
+        for i in (0, 1, 2, 3, 4, 7, 2**32 * 4 + 5, 2**40 + 3):
+            q = i // 4
+            want = orc.philox4x32_10([q & 0xFFFFFFFF, q >> 32, axis, 0], [seed & 0xFFFFFFFF, seed >> 32])[i % 4]
+            assert orc.sr_word(seed, axis, i) == want
+
+
+def test_e2m1_sr_rule_brute_force(orc):
+    # every E2M1 grid interval, at fractions t = j/8, against the rule
+    # written with exact rationals: up iff (r >> 8) < floor(t * 2^24)
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    rs = [0, 1, 255, 256, 0x7FFFFF00, 0x80000000, 0xFFFFFFFF] + [int(v) for v in
+                                                             np.random.default_rng(5).integers(0, 2**32, 40)]
+    for c in range(7):
+        lo, hi = Fraction(grid[c]), Fraction(grid[c + 1])
+        for j in range(8):
+            t = Fraction(j, 8)
+            v = lo + t * (hi - lo)
+            for sign in (1, -1):
+                for r in rs:
+                    up = (r >> 8) < math.floor(t * 2**24)
+                    want = (c + up) | (8 if sign < 0 else 0)
+                    assert orc.encode_e2m1_sr(math.copysign(float(v), sign), r) == want, (float(v), r)
+    # saturation at and above the largest magnitude; -0 keeps its sign
+    for r in rs:
+        assert orc.encode_e2m1_sr(6.0, r) == 7 and orc.encode_e2m1_sr(7.9, r) == 7
+        assert orc.encode_e2m1_sr(-0.0, r) == 8 and orc.encode_e2m1_sr(0.0, r) == 0
+
+
+def test_e2m1_sr_is_unbiased_and_keeps_grid_values(orc):
+    rng = np.random.default_rng(6)
+    # grid values never move, whatever the random word
+    for v in (0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -3):
+        for r in rng.integers(0, 2**32, 50):
+            assert orc.decode(orc.E2M1, orc.encode_e2m1_sr(v, int(r))) == v
+    # E[q] = v: mean of 20000 draws within 5 standard errors, for values
+    # inside each spacing regime
+    for v in (0.3, 1.1, 2.6, 4.5, -5.2):
+        draws = np.array([orc.decode(orc.E2M1, orc.encode_e2m1_sr(v, int(r)))
+                          for r in rng.integers(0, 2**32, 20000)])
+        assert abs(draws.mean() - v) < 5 * draws.std() / math.sqrt(len(draws)) + 1e-9, v
+
+
+def test_quantize_sr_matches_nearest_scales_and_neighbour_codes(orc):
+    # SR packing keeps the nearest-rounding pack's scales; each code is one
+    # of the two grid neighbours of x / 2^X (the nearest-rounding code or
+    # its neighbour toward x); the same seed gives the same bytes, another
+    # seed other bytes; columnwise SR is rowwise SR of the transpose with
+    # axis 1 (checked element by element through the rule)
+    rng = np.random.default_rng(8)
+    R, C = 64, 96
+    x = I.bf16_normal(rng, (R, C))
+    sr = orc.quantize_sr(x, R, C, seed=42, row=True, col=True)
+    rn = orc.quantize(x, R, C, orc.E2M1, orc.FLOOR, row=True, col=True)
+    assert np.array_equal(sr["row_scales"], rn["row_scales"]) and np.array_equal(sr["col_scales"], rn["col_scales"])
+    codes = orc.unpack_codes(sr["row_codes"], orc.E2M1, C)
+    xf = I.bf16_bits_to_f32(x).astype(np.float64)
+    moved = 0
+    for r in range(R):
+        for k in range(C):
+            X = int(sr["row_scales"][r, k // 32]) - 127
+            v = math.ldexp(xf[r, k], -X)
+            want = orc.encode_e2m1_sr(v, orc.sr_word(42, 0, r * C + k))
+            assert codes[r, k] == want
+            moved += want != orc.encode(orc.E2M1, v)
+            grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+            lo = max(g for g in grid if g <= min(abs(v), 6))
+            hi = min(g for g in grid if g >= min(abs(v), 6))
+            assert abs(orc.decode(orc.E2M1, want)) in (lo, hi)
+    assert 0 < moved < R * C  # some elements round away from the nearest code, not all
+    ccodes = orc.unpack_codes(sr["col_codes"], orc.E2M1, R)
+    for c in range(0, C, 7):
+        for r in range(R):
+            X = int(sr["col_scales"][c, r // 32]) - 127
+            assert ccodes[c, r] == orc.encode_e2m1_sr(math.ldexp(xf[r, c], -X), orc.sr_word(42, 1, c * R + r))
+    again = orc.quantize_sr(x, R, C, seed=42, row=True)
+    other = orc.quantize_sr(x, R, C, seed=43, row=True)
+    assert np.array_equal(again["row_codes"], sr["row_codes"])
+    assert not np.array_equal(other["row_codes"], sr["row_codes"])
