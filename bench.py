@@ -391,16 +391,32 @@ def bench_main_grad(mx, T):
             "accumulate_tflops": fl / (accum * 1e-6) / 1e12}
 
 
+def bench_sr_pack(mx, T):
+    """MXFP4 gradient pack (dY of the out-projection at M = 16384, [16384,
+    3072], row + column) with stochastic rounding against nearest rounding,
+    device time per launch."""
+    from microscaling_block_scaled_mx_amd import inputs as I
+    R, C = 16384, 3072
+    x = dev(I.bf16_normal(np.random.default_rng(11), (R, C)))
+    row, col = mx.alloc_packed(R, C, mx.E2M1), mx.alloc_packed(C, R, mx.E2M1)
+    rn = graph_time(lambda r: mx.quantize(x, R, C, mx.E2M1, mx.FLOOR, row=row, col=col))
+    sr = graph_time(lambda r: mx.quantize_sr(x, R, C, 1234 + r, row=row, col=col))
+    b = R * C * (2 + 2 * PACK_OUT[4])
+    return {"workload": "MXFP4 dual pack of dY [16384,3072]: stochastic vs nearest rounding",
+            "nearest_us": rn, "sr_us": sr, "nearest_gbs": b / (rn * 1e-6) / 1e9, "sr_gbs": b / (sr * 1e-6) / 1e9}
+
+
 def only(mx, spec, steps, warmup, T):
     """One kernel configuration, for profilers: gemm:FMT:M:N:K, pack:FMT:R:C
     (dual pack), packs:FMT:M:N:K (the linear step's fused dual packs of X,
     W and dY), gemms:FMT:M:N:K (its three GEMMs in one launch; random
     codes) or copy:BYTES; or one whole other workload: linear256, mlp,
-    sweep, grouped or main_grad.  Prints one JSON line with its average time."""
+    sweep, grouped, main_grad or sr_pack.  Prints one JSON line with its
+    average time."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     workloads = {"linear256": bench_cfg1, "mlp": bench_cfg3, "sweep": bench_cfg4, "grouped": bench_cfg5,
-                 "main_grad": bench_main_grad}
+                 "main_grad": bench_main_grad, "sr_pack": bench_sr_pack}
     if spec in workloads:  # one of the other workloads, as in the full run
         print(json.dumps({"only": spec, **workloads[spec](mx, T)}), flush=True)
         return
@@ -467,7 +483,7 @@ def main():
                     help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C, packs:FMT:M:N:K, "
                          "gemms:FMT:M:N:K "
                          "(FMT = 4, 6 or 8), copy:BYTES (a plain device copy), or one workload: "
-                         "linear256, mlp, sweep, grouped, main_grad")
+                         "linear256, mlp, sweep, grouped, main_grad, sr_pack")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
@@ -530,7 +546,8 @@ def main():
     if args.extra == "all":
         extra = {}
         for name, fn in (("mxfp4_256", bench_cfg1), ("fused_mlp_mxfp6", bench_cfg3), ("mxfp4_flux_sweep", bench_cfg4),
-                         ("grouped_mxfp8", bench_cfg5), ("wgrad_main_grad", bench_main_grad)):
+                         ("grouped_mxfp8", bench_cfg5), ("wgrad_main_grad", bench_main_grad),
+                         ("mxfp4_sr_pack", bench_sr_pack)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = fn(mx, T)
             torch.cuda.empty_cache()

@@ -160,6 +160,27 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
                 void* stream);
 
 /*
+ * mx_quantize_sr -- mx_quantize for MXFP4 gradient packs with stochastic
+ * rounding of the elements ([P3] Overview, configuration table: SR of the
+ * FP4 gradient quantization, an optional switch).  Format E2M1, FLOOR
+ * scales, no rotation, identity prologue; arguments, layouts and errors as
+ * mx_quantize with those fixed.
+ *
+ * The scales are those of mx_quantize.  For an element with v = x / 2^X:
+ * |v| >= 6 saturates to 6; otherwise, with grid neighbours lo <= |v| < hi
+ * and t = (|v| - lo) / (hi - lo), the magnitude is hi iff
+ * (r >> 8) < floor(t * 2^24), else lo; the sign is kept.  r is word i % 4 of
+ * Philox4x32-10 (Salmon et al., SC 2011) at counter (i/4 mod 2^32,
+ * i/4 div 2^32, axis, 0) with key (seed mod 2^32, seed div 2^32), where i is
+ * the element's index in its packed operand, i = (batch entry * rows +
+ * operand row) * K + k, and axis is 0 for the rowwise operand and 1 for the
+ * columnwise one.  The same seed gives the same bytes on every run.
+ */
+int mx_quantize_sr(const void* x, int64_t batch, int64_t R, int64_t C, void* row_codes, void* row_scales,
+                   void* col_codes, void* col_scales, float* colsum_partials, float* colsum, uint64_t seed,
+                   void* stream);
+
+/*
  * mx_quantize_many -- several packs of one format, scale mode, rotation and
  * prologue in a single launch, with the results of n mx_quantize calls made
  * with each item's arguments.  For callers that pack several tensors at

@@ -109,6 +109,7 @@ int quantize_launch(const void* x, const void* aux, int64_t batch, int64_t R, in
   p.col_codes = static_cast<uint8_t*>(cc);
   p.col_scales = static_cast<uint8_t*>(cs);
   p.partials = part;
+  p.sr_seed = 0;
   int st = launched(mx::launch_pack(p, fmt, mode, had, pro, batch, s));
   if (st != MX_OK) return st;
   if (sum) st = launched(mx::launch_colsum_finish(part, R / 32, C, sum, batch, s));
@@ -170,6 +171,31 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
   if ((st = check_device()) != MX_OK) return st;
   return quantize_launch(x, aux, batch, R, C, fmt, scale_mode, hadamard, prologue, row_codes, row_scales,
                          col_codes, col_scales, colsum_partials, colsum, static_cast<hipStream_t>(stream));
+}
+
+int mx_quantize_sr(const void* x, int64_t batch, int64_t R, int64_t C, void* row_codes, void* row_scales,
+                   void* col_codes, void* col_scales, float* colsum_partials, float* colsum, uint64_t seed,
+                   void* stream) {
+  int st = validate_quantize(x, nullptr, batch, R, C, MX_E2M1, MX_SCALE_FLOOR, 0, MX_PRO_IDENTITY, row_codes,
+                             row_scales, col_codes, col_scales, colsum_partials, colsum);
+  if (st != MX_OK) return st;
+  if ((st = check_device()) != MX_OK) return st;
+  if (R == 0 || C == 0) return MX_OK;
+  PackParams p;
+  memset(&p, 0, sizeof p);
+  p.x = static_cast<const uint16_t*>(x);
+  p.R = R;
+  p.C = C;
+  p.row_codes = static_cast<uint8_t*>(row_codes);
+  p.row_scales = static_cast<uint8_t*>(row_scales);
+  p.col_codes = static_cast<uint8_t*>(col_codes);
+  p.col_scales = static_cast<uint8_t*>(col_scales);
+  p.partials = colsum_partials;
+  p.sr_seed = seed;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launched(mx::launch_pack_sr(p, batch, s))) != MX_OK) return st;
+  if (colsum) st = launched(mx::launch_colsum_finish(colsum_partials, R / 32, C, colsum, batch, s));
+  return st;
 }
 
 int mx_quantize_many(const mx_quantize_item* items, int n, int fmt, int scale_mode, int hadamard, int prologue,

@@ -258,6 +258,92 @@ __device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* g, int blk,
   *scale = (uint8_t)s;
 }
 
+// ------------------------------------------------------------------ stochastic rounding (E2M1)
+// MXFP4 gradient packs may round stochastically ([P3] Overview, configuration
+// table: SR of the FP4 gradient quantization).  The random word of element
+// i of a packed operand is word i % 4 of Philox4x32-10 (Salmon, Moraes,
+// Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011)
+// at counter (i/4 low, i/4 high, axis, 0), key (seed low, seed high); axis
+// 0 = rowwise operand, 1 = columnwise.  One round multiplies counter words 0
+// and 2 by 0xD2511F53 and 0xCD9E8D57 (full 64-bit products) and recombines
+// them with words 1, 3 and the key; the key advances by 0x9E3779B9 and
+// 0xBB67AE85 between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// E2M1 code of v = x / 2^X (exact) rounded stochastically with the random
+// word r: |v| >= 6 saturates; otherwise, with grid neighbours lo <= |v| < hi
+// (spacing 0.5 below 2, 1 below 4, else 2) and t = (|v| - lo) / (hi - lo),
+// the magnitude is hi iff (r >> 8) < floor(t * 2^24).  Every step is exact
+// in binary32.  The sign is kept (-0 included).
+__device__ __forceinline__ uint32_t e2m1_sr_code(float v, uint32_t r) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = __builtin_fabsf(v);
+  uint32_t clo;
+  float lo, inv;
+  if (a < 2.0f) {
+    const float f = __builtin_floorf(a * 2.0f);
+    clo = (uint32_t)f;
+    lo = f * 0.5f;
+    inv = 2.0f;
+  } else if (a < 4.0f) {
+    const float f = __builtin_floorf(a);
+    clo = 2u + (uint32_t)f;
+    lo = f;
+    inv = 1.0f;
+  } else {
+    clo = 6u;
+    lo = 4.0f;
+    inv = 0.5f;
+  }
+  const uint32_t k = (uint32_t)(((a - lo) * inv) * 16777216.0f);
+  const uint32_t c = a >= 6.0f ? 7u : clo + ((r >> 8) < k ? 1u : 0u);
+  return sign | c;
+}
+
+// One E2M1 block with stochastic rounding: the FLOOR scale of nearest
+// packing, codes by e2m1_sr_code with the words of elements i0 .. i0 + 31
+// (i0 a multiple of 32).  A NaN/Inf block gets zero codes.
+__device__ __forceinline__ void quant_store_sr(const float (&v)[32], uint8_t* g, int blk, int64_t row,
+                                               uint8_t* scale, uint64_t seed, uint32_t axis, uint64_t i0) {
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+    amax = amax > b ? amax : b;
+  }
+  const uint32_t s = scale_byte<kE2M1, kFloor>(amax);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (s != 0xffu) {
+    const int nx = 127 - (int)s;  // -X
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t q = (i0 >> 2) + (uint64_t)j;
+      uint32_t c[4] = {(uint32_t)q, (uint32_t)(q >> 32), axis, 0u};
+      philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int el = 4 * j + e;
+        w[el / 8] |= e2m1_sr_code(__builtin_ldexpf(v[el], nx), c[e]) << (4 * (el % 8));
+      }
+    }
+  }
+  store_block<kE2M1>(g, blk, row, w);
+  *scale = (uint8_t)s;
+}
+
 // ------------------------------------------------------------------ prologue math
 // Own exp (binary32), the library's contract: Cody-Waite reduction
 // n = rint(x * LOG2E), r = (x - n*LN2_HI) - n*LN2_LO with LN2_HI = ln 2 cut

@@ -46,6 +46,7 @@ struct PackParams {
   uint8_t* col_codes;   // K-group-major codes, rows C, K = R, or nullptr
   uint8_t* col_scales;  // blocked layout, rows C, K = R
   float* partials;      // [R/32][C] or nullptr
+  uint64_t sr_seed;     // stochastic-rounding kernels only: Philox key
 };
 
 // Up to kPackManyMax tensors packed in one launch: item i owns workgroups
@@ -61,6 +62,8 @@ bool pack_supported(int fmt, int mode, int had, int pro);
 hipError_t launch_pack(const PackParams& p, int fmt, int mode, int had, int pro, int64_t batch,
                        hipStream_t stream);
 hipError_t launch_pack_many(const PackMany& m, int fmt, int mode, int had, int pro, hipStream_t stream);
+// MXFP4 (E2M1, FLOOR, no rotation, identity prologue) with stochastic rounding
+hipError_t launch_pack_sr(const PackParams& p, int64_t batch, hipStream_t stream);
 hipError_t launch_colsum_finish(const float* partials, int64_t nb, int64_t C, float* out, int64_t batch,
                                 hipStream_t stream);
 

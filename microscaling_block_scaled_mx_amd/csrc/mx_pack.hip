@@ -122,9 +122,10 @@ __device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<
 
 // One workgroup packs one 128 x 128 tile (column tile bx, row tile by) of
 // batch entry z.
-template <int FMT, int MODE, int HAD, int PRO>
+template <int FMT, int MODE, int HAD, int PRO, int SR = 0>
 __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64_t by, int64_t z,
                                           uint8_t* tile) {
+  static_assert(!SR || (FMT == kE2M1 && MODE == kFloor && !HAD), "stochastic rounding: MXFP4 only");
   constexpr int B = FmtTraits<FMT>::kBits;
   const int t = threadIdx.x;
   const int64_t r0 = by * kTileR, c0 = bx * kTileC;
@@ -170,7 +171,10 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
         if (c < p.C) {
           float v[32];
           lds_row_block(tile + lds_row(row), 0, 0, blk * 32, v);
-          quant_store<FMT, MODE, HAD>(v, group, blk, r, scales);
+          if constexpr (SR)
+            quant_store_sr(v, group, blk, r, scales, p.sr_seed, 0u, (uint64_t)((z * p.R + r) * p.C + c));
+          else
+            quant_store<FMT, MODE, HAD>(v, group, blk, r, scales);
         } else {
           // pad block of the row's last K group (a tile spans one group)
           *scales = 0;
@@ -203,7 +207,10 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
           if (p.col_codes) {
             uint8_t* group = p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B);
             uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
-            quant_store<FMT, MODE, HAD>(v, group, blk, c, scales);
+            if constexpr (SR)
+              quant_store_sr(v, group, blk, c, scales, p.sr_seed, 1u, (uint64_t)((z * p.C + c) * p.R + r));
+            else
+              quant_store<FMT, MODE, HAD>(v, group, blk, c, scales);
           }
         } else if (p.col_codes) {
           // a 128-row tile spans one K group; blocks past R are pad
@@ -215,10 +222,10 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
   }
 }
 
-template <int FMT, int MODE, int HAD, int PRO>
+template <int FMT, int MODE, int HAD, int PRO, int SR = 0>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
-  pack_tile<FMT, MODE, HAD, PRO>(p, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+  pack_tile<FMT, MODE, HAD, PRO, SR>(p, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
 // Several tensors in one launch: workgroup w packs tile w - first[i] of
@@ -305,6 +312,12 @@ hipError_t launch_pack_many(const PackMany& m, int fmt, int mode, int had, int p
   const int64_t tiles = m.first[m.n];
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_sr(const PackParams& p, int64_t batch, hipStream_t stream) {
+  dim3 grid((unsigned)((p.C + kTileC - 1) / kTileC), (unsigned)((p.R + kTileR - 1) / kTileR), (unsigned)batch);
+  hipLaunchKernelGGL((pack_kernel<kE2M1, kFloor, 0, kIdentity, 1>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -96,6 +96,8 @@ def lib():
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.mx_quantize.restype = ci
         L.mx_quantize.argtypes = [vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.mx_quantize_sr.restype = ci
+        L.mx_quantize_sr.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
         L.mx_quantize_many.restype = ci
         L.mx_quantize_many.argtypes = [ctypes.POINTER(QuantizeItem), ci, ci, ci, ci, ci, vp]
         L.mx_gemm_many.restype = ci
@@ -202,6 +204,21 @@ def quantize(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = Fals
                            _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
                            _ptr(colsum_partials), _ptr(colsum), _stream(stream))
     _check(st, "mx_quantize")
+
+
+def quantize_sr(x, R: int, C: int, seed: int, row=None, col=None, colsum_partials=None, colsum=None,
+                batch: int = 1, stream=None):
+    """mx_quantize_sr: MXFP4 pack with stochastic rounding; row=(codes,
+    scales) [R] x K=C, col=(codes, scales) [C] x K=R."""
+    _need(x, 2 * batch * R * C, "quantize_sr input")
+    _need_packed(row, R, C, E2M1, "quantize_sr row", batch)
+    _need_packed(col, C, R, E2M1, "quantize_sr col", batch)
+    _need(colsum_partials, 4 * batch * (R // 32) * C, "colsum partials")
+    _need(colsum, 4 * batch * C, "colsum")
+    st = lib().mx_quantize_sr(_ptr(x), batch, R, C, _ptr(row[0]) if row else None, _ptr(row[1]) if row else None,
+                              _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
+                              _ptr(colsum_partials), _ptr(colsum), seed & 0xFFFFFFFFFFFFFFFF, _stream(stream))
+    _check(st, "mx_quantize_sr")
 
 
 def quantize_many(items, fmt, scale_mode, hadamard=False, prologue=PRO_IDENTITY, stream=None):

@@ -606,3 +606,65 @@ def test_fused_mlp_bwd_accumulates_weight_gradients(mxl):
     assert not torch.equal(t["dW1"], first["dW1"])
     for k in ("dX", "da", "db1"):
         assert torch.equal(t[k], first[k]), k
+
+
+# ------------------------------------------------------------------ MXFP4 stochastic rounding
+def test_quantize_sr_parity(mxl, orc):
+    # every packed byte and scale against the oracle's SR pack (two batch
+    # entries, ragged tile tails, special blocks); column sums as the
+    # nearest-rounding pack's
+    rng = np.random.default_rng(800)
+    R, C, B = 352, 416, 2
+    xs = [with_specials(I.bf16_normal(rng, (R, C)), rng) for _ in range(B)]
+    x = np.stack(xs)
+    seed = 0xDEADBEEF12345678
+    rowp = (torch.full(tiled_shape(R, C, 4, B), 0xA5, dtype=torch.uint8, device="cuda"),
+            torch.full(blocked_shape(R, C, B), 0xA5, dtype=torch.uint8, device="cuda"))
+    colp = (torch.full(tiled_shape(C, R, 4, B), 0xA5, dtype=torch.uint8, device="cuda"),
+            torch.full(blocked_shape(C, R, B), 0xA5, dtype=torch.uint8, device="cuda"))
+    part = torch.zeros((B, R // 32, C), dtype=torch.float32, device="cuda")
+    sums = torch.zeros((B, C), dtype=torch.float32, device="cuda")
+    mxl.quantize_sr(dev(x), R, C, seed, row=rowp, col=colp, colsum_partials=part, colsum=sums, batch=B)
+    rc, rs = untiled(host(rowp[0]), C, 4), unblocked(host(rowp[1]), C // 32)
+    cc, cs = untiled(host(colp[0]), R, 4), unblocked(host(colp[1]), R // 32)
+    for z in range(B):
+        want = orc.quantize_sr(xs[z], R, C, seed, row=True, col=True, index_base=z * R * C)
+        assert_packs_equal(dict(row_codes=rc[z], row_scales=rs[z], col_codes=cc[z], col_scales=cs[z]), want, 1,
+                           ("row_codes", "row_scales", "col_codes", "col_scales"))
+        rn = orc.quantize(xs[z], R, C, 1, 0, row=False, col=False, colsum=True)
+        assert_f32_bitwise(host(part)[z], rn["colsum_partials"])
+        assert_f32_bitwise(host(sums)[z], rn["colsum"])
+
+
+def test_quantize_sr_seed_determinism(mxl):
+    rng = np.random.default_rng(801)
+    R, C = 256, 512
+    x = dev(I.bf16_normal(rng, (R, C)))
+    outs = []
+    for seed in (7, 7, 8):
+        p = mxl.alloc_packed(R, C, 1)
+        mxl.quantize_sr(x, R, C, seed, row=p)
+        outs.append(p)
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert not torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+
+
+def test_quantize_sr_full_size_sampled(mxl, orc):
+    # the MXFP4 sweep's gradient shape dY [16384, 3072] (out-projection),
+    # dual pack with SR: 32-row and 32-column slices at sampled places
+    # against the oracle (the element index of a slice starts at its offset)
+    R, C = 16384, 3072
+    rng = np.random.default_rng(802)
+    x = I.bf16_normal(rng, (R, C))
+    seed = 2024
+    row, col = mxl.alloc_packed(R, C, 1), mxl.alloc_packed(C, R, 1)
+    mxl.quantize_sr(dev(x), R, C, seed, row=row, col=col)
+    rc, rs = untiled(host(row[0]), C, 4), unblocked(host(row[1]), C // 32)
+    cc, cs = untiled(host(col[0]), R, 4), unblocked(host(col[1]), R // 32)
+    for r0 in (0, 32 * int(rng.integers(1, R // 32 - 1)), R - 32):
+        want = orc.quantize_sr(np.ascontiguousarray(x[r0:r0 + 32]), 32, C, seed, row=True, index_base=r0 * C)
+        assert np.array_equal(rc[r0:r0 + 32], want["row_codes"]) and np.array_equal(rs[r0:r0 + 32], want["row_scales"])
+    for c0 in (0, 32 * int(rng.integers(1, C // 32 - 1)), C - 32):
+        want = orc.quantize_sr(np.ascontiguousarray(x[:, c0:c0 + 32]), R, 32, seed, row=False, col=True,
+                               index_base=c0 * R)
+        assert np.array_equal(cc[c0:c0 + 32], want["col_codes"]) and np.array_equal(cs[c0:c0 + 32], want["col_scales"])
