@@ -428,13 +428,15 @@ def test_fused_mlp_zero_output_projection(mxl):
 
 
 # ------------------------------------------------------------------ grouped
-def run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=3, mode=1):
+def run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=3, mode=1, poison=None):
     P = lambda r, k, b=None: mxl.alloc_packed(r, k, fmt, batch=b)
     off = dev(offsets.astype(np.int32))
+    out16 = (lambda *s: bf16_empty(*s)) if poison is None else \
+        (lambda *s: torch.full(s, poison, dtype=torch.int16, device="cuda"))
     t = dict(Xr=P(R, D), Xc=P(D, R), W1r=P(2 * F, D, G), W1c=P(D, 2 * F, G), W2r=P(D, F, G), W2c=P(F, D, G),
-             H=bf16_empty(R, 2 * F), zr=P(R, F), zc=P(F, R), Y=bf16_empty(R, D), dYr=P(R, D), dYc=P(D, R),
-             dz=bf16_empty(R, F), dHr=P(R, 2 * F), dHc=P(2 * F, R), dX=bf16_empty(R, D),
-             dW1=bf16_empty(G, 2 * F, D), dW2=bf16_empty(G, D, F))
+             H=out16(R, 2 * F), zr=P(R, F), zc=P(F, R), Y=out16(R, D), dYr=P(R, D), dYc=P(D, R),
+             dz=out16(R, F), dHr=P(R, 2 * F), dHc=P(2 * F, R), dX=out16(R, D),
+             dW1=out16(G, 2 * F, D), dW2=out16(G, D, F))
     Xd, W1d, W2d, dYd = dev(X), dev(W1), dev(W2), dev(dY)
     mxl.quantize(Xd, R, D, fmt, mode, row=t["Xr"], col=t["Xc"])
     mxl.quantize(W1d, 2 * F, D, fmt, mode, row=t["W1r"], col=t["W1c"], batch=G)
@@ -668,3 +670,42 @@ def test_quantize_sr_full_size_sampled(mxl, orc):
         want = orc.quantize_sr(np.ascontiguousarray(x[:, c0:c0 + 32]), R, 32, seed, row=False, col=True,
                                index_base=c0 * R)
         assert np.array_equal(cc[c0:c0 + 32], want["col_codes"]) and np.array_equal(cs[c0:c0 + 32], want["col_scales"])
+
+
+def test_grouped_256_aligned_with_inactive_tail(mxl, orc):
+    # per-expert counts in multiples of 256 (the alignment another stack on
+    # the pages requires; here a special case of the 128-row contract, every
+    # tile full), one empty expert, and offsets[-1] < R: tail rows of X and
+    # dY are NaN / Inf poisoned, so the columnwise packs carry 0xFF scale
+    # bytes past the last offset.  The whole chain matches the oracle on the
+    # active rows, and no output row past offsets[-1] is written.
+    fmt, mode = 3, 1
+    R, D, F, G = 2048, 256, 256, 4
+    counts = np.array([512, 0, 768, 256])
+    offsets = np.cumsum(counts).astype(np.int32)  # last end 1536 < R
+    rng = np.random.default_rng(900)
+    X, dY = I.bf16_normal(rng, (R, D)), I.bf16_normal(rng, (R, D))
+    W1, W2 = I.bf16_normal(rng, (G, 2 * F, D), 0.02), I.bf16_normal(rng, (G, D, F), 0.02)
+    A = int(offsets[-1])
+    X[A:] = 0x7FC0
+    dY[A:] = 0x7F80
+    t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=fmt, mode=mode, poison=0x1234)
+    assert np.all(unblocked(host(t["Xc"][1]), R // 32)[:, A // 32:] == 0xFF)  # the poisoned colwise tail
+    H, dz = host(t["H"]), host(t["dz"])
+    for k in ("H", "Y", "dz", "dX"):
+        v = host(t[k])
+        assert np.all(v[A:] == 0x1234), k
+        assert not np.any(v[:A] == 0x1234), k
+    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H, fmt=fmt, mode=mode)
+    assert bf16_close(H[:A], fwd["H64"])
+    assert bf16_close(host(t["Y"])[:A], fwd["Y64"])
+    bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=dz, H_in=H)
+    assert bf16_close(dz[:A], bwd["dz64"])
+    assert bf16_close(host(t["dX"])[:A], bwd["dX64"])
+    dW1, dW2 = host(t["dW1"]), host(t["dW2"])
+    assert not np.any(dW1[1]) and not np.any(dW2[1])  # the empty expert's gradients: zeros written
+    assert bf16_close(dW1, bwd["dW1_64"]) and bf16_close(dW2, bwd["dW2_64"])
+    # packed outputs of the epilogues: tail rows untouched (left as allocated
+    # bytes is not checkable), active rows as the oracle
+    assert np.array_equal(untiled(host(t["zr"][0]), F, 8)[:A], fwd["z"]["row_codes"])
+    assert np.array_equal(untiled(host(t["dHr"][0]), 2 * F, 8)[:A], bwd["dH"]["row_codes"])
