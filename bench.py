@@ -44,9 +44,9 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # (scaled by what they read for a plain copy), valid while the kernel
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "ef27be76101b9ce922fac3c4d0dfb8245a78263a"}
+                "sources_sha1": "55ac4bc5daf5a029edb9875ccb3add0ed2e59e5e"}
 PACK_TRAFFIC = {"bytes_per_launch": 123.6e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "f691e4c7e40566e0e5bced1b3448250272ffd74f"}
+                "sources_sha1": "dde48af630ba02db69ba3dc2e61797b9417ddf4c"}
 
 
 def measured_traffic(rec):

@@ -242,15 +242,36 @@ __global__ __launch_bounds__(256) void pack_many_kernel(PackMany m) {
   pack_tile<FMT, MODE, HAD, PRO>(m.p[i], local % tx, (local / tx) % ty, local / (tx * ty), tile);
 }
 
-// db[c] = sum over blocks b (increasing) of partials[b][c], from +0.
-__global__ __launch_bounds__(256) void colsum_finish_kernel(const float* partials, int64_t nb, int64_t C,
-                                                            float* out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// db[c] = sum over blocks b (increasing) of partials[b][c], from +0.  One
+// thread per column (64-thread workgroups, so that a few thousand columns
+// still spread over the compute units).  The additions stay one sequential
+// chain per column; the loads run ahead of it in batches of 32, the next
+// batch in flight while the current one is added (a batch past the end
+// re-loads the last one, so no load sits under a branch).
+constexpr int kColsumThreads = 64;
+__global__ __launch_bounds__(kColsumThreads) void colsum_finish_kernel(const float* partials, int64_t nb,
+                                                                       int64_t C, float* out) {
+  const int64_t c = (int64_t)blockIdx.x * kColsumThreads + threadIdx.x;
   const int64_t z = blockIdx.y;
   if (c >= C) return;
-  const float* src = partials + z * nb * C;
+  const float* src = partials + z * nb * C + c;
+  const int64_t full = nb / 32;  // whole batches
   float s = 0.0f;
-  for (int64_t b = 0; b < nb; ++b) s = s + src[b * C + c];
+  if (full > 0) {
+    float cur[32], nxt[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cur[i] = src[(int64_t)i * C];
+    for (int64_t b = 0; b < full; ++b) {
+      const int64_t nb0 = 32 * (b + 1 < full ? b + 1 : b);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) nxt[i] = src[(nb0 + i) * C];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s = s + cur[i];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) cur[i] = nxt[i];
+    }
+  }
+  for (int64_t b = 32 * full; b < nb; ++b) s = s + src[b * C];
   out[z * C + c] = s;
 }
 
@@ -323,8 +344,8 @@ hipError_t launch_pack_sr(const PackParams& p, int64_t batch, hipStream_t stream
 
 hipError_t launch_colsum_finish(const float* partials, int64_t nb, int64_t C, float* out, int64_t batch,
                                 hipStream_t stream) {
-  dim3 grid((unsigned)((C + 255) / 256), (unsigned)batch);
-  hipLaunchKernelGGL(colsum_finish_kernel, grid, dim3(256), 0, stream, partials, nb, C, out);
+  dim3 grid((unsigned)((C + kColsumThreads - 1) / kColsumThreads), (unsigned)batch);
+  hipLaunchKernelGGL(colsum_finish_kernel, grid, dim3(kColsumThreads), 0, stream, partials, nb, C, out);
   return hipGetLastError();
 }
 
