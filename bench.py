@@ -45,6 +45,13 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
                 "sources_sha1": "55ac4bc5daf5a029edb9875ccb3add0ed2e59e5e"}
+# VALU wavefront-instructions per launch of the fused pack (rocprofv3
+# SQ_INSTS_VALU), valid while the pack sources are those it was counted with
+PACK_VALU = {"instructions_per_launch": 1.180e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
+             "sources_sha1": "dde48af630ba02db69ba3dc2e61797b9417ddf4c"}
+# peak VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per 4
+# cycles on a 16-lane SIMD (G wavefront-instructions per second)
+VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
 PACK_TRAFFIC = {"bytes_per_launch": 123.6e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
                 "sources_sha1": "dde48af630ba02db69ba3dc2e61797b9417ddf4c"}
 
@@ -56,13 +63,27 @@ def measured_traffic(rec):
     for f in rec["sources"]:
         with open(os.path.join(ROOT, "microscaling_block_scaled_mx_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha1"] else None
+    key = "bytes_per_launch" if "bytes_per_launch" in rec else "instructions_per_launch"
+    return rec[key] if h.hexdigest() == rec["sources_sha1"] else None
 
 
 PEAK_TFLOPS = {"fp4": 10100.0, "fp6": 10100.0, "fp8": 5000.0}  # MI355X dense MFMA
 HBM_GBS = 8000.0
 # algorithmic bytes per element of a pack: 2 B bf16 in + (bits/8 + 1/32) per output axis
 PACK_OUT = {4: 0.5 + 1 / 32, 6: 0.75 + 1 / 32, 8: 1.0 + 1 / 32}
+
+
+def alu_roofline(pack_us):
+    """The fused pack against its bound, VALU issue: the counted VALU
+    wavefront-instructions per launch over the launch time, against the
+    chip's issue peak.  None when the pack sources changed since the count."""
+    n = measured_traffic(PACK_VALU)
+    if n is None:
+        return None
+    achieved = n / (pack_us * 1e-6) / 1e9
+    return {"bound": "alu", "achieved": round(achieved, 1), "peak": VALU_PEAK_GIPS,
+            "unit": "G wavefront-instructions/s", "frac": round(achieved / VALU_PEAK_GIPS, 4),
+            "valu_instructions_per_launch": n}
 
 
 def dev(a):
@@ -537,7 +558,8 @@ def main():
         "quantizer": {"kernel": "pack_many_kernel<E2M3, Hadamard>: dual packs of X, W and dY in one launch",
                       "achieved_gbs": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
                       "frac": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9 / HBM_GBS, 4),
-                      "algorithmic_bytes": pack_bytes, "traffic": measured_traffic(PACK_TRAFFIC)},
+                      "algorithmic_bytes": pack_bytes, "traffic": measured_traffic(PACK_TRAFFIC),
+                      "alu": alu_roofline(k["pack_XWdY"])},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
