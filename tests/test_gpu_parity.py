@@ -709,3 +709,25 @@ def test_grouped_256_aligned_with_inactive_tail(mxl, orc):
     # bytes is not checkable), active rows as the oracle
     assert np.array_equal(untiled(host(t["zr"][0]), F, 8)[:A], fwd["z"]["row_codes"])
     assert np.array_equal(untiled(host(t["dHr"][0]), 2 * F, 8)[:A], bwd["dH"]["row_codes"])
+
+
+def test_grouped_two_stream_schedule_matches_one_stream(mxl):
+    # the grouped step bench.py times runs independent launches on a second
+    # stream; every output must equal the one-stream schedule's bit for bit
+    import bench
+    R, D, F, G = 2048, 256, 256, 4
+    counts, offsets, X, W1, W2, dY = I.grouped_mlp(503, R, D, F, G, zero_expert=1)
+    fmt, mode = 3, 1
+    a = bench.grouped_buffers(mxl, R, D, F, G, X, W1, W2, dY, offsets, fmt)
+    b = bench.grouped_buffers(mxl, R, D, F, G, X, W1, W2, dY, offsets, fmt)
+    bench.grouped_step(mxl, a, R, D, F, G, fmt, mode)
+    side = torch.cuda.Stream()
+    for _ in range(2):
+        bench.grouped_step(mxl, b, R, D, F, G, fmt, mode, side=side)
+    torch.cuda.synchronize()
+    for k in ("H", "Y", "dX", "dW1", "dW2", "zr", "zc", "dHr", "dHc", "Xc", "dYc"):
+        va, vb = a[k], b[k]
+        if isinstance(va, tuple):
+            assert torch.equal(va[0], vb[0]) and torch.equal(va[1], vb[1]), k
+        else:
+            assert torch.equal(va, vb), k
