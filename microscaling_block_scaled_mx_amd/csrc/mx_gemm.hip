@@ -17,7 +17,9 @@
 //
 // Tiling.  256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN output
 // tile; a wavefront owns (BM/2) x (BN/2) = (BM/64) x (BN/64) MFMA tiles of
-// 32 x 32, whose accumulators live in AGPRs (one wavefront per SIMD).  K
+// 32 x 32, whose accumulators live in AGPRs (one wavefront per SIMD).
+// 256 x 256 tiles instead run 512 threads = 8 wavefronts in a 2 x 4 grid
+// (128 x 64 each, two per SIMD).  K
 // advances BK elements per stage (128 for E2M1/E2M3, 64 for E4M3), in steps
 // of 64 (one MFMA per output tile).  Stages form a ring of S = 3 or 4
 // buffers in LDS filled by direct global -> LDS loads (global_load_lds:
@@ -64,16 +66,25 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
 
 template <int FMT> struct MfmaFmt;
 template <> struct MfmaFmt<kE4M3> { static constexpr int kCode = 0; };
 template <> struct MfmaFmt<kE2M3> { static constexpr int kCode = 2; };
 template <> struct MfmaFmt<kE2M1> { static constexpr int kCode = 4; };
 
+// Threads per workgroup of a BM x BN tile: 8 wavefronts for 256 x 256, else 4.
+constexpr int tile_threads(int bm, int bn) { return (bm == 256 && bn == 256) ? 512 : 256; }
+
 template <int FMT, int BM, int BN, int MODE, int EPI>
 struct Cfg {
   static constexpr int kBits = FmtTraits<FMT>::kBits;
+  // 256 x 256 tiles run 8 wavefronts (2 per SIMD, 2 x 4 over the tile, 128
+  // accumulator registers each), so that one wavefront's MFMAs can cover
+  // the other's LDS and barrier waits (measured 2-4% faster than 4
+  // wavefronts of 256 accumulators each); the other shapes run 4 (2 x 2)
+  static constexpr int kThreads = tile_threads(BM, BN);
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kWavesN = kWaves / 2;  // wavefronts across N (2 across M)
   // K elements per stage: one 128-element K group (64 / 96 bytes per row)
   // for E2M1 / E2M3, half of one (64 bytes) for E4M3, so that every stage
   // fits a ring of three or four in the LDS
@@ -81,6 +92,7 @@ struct Cfg {
   static constexpr int kRowBytes = kBK * kBits / 8;      // 64 / 96 / 64 bytes per row per stage
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
   static constexpr int kScaleDw = 1;                     // scale dword (4 blocks of 32 along K) per row per stage
+  static constexpr int kSJ = 512 / kThreads;            // scale-dword loads per thread per stage (512 slots)
   // 16-byte loads per thread per stage; a tile side whose chunks do not fill
   // whole loads (192 rows of 96 bytes) leaves the last load of some
   // wavefronts idle: they load a valid chunk into a junk area, so that every
@@ -106,9 +118,10 @@ struct Cfg {
   static constexpr int boff(int b) { return kStages * kARegion + b * kBRegion; }
   static constexpr int soff(int b) { return kStages * (kARegion + kBRegion) + b * kSRegion; }
   static constexpr int kJOff = kStages * kStage;
-  static constexpr int kWM = BM / 2, kWN = BN / 2;
+  static constexpr int kWM = BM / 2, kWN = BN / kWavesN;
+  static_assert(kWN % 32 == 0, "wavefront tile width");
   static constexpr int kMI = kWM / 32, kNJ = kWN / 32;
-  static constexpr int kLoads = kAIters + kBIters + 2 * kScaleDw;  // vector-memory instructions per stage per wave
+  static constexpr int kLoads = kAIters + kBIters + kSJ * kScaleDw;  // vector-memory instructions per stage per wave
   static_assert(BM + BN <= 512, "scale slots");
   // epilogue staging
   static constexpr int kCPitch = kWN * 2 + 8;         // bf16 store: per-wave kWM x kWN tile
@@ -116,7 +129,7 @@ struct Cfg {
   static constexpr int kDPitch = BN * 2 + 8;          // dSwiGLU: two BM x BN tiles
   static constexpr int kEpiBytes = EPI == kEpiSwiglu    ? BM * kZPitch
                                    : EPI == kEpiDSwiglu ? 2 * BM * kDPitch
-                                                        : 4 * kWM * kCPitch;
+                                                        : kWaves * kWM * kCPitch;
   static constexpr int kSmem = (kJOff + kJunk > kEpiBytes) ? kJOff + kJunk : kEpiBytes;
   static_assert(kSmem <= 163840, "LDS budget");
 };
@@ -276,7 +289,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / CF::kWavesN, wn = wave % CF::kWavesN;
+  constexpr int kThreads = CF::kThreads;
   const int lrow = lane & 31, g = lane >> 5;
 
   // ---------------------------------------------------------------- tile
@@ -390,11 +404,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   // scale dwords (4 blocks of 32 along K, blocked layout): slot t and t + 256
   // of [A rows | B rows]; slots past BM + BN load row 0's dword into unused
   // slots, so every wave issues the same number of loads
-  const uint8_t* s_src[2];
-  int64_t s_step[2];  // bytes between consecutive K groups
+  const uint8_t* s_src[CF::kSJ];
+  int64_t s_step[CF::kSJ];  // bytes between consecutive K groups
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = t + 256 * j;
+  for (int j = 0; j < CF::kSJ; ++j) {
+    const int r = t + kThreads * j;
     const bool is_b = r >= BM && r < BM + BN;
     const int64_t ar = MODE == kRaggedM && m0 + (r < BM ? r : 0) >= m_end ? m_end - 1 : m0 + (r < BM ? r : 0);
     s_src[j] = is_b ? p.b_scales + b_soff + (b_row(r - BM) - b_row0) * 4 : p.a_scales + ar * 4;
@@ -415,17 +429,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
       const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
       const bool junk_ = CF::kARem && i_ == CF::kAIters - 1 && wave_u * 64 >= CF::kARem;                 \
       lds_dma16_s(p.a_codes + (k0_ / 128) * a_rows * kGB + (k0_ % 128) * kBits / 8, a_off[i_],          \
-                  st_ + (junk_ ? CF::kJOff : CF::aoff(buf) + (i_ * 256 + wave_u * 64) * 16));            \
+                  st_ + (junk_ ? CF::kJOff : CF::aoff(buf) + (i_ * kThreads + wave_u * 64) * 16));            \
     } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
       const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
       const bool junk_ = CF::kBRem && i_ == CF::kBIters - 1 && wave_u * 64 >= CF::kBRem;                 \
       lds_dma16_s(p.b_codes + (k0_ / 128) * b_rows * kGB + (k0_ % 128) * kBits / 8, b_off[i_],          \
-                  st_ + (junk_ ? CF::kJOff : CF::boff(buf) + (i_ * 256 + wave_u * 64) * 16));            \
+                  st_ + (junk_ ? CF::kJOff : CF::boff(buf) + (i_ * kThreads + wave_u * 64) * 16));            \
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
-      const int d_ = e_ / 2, j_ = e_ % 2;                                                                \
+      const int d_ = e_ / CF::kSJ, j_ = e_ % CF::kSJ;                                                    \
       lds_dma4(s_src[j_] + (k0_ / 128 + d_) * s_step[j_],                                               \
-               st_ + CF::soff(buf) + (d_ * 512 + j_ * 256 + wave_u * 64) * 4);                          \
+               st_ + CF::soff(buf) + (d_ * 512 + j_ * kThreads + wave_u * 64) * 4);                     \
     }                                                                                                    \
   } while (0)
 #define MX_ISSUE(k, buf)                                                                                  \
@@ -932,7 +946,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
 // One launch, one GEMM (or one grouped GEMM): workgroup (x, y, z) computes
 // tile (x, y) of group z.
 template <int FMT, int BM, int BN, int MODE, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(tile_threads(BM, BN), 1) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg<FMT, BM, BN, MODE, EPI>::kSmem];
   gemm_tile<FMT, BM, BN, MODE, EPI>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
@@ -951,9 +965,10 @@ __device__ __forceinline__ void dense_tile_sh(const GemmParams& p, int local, ui
 // Several dense GEMMs in one launch: workgroup w computes tile
 // w - first[i] of GEMM i (first[i] <= w < first[i + 1]) with that GEMM's
 // tile shape, SA or SB (indices into kDenseShapes); the branch is uniform
-// across the workgroup.
+// across the workgroup.  Both shapes run the same number of wavefronts.
 template <int FMT, int SA, int SB>
-__global__ __launch_bounds__(kThreads, 1) void gemm_many_kernel(GemmMany m) {
+__global__ __launch_bounds__(tile_threads(kDenseShapes[SA][0], kDenseShapes[SA][1]), 1) void gemm_many_kernel(GemmMany m) {
+  static_assert(DenseCfg<FMT, SA>::kThreads == DenseCfg<FMT, SB>::kThreads, "one workgroup size per launch");
   constexpr int kA = DenseCfg<FMT, SA>::kSmem, kB = DenseCfg<FMT, SB>::kSmem;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kA > kB ? kA : kB];
   const int w = blockIdx.x;
@@ -980,7 +995,8 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
     grid = dim3((unsigned)(p.N / BN), (unsigned)(p.M / BM), (unsigned)p.G);
   }
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE, EPI>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE, EPI>), grid, dim3(Cfg<FMT, BM, BN, MODE, EPI>::kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -1073,7 +1089,7 @@ hipError_t launch_many_k(GemmMany m, hipStream_t stream) {
   if (!plan_many(m)) return hipErrorInvalidValue;
   const unsigned tiles = (unsigned)m.first[m.n];
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_many_kernel<FMT, SA, SB>), dim3(tiles), dim3(kThreads), 0, stream, m);
+  hipLaunchKernelGGL((gemm_many_kernel<FMT, SA, SB>), dim3(tiles), dim3(DenseCfg<FMT, SA>::kThreads), 0, stream, m);
   return hipGetLastError();
 }
 
