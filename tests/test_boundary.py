@@ -264,3 +264,37 @@ def test_gemm_many_valid_args_need_the_device():
         assert st in (OK, DEVICE)
         if not mx.lib().mx_device_supported(0):
             assert st == DEVICE
+
+
+def qsr(**kw):
+    a = dict(x=P, batch=1, R=64, C=128, rc=P2, rs=P3, cc=P4, cs=P5, part=None, sum=None, seed=1)
+    a.update(kw)
+    return mx.lib().mx_quantize_sr(a["x"], a["batch"], a["R"], a["C"], a["rc"], a["rs"], a["cc"], a["cs"],
+                                   a["part"], a["sum"], a["seed"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(rc=None), NULL), (dict(rc=None, rs=None, cc=None, cs=None), NULL),
+    (dict(sum=P6), NULL),
+    (dict(R=48), SHAPE), (dict(C=40), SHAPE), (dict(batch=0), SHAPE),
+    (dict(x=P + 8), ALIGN), (dict(cs=P5 + 4), ALIGN),
+    (dict(batch=70000), OVERFLOW),
+])
+def test_quantize_sr_rejections(kw, want):
+    assert qsr(**kw) == want
+
+
+def test_quantize_sr_valid_args_need_the_device():
+    for kw in (dict(), dict(seed=2**64 - 1), dict(R=0), dict(cc=None, cs=None, part=P6, sum=P7)):
+        st = qsr(**kw)
+        assert st in (OK, DEVICE), (kw, st)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def test_binding_quantize_sr_rejects_short_buffers():
+    import torch
+    R, C = 64, 128
+    small = (torch.empty(8, dtype=torch.uint8), torch.empty(8, dtype=torch.uint8))
+    with pytest.raises(mx.MXError, match="quantize_sr row"):
+        mx.quantize_sr(torch.empty(R, C, dtype=torch.int16), R, C, 1, row=small)
