@@ -271,13 +271,13 @@ __device__ __forceinline__ void quant_store(float (&v)[32], uint8_t* g, int blk,
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    // one 32 x 32 -> 64-bit product each (both halves from one instruction)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
     c[0] = n0;
-    c[1] = lo1;
+    c[1] = (uint32_t)p1;
     c[2] = n2;
-    c[3] = lo0;
+    c[3] = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -291,23 +291,12 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 __device__ __forceinline__ uint32_t e2m1_sr_code(float v, uint32_t r) {
   const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
   const float a = __builtin_fabsf(v);
-  uint32_t clo;
-  float lo, inv;
-  if (a < 2.0f) {
-    const float f = __builtin_floorf(a * 2.0f);
-    clo = (uint32_t)f;
-    lo = f * 0.5f;
-    inv = 2.0f;
-  } else if (a < 4.0f) {
-    const float f = __builtin_floorf(a);
-    clo = 2u + (uint32_t)f;
-    lo = f;
-    inv = 1.0f;
-  } else {
-    clo = 6u;
-    lo = 4.0f;
-    inv = 0.5f;
-  }
+  // the three spacing regimes as selects, not branches (|v| < 8 here)
+  const bool r1 = a < 2.0f, r2 = a < 4.0f;
+  const float f2 = __builtin_floorf(a * 2.0f), f1 = __builtin_floorf(a);
+  const uint32_t clo = r1 ? (uint32_t)f2 : (r2 ? 2u + (uint32_t)f1 : 6u);
+  const float lo = r1 ? f2 * 0.5f : (r2 ? f1 : 4.0f);
+  const float inv = r1 ? 2.0f : (r2 ? 1.0f : 0.5f);
   const uint32_t k = (uint32_t)(((a - lo) * inv) * 16777216.0f);
   const uint32_t c = a >= 6.0f ? 7u : clo + ((r >> 8) < k ? 1u : 0u);
   return sign | c;
