@@ -44,16 +44,16 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # (scaled by what they read for a plain copy), valid while the kernel
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "55ac4bc5daf5a029edb9875ccb3add0ed2e59e5e"}
+                "sources_sha1": "f79d04009270b8171fbc24837cc685d1bf3c587f"}
 # VALU wavefront-instructions per launch of the fused pack (rocprofv3
 # SQ_INSTS_VALU), valid while the pack sources are those it was counted with
 PACK_VALU = {"instructions_per_launch": 1.180e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-             "sources_sha1": "dde48af630ba02db69ba3dc2e61797b9417ddf4c"}
+             "sources_sha1": "efbd76a8defce0f6f37430d9d6d8d7452acdab6b"}
 # peak VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per 4
 # cycles on a 16-lane SIMD (G wavefront-instructions per second)
 VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
 PACK_TRAFFIC = {"bytes_per_launch": 123.6e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "dde48af630ba02db69ba3dc2e61797b9417ddf4c"}
+                "sources_sha1": "efbd76a8defce0f6f37430d9d6d8d7452acdab6b"}
 
 
 def measured_traffic(rec):
