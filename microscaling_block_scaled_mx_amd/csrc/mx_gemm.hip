@@ -209,9 +209,9 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 #endif
 }
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
+__device__ __forceinline__ void lds_dma4_s(const void* base, uint32_t off, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 #endif
 }
 
@@ -401,17 +401,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     const int c = chunk_at<CF::kChunks>(rr, pos);
     b_off[i] = (uint32_t)(b_coff + (b_row(rr) - b_row0) * kGB + 16 * c);
   }
-  // scale dwords (4 blocks of 32 along K, blocked layout): slot t and t + 256
+  // scale dwords (4 blocks of 32 along K, blocked layout): slot t + kThreads j
   // of [A rows | B rows]; slots past BM + BN load row 0's dword into unused
-  // slots, so every wave issues the same number of loads
-  const uint8_t* s_src[CF::kSJ];
+  // slots, so every wave issues the same number of loads.  BM and BN are
+  // multiples of 64, so a wavefront's 64 slots are all A rows, all B rows or
+  // all unused: each load takes a wavefront-uniform base and K-group stride
+  // (scalar registers) and a fixed per-lane 32-bit offset, and no vector
+  // address arithmetic is left in the main loop.
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale slots of a wavefront are one operand's");
+  const uint8_t* s_base[CF::kSJ];
   int64_t s_step[CF::kSJ];  // bytes between consecutive K groups
+  uint32_t s_off[CF::kSJ];
 #pragma unroll
   for (int j = 0; j < CF::kSJ; ++j) {
     const int r = t + kThreads * j;
-    const bool is_b = r >= BM && r < BM + BN;
+    const int rw = wave_uniform(r);  // the wavefront's first slot
+    const bool is_b = rw >= BM && rw < BM + BN;
     const int64_t ar = MODE == kRaggedM && m0 + (r < BM ? r : 0) >= m_end ? m_end - 1 : m0 + (r < BM ? r : 0);
-    s_src[j] = is_b ? p.b_scales + b_soff + (b_row(r - BM) - b_row0) * 4 : p.a_scales + ar * 4;
+    s_base[j] = is_b ? p.b_scales + b_soff : p.a_scales;
+    s_off[j] = (uint32_t)(is_b ? (b_row(r - BM) - b_row0) * 4 : ar * 4);
     s_step[j] = (is_b ? b_rows : a_rows) * 4;
   }
   const int wave_u = wave_uniform(wave);
@@ -438,7 +446,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
       const int d_ = e_ / CF::kSJ, j_ = e_ % CF::kSJ;                                                    \
-      lds_dma4(s_src[j_] + (k0_ / 128 + d_) * s_step[j_],                                               \
+      lds_dma4_s(s_base[j_] + (k0_ / 128 + d_) * s_step[j_], s_off[j_],                                 \
                st_ + CF::soff(buf) + (d_ * 512 + j_ * kThreads + wave_u * 64) * 4);                     \
     }                                                                                                    \
   } while (0)
