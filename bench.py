@@ -44,7 +44,7 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # (scaled by what they read for a plain copy), valid while the kernel
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "f79d04009270b8171fbc24837cc685d1bf3c587f"}
+                "sources_sha1": "ae15139d47b2709b1d403d0d94aad14eb9d44c66"}
 # VALU wavefront-instructions per launch of the fused pack (rocprofv3
 # SQ_INSTS_VALU), valid while the pack sources are those it was counted with
 PACK_VALU = {"instructions_per_launch": 1.180e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
