@@ -25,7 +25,7 @@ Per-launch
 device durations come from HIP events around replays of a graph of ten
 back-to-back copies of each launch.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--extra all|none] [--no-cpu-baseline] [--no-graph]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--extra all|none] [--no-cpu-baseline] [--no-graph]
 """
 import argparse
 import json
@@ -202,6 +202,9 @@ def capture_steps(step, copies):
     return graphs
 
 
+STEP_STATS = {}  # per-replay step times of the last time_graph_steps call
+
+
 def time_graph_steps(graphs, copies, steps, warmup):
     """Wall time per step of exactly `steps` steps (whole `copies`-step
     graphs, then single-step graphs for the remainder), between two device
@@ -210,19 +213,33 @@ def time_graph_steps(graphs, copies, steps, warmup):
     for i in range(warmup):
         graphs[1 + i % copies].replay()
     torch.cuda.synchronize()
+    n = steps // copies
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     t0 = time.perf_counter()
-    for _ in range(steps // copies):
+    ev[0].record()
+    for i in range(n):
         graphs[0].replay()
+        ev[i + 1].record()
     for i in range(steps % copies):
         graphs[1 + i].replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    sec = (time.perf_counter() - t0) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) / copies for i in range(n)]  # ms per step, per replay
+    STEP_STATS.clear()
+    if per:
+        STEP_STATS.update(median_ms=float(np.median(per)), min_ms=float(np.min(per)), replays=n)
+    return sec
+
+
+LAST_GRAPH_TIMES = {}  # statistics of the last graph_time call (us per launch)
 
 
 def graph_time(launch, reps=10, replays=4, warm=None):
     """Device time of one launch: a graph of `reps` back-to-back calls
-    `launch(r)` (r = 0 .. reps-1) replayed `replays` times between HIP events
-    on the replay stream; the average per call excludes host launch cost.
+    `launch(r)` (r = 0 .. reps-1) replayed `replays` times, a pair of HIP
+    events on the replay stream around each replay; the time per call
+    excludes host launch cost.  Returns the mean over all replays; the
+    median and minimum over replays are left in LAST_GRAPH_TIMES.
     `warm(r)` runs eagerly first (default: `launch`)."""
     import torch
     s = torch.cuda.Stream()
@@ -237,14 +254,20 @@ def graph_time(launch, reps=10, replays=4, warm=None):
             launch(r)
     g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(replays):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for i in range(replays):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * replays)
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / reps for i in range(replays)]
+    LAST_GRAPH_TIMES.clear()
+    LAST_GRAPH_TIMES.update(mean=float(np.mean(per)), median=float(np.median(per)), min=float(np.min(per)),
+                            replays=replays, launches_per_replay=reps)
+    return ev[0].elapsed_time(ev[replays]) * 1e3 / (reps * replays)
+
+
+KERNEL_STATS = {}  # median / min per launch name from kernel_times
 
 
 def kernel_times(step):
@@ -255,7 +278,8 @@ def kernel_times(step):
         def launch(r, name=name):
             fn, a, kw = step.calls(r)[name]
             fn(*a, **kw)
-        out[name] = graph_time(launch)
+        out[name] = graph_time(launch, replays=8)
+        KERNEL_STATS[name] = dict(LAST_GRAPH_TIMES)
     return out
 
 
@@ -552,8 +576,8 @@ def only(mx, spec, steps, warmup, T):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)  # ~13 ms timed: fixed host latency < 1% of it
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--extra", choices=["all", "none"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
@@ -596,12 +620,16 @@ def main():
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
     # algorithmic bytes of the fused pack: X [M,K], W [N,K], dY [M,N], each read once (bf16) and written twice
     pack_bytes = (M * K + N * K + M * N) * (2 + 2 * PACK_OUT[6])
-    kernels = {n: {"us": round(v, 2)} for n, v in k.items()}
+    kernels = {n: {"us": round(v, 2), "median_us": round(KERNEL_STATS[n]["median"], 2),
+                   "min_us": round(KERNEL_STATS[n]["min"], 2)} for n, v in k.items()}
     kernels["gemm_fwd_dgrad_wgrad"]["tflops"] = round(achieved, 1)
     kernels["pack_XWdY"]["gbs"] = round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
+        "ms_per_step_median": round(STEP_STATS["median_ms"], 4) if STEP_STATS else None,
+        "ms_per_step_min": round(STEP_STATS["min_ms"], 4) if STEP_STATS else None,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp6 (e2m3 x e2m3, fp32 accumulate)", "data": "synthetic",
         "launch": "eager" if args.no_graph else "hip_graph (4 consecutive steps per graph)",
         "config": {"workload": "MXFP6 linear (E2M3, FLOOR, Hadamard-32) X[4096,3072] W[3072,3072]: dual packs "
