@@ -324,16 +324,34 @@ int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
   if (M == 0 || D == 0 || F == 0) return MX_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
-  // packs of X, W1, W2: rows for the forward, columns kept for the backward
-  if ((st = quantize_launch(a->X, nullptr, 1, M, D, fmt, mode, had, MX_PRO_IDENTITY, a->Xr.codes, a->Xr.scales,
-                            a->Xc.codes, a->Xc.scales, nullptr, nullptr, s)))
-    return st;
-  if ((st = quantize_launch(a->W1, nullptr, 1, F, D, fmt, mode, had, MX_PRO_IDENTITY, a->W1r.codes,
-                            a->W1r.scales, a->W1c.codes, a->W1c.scales, nullptr, nullptr, s)))
-    return st;
-  if ((st = quantize_launch(a->W2, nullptr, 1, D, F, fmt, mode, had, MX_PRO_IDENTITY, a->W2r.codes,
-                            a->W2r.scales, a->W2c.codes, a->W2c.scales, nullptr, nullptr, s)))
-    return st;
+  // packs of X, W1, W2 (rows for the forward, columns kept for the
+  // backward), in one launch: the same tile body as one launch each, so
+  // the same bytes, without two launch boundaries and their drained tails
+  {
+    mx::PackMany m;
+    memset(&m, 0, sizeof m);
+    const void* xs[3] = {a->X, a->W1, a->W2};
+    const int64_t rs[3] = {M, F, D}, cs[3] = {D, D, F};
+    const mx_packed* rows[3] = {&a->Xr, &a->W1r, &a->W2r};
+    const mx_packed* cols[3] = {&a->Xc, &a->W1c, &a->W2c};
+    int64_t tiles = 0;
+    for (int i = 0; i < 3; ++i) {
+      PackParams& q = m.p[i];
+      q.x = static_cast<const uint16_t*>(xs[i]);
+      q.R = rs[i];
+      q.C = cs[i];
+      q.row_codes = static_cast<uint8_t*>(rows[i]->codes);
+      q.row_scales = static_cast<uint8_t*>(rows[i]->scales);
+      q.col_codes = static_cast<uint8_t*>(cols[i]->codes);
+      q.col_scales = static_cast<uint8_t*>(cols[i]->scales);
+      m.first[i] = tiles;
+      tiles += ((cs[i] + 127) / 128) * ((rs[i] + 127) / 128);
+    }
+    m.first[3] = tiles;
+    m.n = 3;
+    if (!grid_fits(tiles, 1, 1)) return MX_ERR_INDEX_OVERFLOW;
+    if ((st = launched(mx::launch_pack_many(m, fmt, mode, had, MX_PRO_IDENTITY, s))) != MX_OK) return st;
+  }
   // fc1: h = X W1^T + b1 (bias in the fp32 accumulator, one rounding)
   if ((st = gemm_launch(a->Xr.codes, a->Xr.scales, a->W1r.codes, a->W1r.scales, M, F, D, fmt, a->b1, MX_BF16,
                         a->h, MX_BF16, F, 0, s)))
