@@ -371,9 +371,29 @@ __device__ __forceinline__ float gelu_u(float x) {
   float inner = x + K1 * x3;
   return K0 * inner;
 }
+// n / d for n = 1 or 2 and d >= 1, rounded to nearest even: the hardware
+// reciprocal and one FMA refinement, which equals the IEEE division bit for
+// bit for every binary32 d in [1, 2^126) (checked exhaustively on gfx950,
+// for both numerators).  Past that the quotient is subnormal and the
+// reciprocal flushes it, so a wavefront holding such a d (or a NaN, or
+// +inf) takes the IEEE division for those lanes.
+__device__ __forceinline__ float div_small(float n, float d) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q0 = n * r;
+  const float e = __builtin_fmaf(-d, q0, n);
+  float q = __builtin_fmaf(e, r, q0);
+  const bool slow = !(d < 0x1p126f);
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) q = slow ? n / d : q;
+  return q;
+#else
+  return n / d;
+#endif
+}
+
 __device__ __forceinline__ float gelu_q(float u) {
   float e = mx_exp(2.0f * __builtin_fabsf(u));
-  return 2.0f / (e + 1.0f);
+  return div_small(2.0f, e + 1.0f);
 }
 
 // a = bf16((0.5*x) * (1 + tanh u))
@@ -399,18 +419,22 @@ __device__ __forceinline__ float dgelu_bf16(float da, float x) {
 }
 
 // SwiGLU on [gate | up] ([P4] commit messages: sigmoid as 1/(1+exp(-x))).
-__device__ __forceinline__ float sigmoid_mx(float g) { return 1.0f / (1.0f + mx_exp(-g)); }
+__device__ __forceinline__ float sigmoid_mx(float g) { return div_small(1.0f, 1.0f + mx_exp(-g)); }
+// The same value with the plain IEEE division: the dSwiGLU epilogue of the
+// grouped GEMM interleaves its loads of H with this arithmetic, and there
+// the reciprocal path's wavefront-uniform branch measured slower.
+__device__ __forceinline__ float sigmoid_ieee(float g) { return 1.0f / (1.0f + mx_exp(-g)); }
 __device__ __forceinline__ float swiglu_bf16(float g, float u) {
   float s = sigmoid_mx(g);
   return round_bf16((g * s) * u);
 }
 // d_gate = bf16((dz*u) * (s*(1 + g*(1-s)))),  d_up = bf16(dz*(g*s)).
 __device__ __forceinline__ float dswiglu_gate_bf16(float dz, float g, float u) {
-  float s = sigmoid_mx(g);
+  float s = sigmoid_ieee(g);
   return round_bf16((dz * u) * (s * (1.0f + g * (1.0f - s))));
 }
 __device__ __forceinline__ float dswiglu_up_bf16(float dz, float g) {
-  float s = sigmoid_mx(g);
+  float s = sigmoid_ieee(g);
   return round_bf16(dz * (g * s));
 }
 
