@@ -731,3 +731,27 @@ def test_grouped_two_stream_schedule_matches_one_stream(mxl):
             assert torch.equal(va[0], vb[0]) and torch.equal(va[1], vb[1]), k
         else:
             assert torch.equal(va, vb), k
+
+
+@pytest.mark.parametrize("pro", [1, 2, 3])
+def test_prologue_pack_over_every_bf16_input(mxl, orc, pro):
+    # every one of the 65536 bf16 bit patterns (NaNs and infinities
+    # included) as the prologue's main input: GELU of h, dGELU with h (and a
+    # random da), SwiGLU with it as the gate (and a random up).  The
+    # column-sum partials are binary32 sums of the bf16 prologue outputs, so
+    # a one-ulp difference in any single prologue value shows; codes and
+    # scales must match too.  Covers the division's reciprocal path and its
+    # fallback (quotients below 2^-126, infinite and NaN denominators).
+    rng = np.random.default_rng(950 + pro)
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    R, C = 256, 256
+    if pro == 1:    # GELU(h)
+        x, aux = allb, None
+    elif pro == 2:  # dGELU(da, h): x = da, aux = h
+        x, aux = I.bf16_normal(rng, (R, C)), allb
+    else:           # SwiGLU(gate | up): x = [gate | up], output [R][C]
+        x, aux = np.ascontiguousarray(np.concatenate([allb, I.bf16_normal(rng, (R, C))], 1)), None
+    got = gpu_quantize(mxl, x, aux, R, C, 2, 0, True, pro, colsum=True)
+    want = orc.quantize(x, R, C, 2, 0, True, pro=pro, aux=aux, row=True, col=True, colsum=True)
+    assert_packs_equal(got, want, 2, ("row_codes", "row_scales", "col_codes", "col_scales"))
+    assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
