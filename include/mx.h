@@ -366,10 +366,16 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* args, void* stream);
  * messages).  offsets: device int32 [G], cumulative group ends: group g owns
  * ragged indices [offsets[g-1], offsets[g]) (offsets[-1] := 0).  Contract
  * (caller invariant): non-decreasing, multiples of 128 ([P4] first commit
- * message: per-expert row counts are multiples of 128, so no tile straddles
- * two experts), offsets[G-1] <= R.  Indices at or past offsets[G-1] are
- * neither read nor written.  validate_offsets = 1 copies offsets to the
- * host, synchronizing `stream`, and checks them (MX_ERR_OFFSETS).
+ * message: per-expert row counts are multiples of 128, so no 32-row
+ * quantization block straddles two experts), offsets[G-1] <= R.  Indices at
+ * or past offsets[G-1] are neither read nor written.  validate_offsets = 1
+ * copies offsets to the host, synchronizing `stream`, and checks them
+ * (MX_ERR_OFFSETS).  Counts that are multiples of 256 (the alignment another
+ * stack on the pages requires) are a special case and need nothing else.
+ * Tiling (RAGGED_M): each group's rows are cut into 256-row tiles (128x256
+ * for DSWIGLU), the last one holding 128 rows when the count is an odd
+ * multiple of 128; rows of a tile past its group's end are neither read nor
+ * stored.
  *
  * MX_GROUPED_RAGGED_M (forward and data gradients):
  *   A [R] x K, B [G][N] x K (expert g's rows at B + g*N rows; its scales
