@@ -389,6 +389,9 @@ def grouped_buffers(mx, R, D, F, G, X, W1, W2, dY, offsets, fmt):
                 dX=e16(R, D), dW1=e16(G, 2 * F, D), dW2=e16(G, D, F))
 
 
+_STEP_EVENTS = {}  # the two-stream schedule's events, made once per side stream
+
+
 def grouped_step(mx, t, R, D, F, G, fmt, mode, T=None, side=None):
     """One grouped SwiGLU MLP step (forward + backward) through the C ABI.
 
@@ -425,7 +428,7 @@ def grouped_step(mx, t, R, D, F, G, fmt, mode, T=None, side=None):
             f()
         return
     main = torch.cuda.current_stream()
-    ev = [torch.cuda.Event() for _ in range(4)]
+    ev = _STEP_EVENTS.setdefault(id(side), [torch.cuda.Event() for _ in range(4)])
     side.wait_stream(main)
     with torch.cuda.stream(side):
         pack_w1()
