@@ -755,3 +755,35 @@ def test_prologue_pack_over_every_bf16_input(mxl, orc, pro):
     want = orc.quantize(x, R, C, 2, 0, True, pro=pro, aux=aux, row=True, col=True, colsum=True)
     assert_packs_equal(got, want, 2, ("row_codes", "row_scales", "col_codes", "col_scales"))
     assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
+
+
+@pytest.mark.parametrize("counts", [[0, 128, 640, 128], [1024], [128, 128, 128, 128, 0, 512]],
+                         ids=["leading-empty-and-128-groups", "one-group", "six-groups"])
+def test_grouped_chain_count_patterns(mxl, orc, counts):
+    # the 256-row ragged tiles at group boundaries: groups of exactly 128
+    # rows (a lone half tile), an empty first group, a single group, and
+    # several half tiles in a row; the whole MXFP8 chain against the oracle
+    fmt, mode = 3, 1
+    G, D, F = len(counts), 256, 256
+    R = int(sum(counts))
+    offsets = np.cumsum(counts).astype(np.int32)
+    rng = np.random.default_rng(960 + G)
+    X, dY = I.bf16_normal(rng, (R, D)), I.bf16_normal(rng, (R, D))
+    W1, W2 = I.bf16_normal(rng, (G, 2 * F, D), 0.02), I.bf16_normal(rng, (G, D, F), 0.02)
+    t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=fmt, mode=mode)
+    H, dz = host(t["H"]), host(t["dz"])
+    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H, fmt=fmt, mode=mode)
+    assert bf16_close(H, fwd["H64"])
+    assert np.array_equal(untiled(host(t["zr"][0]), F, 8), fwd["z"]["row_codes"])
+    assert np.array_equal(untiled(host(t["zc"][0]), R, 8), fwd["z"]["col_codes"])
+    assert bf16_close(host(t["Y"]), fwd["Y64"])
+    bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=dz, H_in=H)
+    assert bf16_close(dz, bwd["dz64"])
+    assert np.array_equal(untiled(host(t["dHr"][0]), 2 * F, 8), bwd["dH"]["row_codes"])
+    assert np.array_equal(untiled(host(t["dHc"][0]), R, 8), bwd["dH"]["col_codes"])
+    assert bf16_close(host(t["dX"]), bwd["dX64"])
+    dW1, dW2 = host(t["dW1"]), host(t["dW2"])
+    for g, c in enumerate(counts):
+        if c == 0:
+            assert not np.any(dW1[g]) and not np.any(dW2[g])
+    assert bf16_close(dW1, bwd["dW1_64"]) and bf16_close(dW2, bwd["dW2_64"])
