@@ -310,21 +310,29 @@ def cpu_baseline(step: LinearStep, repeats=3):
 
 # ------------------------------------------------------------------ other workloads
 def bench_cfg1(mx, T, iters=20):
+    """The 256^3 MXFP4 case: packs of A and B (one launch) and the GEMM with an
+    fp32 C.  Device time per step from graph replays (a latency-bound case:
+    one 256x256 tile, reported in microseconds)."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     A, B = I.gemm_pair(101, 256, 256, 256)
     Ad, Bd = dev(A), dev(B)
     pa, pb = mx.alloc_packed(256, 256, mx.E2M1), mx.alloc_packed(256, 256, mx.E2M1)
     C = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+    items = [dict(x=Ad, R=256, C=256, row=pa), dict(x=Bd, R=256, C=256, row=pb)]
 
-    def one(i):
-        T.run("c1_pack", mx.quantize, Ad, 256, 256, mx.E2M1, mx.FLOOR, row=pa)
-        T.run("c1_pack", mx.quantize, Bd, 256, 256, mx.E2M1, mx.FLOOR, row=pb)
-        T.run("c1_gemm", mx.gemm, pa, pb, 256, 256, 256, mx.E2M1, C, c_dtype=mx.F32)
-    sec = time_steps(one, iters, 5, T)
-    k = T.summary()
-    return {"workload": "MXFP4 quantize + GEMM 256^3, fp32 C", "us_per_step": sec * 1e6,
-            "gemm_us": k["c1_gemm"], "pack_us": k["c1_pack"]}
+    def pack(r):
+        mx.quantize_many(items, mx.E2M1, mx.FLOOR)
+
+    def gemm(r):
+        mx.gemm(pa, pb, 256, 256, 256, mx.E2M1, C, c_dtype=mx.F32)
+
+    def step(r):
+        pack(r)
+        gemm(r)
+    return {"workload": "MXFP4 quantize + GEMM 256^3, fp32 C", "us_per_step": graph_time(step, replays=8),
+            "step_median_us": LAST_GRAPH_TIMES["median"], "pack_us": graph_time(pack, replays=8),
+            "gemm_us": graph_time(gemm, replays=8)}
 
 
 def bench_cfg3(mx, T, iters=5):
