@@ -38,6 +38,7 @@ constexpr int kBlockSkew = 32;
 constexpr int kTileBytes = kTileR * kPitch + 3 * kBlockSkew;
 constexpr int kChunksPerRow = kTileC / 8;  // 16-byte chunks (8 bf16) per tile row
 constexpr int kLoads = kTileR * kChunksPerRow / 256;  // chunks per thread
+static_assert(256 / kChunksPerRow == 16 && kTileR == 16 * kLoads, "a load step is 16 tile rows");
 __device__ __forceinline__ int lds_row(int row) { return row * kPitch + (row >> 5) * kBlockSkew; }
 
 struct Chunk8 {
@@ -58,26 +59,48 @@ __device__ __forceinline__ Chunk8 as_chunk(const uint4 v) {
   return c;
 }
 
+// Where the inputs behind logical chunk (r, c..c+7) start, and each input's
+// row pitch in elements (the chunk of row r + d sits d pitches further on).
+template <int PRO>
+struct InputAt {
+  const uint16_t* ptr[Raw<PRO>::kN];
+  int64_t pitch[Raw<PRO>::kN];
+};
+template <int PRO>
+__device__ __forceinline__ InputAt<PRO> input_at(const PackParams& p, const uint16_t* xb, const uint16_t* ab,
+                                                 int64_t r, int64_t c) {
+  InputAt<PRO> a;
+  if constexpr (PRO == kIdentity || PRO == kGelu) {
+    a.ptr[0] = xb + r * p.C + c;
+    a.pitch[0] = p.C;
+  } else if constexpr (PRO == kDGelu) {
+    a.ptr[0] = xb + r * p.C + c;
+    a.ptr[1] = ab + r * p.C + c;
+    a.pitch[0] = a.pitch[1] = p.C;
+  } else if constexpr (PRO == kSwiglu) {  // x = H [R][2C] = [gate | up]
+    a.ptr[0] = xb + r * 2 * p.C + c;
+    a.ptr[1] = xb + r * 2 * p.C + p.C + c;
+    a.pitch[0] = a.pitch[1] = 2 * p.C;
+  } else {  // kDSwiglu: C = 2F, x = dz [R][F], aux = H [R][2F]
+    const int64_t F = p.C / 2;
+    const int64_t j = c < F ? c : c - F;
+    a.ptr[0] = xb + r * F + j;
+    a.ptr[1] = ab + r * p.C + j;
+    a.ptr[2] = ab + r * p.C + F + j;
+    a.pitch[0] = F;
+    a.pitch[1] = a.pitch[2] = p.C;
+  }
+  return a;
+}
+
 // Global loads of the inputs behind logical chunk (r, c..c+7).
 template <int PRO>
 __device__ __forceinline__ Raw<PRO> load_raw(const PackParams& p, const uint16_t* xb, const uint16_t* ab, int64_t r,
                                              int64_t c) {
+  const InputAt<PRO> a = input_at<PRO>(p, xb, ab, r, c);
   Raw<PRO> q;
-  if constexpr (PRO == kIdentity || PRO == kGelu) {
-    q.in[0] = ld16(xb + r * p.C + c);
-  } else if constexpr (PRO == kDGelu) {
-    q.in[0] = ld16(xb + r * p.C + c);
-    q.in[1] = ld16(ab + r * p.C + c);
-  } else if constexpr (PRO == kSwiglu) {  // x = H [R][2C] = [gate | up]
-    q.in[0] = ld16(xb + r * 2 * p.C + c);
-    q.in[1] = ld16(xb + r * 2 * p.C + p.C + c);
-  } else {  // kDSwiglu: C = 2F, x = dz [R][F], aux = H [R][2F]
-    const int64_t F = p.C / 2;
-    const int64_t j = c < F ? c : c - F;
-    q.in[0] = ld16(xb + r * F + j);
-    q.in[1] = ld16(ab + r * p.C + j);
-    q.in[2] = ld16(ab + r * p.C + F + j);
-  }
+#pragma unroll
+  for (int k = 0; k < Raw<PRO>::kN; ++k) q.in[k] = ld16(a.ptr[k]);
   return q;
 }
 
@@ -133,41 +156,66 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
   const uint16_t* xb = p.x + z * p.R * in_cols;
   const uint16_t* ab = p.aux ? p.aux + z * p.R * p.C : nullptr;
 
-  // 1. load + prologue -> LDS (rows / columns past R / C are zero)
+  // 1. load + prologue -> LDS (rows / columns past R / C are zero).  Load i
+  //    of thread t reads chunk t % 16 of tile row t / 16 + 16 i: the column
+  //    is the thread's own, the row steps by 16.
   Raw<PRO> raw[kLoads];
+  const int row_t = t / kChunksPerRow, ch_t = t % kChunksPerRow;
+  const int64_t c_t = c0 + ch_t * 8;
+  // LDS offset of load i: lds_row(row_t + 16 i) + 16 ch_t, where the 32-row
+  // block of row row_t + 16 i is i / 2 (row_t < 16)
+  const int lds_t = row_t * kPitch + ch_t * 16;
+  constexpr auto lds_step = [](int i) { return i * 16 * kPitch + (i >> 1) * kBlockSkew; };
+  if (r0 + kTileR <= p.R && c0 + kTileC <= p.C) {
+    // whole tile inside the tensor (uniform branch): one address per input,
+    // stepped by 16 row pitches per load, and no masks
+    const InputAt<PRO> a = input_at<PRO>(p, xb, ab, r0 + row_t, c_t);
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int q = t + 256 * i;
-    const int64_t r = r0 + q / kChunksPerRow, c = c0 + (q % kChunksPerRow) * 8;
-    if (r < p.R && c < p.C) raw[i] = load_raw<PRO>(p, xb, ab, r, c);
-  }
+    for (int i = 0; i < kLoads; ++i) {
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int q = t + 256 * i;
-    const int row = q / kChunksPerRow, ch = q % kChunksPerRow;
-    const int64_t r = r0 + row, c = c0 + ch * 8;
-    Chunk8 v;
-    if (r < p.R && c < p.C) {
-      v = apply_prologue<PRO>(p, raw[i], c);
-    } else {
-      v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u;
+      for (int k = 0; k < Raw<PRO>::kN; ++k) raw[i].in[k] = ld16(a.ptr[k] + 16 * i * a.pitch[k]);
     }
-    *reinterpret_cast<uint4*>(tile + lds_row(row) + ch * 16) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const Chunk8 v = apply_prologue<PRO>(p, raw[i], c_t);
+      *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int64_t r = r0 + row_t + 16 * i;
+      if (r < p.R && c_t < p.C) raw[i] = load_raw<PRO>(p, xb, ab, r, c_t);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int64_t r = r0 + row_t + 16 * i;
+      Chunk8 v;
+      if (r < p.R && c_t < p.C) {
+        v = apply_prologue<PRO>(p, raw[i], c_t);
+      } else {
+        v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u;
+      }
+      *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+    }
   }
   __syncthreads();
 
   // 2. row pass: blocks (row q/4, blk q%4) along dim 1, q = t, t + 256; the
   //    four blocks of a row come from four adjacent lanes, so their codes and
   //    their scale dword are written as one contiguous run
+  //    (the tile spans K group bx of its rows: scale_offset(r, 4 bx + blk, R)
+  //    and code_group(r, c, R, B) are a tile base plus a small lane offset)
   if (p.row_codes) {
+    uint8_t* const scale_base = p.row_scales + z * scale_bytes(p.R, p.C) + (bx * p.R + r0) * 4;
+    uint8_t* const code_base = p.row_codes + z * code_bytes(p.R, p.C, B) + (bx * p.R + r0) * (16 * B);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int q = t + 256 * h;
       const int row = q >> 2, blk = q & 3;
       const int64_t r = r0 + row, c = c0 + blk * 32;
       if (r < p.R) {
-        uint8_t* scales = p.row_scales + z * scale_bytes(p.R, p.C) + scale_offset(r, c / 32, p.R);
-        uint8_t* group = p.row_codes + z * code_bytes(p.R, p.C, B) + code_group(r, c, p.R, B);
+        uint8_t* scales = scale_base + (row * 4 + blk);
+        uint8_t* group = code_base + row * (16 * B);
         if (c < p.C) {
           float v[32];
           lds_row_block(tile + lds_row(row), 0, 0, blk * 32, v);
@@ -186,7 +234,12 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
 
   // 3. column pass: blocks (column q/4, rows 32*(q%4) .. +31) along dim 0,
   //    q = t, t + 256; a column's four blocks come from four adjacent lanes
+  //    (the tile spans K group by of its columns: scale_offset(c, 4 by + blk,
+  //    C) and code_group(c, r, C, B) are a tile base plus a lane offset)
   if (p.col_codes || p.partials) {
+    const int64_t scale_base = z * scale_bytes(p.C, p.R) + (by * p.C + c0) * 4;
+    const int64_t code_base = z * code_bytes(p.C, p.R, B) + (by * p.C + c0) * (16 * B);
+    float* const part_base = p.partials ? p.partials + z * (p.R / 32) * p.C + 4 * by * p.C + c0 : nullptr;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int q = t + 256 * h;
@@ -202,11 +255,11 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < 32; ++i) part = part + v[i];
-            p.partials[z * (p.R / 32) * p.C + (r / 32) * p.C + c] = part;
+            part_base[blk * p.C + col] = part;
           }
           if (p.col_codes) {
-            uint8_t* group = p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B);
-            uint8_t* scales = p.col_scales + z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C);
+            uint8_t* group = p.col_codes + code_base + col * (16 * B);
+            uint8_t* scales = p.col_scales + scale_base + (col * 4 + blk);
             if constexpr (SR)
               quant_store_sr(v, group, blk, c, scales, p.sr_seed, 1u, (uint64_t)((z * p.C + c) * p.R + r));
             else
@@ -214,8 +267,8 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
           }
         } else if (p.col_codes) {
           // a 128-row tile spans one K group; blocks past R are pad
-          p.col_scales[z * scale_bytes(p.C, p.R) + scale_offset(c, r / 32, p.C)] = 0;
-          zero_block<FMT>(p.col_codes + z * code_bytes(p.C, p.R, B) + code_group(c, r, p.C, B), blk, c);
+          p.col_scales[scale_base + (col * 4 + blk)] = 0;
+          zero_block<FMT>(p.col_codes + code_base + col * (16 * B), blk, c);
         }
       }
     }
@@ -237,9 +290,11 @@ __global__ __launch_bounds__(256) void pack_many_kernel(PackMany m) {
   const int64_t w = blockIdx.x;
   int i = 0;
   while (i + 1 < m.n && w >= m.first[i + 1]) ++i;
-  const int64_t local = w - m.first[i];
-  const int64_t tx = (m.p[i].C + kTileC - 1) / kTileC, ty = (m.p[i].R + kTileR - 1) / kTileR;
-  pack_tile<FMT, MODE, HAD, PRO>(m.p[i], local % tx, (local / tx) % ty, local / (tx * ty), tile);
+  // tile counts of one launch fit 32 bits (the grid is one-dimensional)
+  const uint32_t local = (uint32_t)(w - m.first[i]);
+  const uint32_t tx = (uint32_t)((m.p[i].C + kTileC - 1) / kTileC), ty = (uint32_t)((m.p[i].R + kTileR - 1) / kTileR);
+  const uint32_t row_tile = local / tx;
+  pack_tile<FMT, MODE, HAD, PRO>(m.p[i], local - row_tile * tx, row_tile % ty, row_tile / ty, tile);
 }
 
 // db[c] = sum over blocks b (increasing) of partials[b][c], from +0.  One
