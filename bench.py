@@ -47,13 +47,13 @@ GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_devi
                 "sources_sha1": "7064e466da9550e8fbf37380133117ce32270323"}
 # VALU wavefront-instructions per launch of the fused pack (rocprofv3
 # SQ_INSTS_VALU), valid while the pack sources are those it was counted with
-PACK_VALU = {"instructions_per_launch": 1.180e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-             "sources_sha1": "22be6c4cfd1a6785863ad3212dc0d99e601a8a1f"}
+PACK_VALU = {"instructions_per_launch": 1.0284e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
+             "sources_sha1": "17474bbbeab7e4b6f7c3dbaa303c8354a0605fea"}
 # peak VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per 4
 # cycles on a 16-lane SIMD (G wavefront-instructions per second)
 VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
-PACK_TRAFFIC = {"bytes_per_launch": 123.6e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "22be6c4cfd1a6785863ad3212dc0d99e601a8a1f"}
+PACK_TRAFFIC = {"bytes_per_launch": 123.5e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
+                "sources_sha1": "17474bbbeab7e4b6f7c3dbaa303c8354a0605fea"}
 
 
 def measured_traffic(rec):
