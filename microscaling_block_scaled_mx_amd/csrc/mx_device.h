@@ -391,57 +391,25 @@ __device__ __forceinline__ float div_small(float n, float d) {
 #endif
 }
 
-// How a prologue divides (n / d, n = 1 or 2, d >= 1; every mode gives the
-// IEEE quotient):
-//   kDivChecked  div_small, with its own wavefront test per division;
-//   kDivFast     the reciprocal path alone, valid for d in [1, 2^126); a d
-//                outside that range sets `slow`, and the caller recomputes
-//                the values of such lanes with kDivIeee.  One wavefront test
-//                then covers many divisions, so the compiler can interleave
-//                their independent instruction chains;
-//   kDivIeee     the plain IEEE division.
-enum DivMode { kDivChecked = 0, kDivFast = 1, kDivIeee = 2 };
-template <int DM>
-__device__ __forceinline__ float div_mode(float n, float d, bool& slow) {
-  if constexpr (DM == kDivIeee) {
-    return n / d;
-  } else if constexpr (DM == kDivFast) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const float r = __builtin_amdgcn_rcpf(d);
-    const float q0 = n * r;
-    const float e = __builtin_fmaf(-d, q0, n);
-    slow = slow || !(d < 0x1p126f);
-    return __builtin_fmaf(e, r, q0);
-#else
-    return n / d;
-#endif
-  } else {
-    return div_small(n, d);
-  }
-}
-
-template <int DM = kDivChecked>
-__device__ __forceinline__ float gelu_q(float u, bool& slow) {
+__device__ __forceinline__ float gelu_q(float u) {
   float e = mx_exp(2.0f * __builtin_fabsf(u));
-  return div_mode<DM>(2.0f, e + 1.0f, slow);
+  return div_small(2.0f, e + 1.0f);
 }
 
 // a = bf16((0.5*x) * (1 + tanh u))
-template <int DM = kDivChecked>
-__device__ __forceinline__ float gelu_bf16(float x, bool& slow) {
+__device__ __forceinline__ float gelu_bf16(float x) {
   float u = gelu_u(x);
-  float q = gelu_q<DM>(u, slow);
+  float q = gelu_q(u);
   float opt = (u < 0.0f) ? q : (2.0f - q);
   return round_bf16((0.5f * x) * opt);
 }
 
 // dh = bf16(da * (0.5*(1+tanh u) + (0.5*x) * ((q*(2-q)) * (K0*(1 + (3*K1)*(x*x))))))
 // with the second term taken as 0 when q*(2-q) == 0.
-template <int DM = kDivChecked>
-__device__ __forceinline__ float dgelu_bf16(float da, float x, bool& slow) {
+__device__ __forceinline__ float dgelu_bf16(float da, float x) {
   const float K0 = 0x1.988454p-1f, K1x3 = 0x1.12ba9cp-3f;  // fl32(3 * fl32(0.044715))
   float u = gelu_u(x);
-  float q = gelu_q<DM>(u, slow);
+  float q = gelu_q(u);
   float opt = (u < 0.0f) ? q : (2.0f - q);
   float w = q * (2.0f - q);
   float first = 0.5f * opt;
@@ -451,22 +419,14 @@ __device__ __forceinline__ float dgelu_bf16(float da, float x, bool& slow) {
 }
 
 // SwiGLU on [gate | up] ([P4] commit messages: sigmoid as 1/(1+exp(-x))).
-template <int DM = kDivChecked>
-__device__ __forceinline__ float sigmoid_mx(float g, bool& slow) {
-  return div_mode<DM>(1.0f, 1.0f + mx_exp(-g), slow);
-}
+__device__ __forceinline__ float sigmoid_mx(float g) { return div_small(1.0f, 1.0f + mx_exp(-g)); }
 // The same value with the plain IEEE division: the dSwiGLU epilogue of the
 // grouped GEMM interleaves its loads of H with this arithmetic, and there
 // the reciprocal path's wavefront-uniform branch measured slower.
 __device__ __forceinline__ float sigmoid_ieee(float g) { return 1.0f / (1.0f + mx_exp(-g)); }
-template <int DM = kDivChecked>
-__device__ __forceinline__ float swiglu_bf16(float g, float u, bool& slow) {
-  float s = sigmoid_mx<DM>(g, slow);
-  return round_bf16((g * s) * u);
-}
 __device__ __forceinline__ float swiglu_bf16(float g, float u) {
-  bool unused = false;
-  return swiglu_bf16<kDivChecked>(g, u, unused);
+  float s = sigmoid_mx(g);
+  return round_bf16((g * s) * u);
 }
 // d_gate = bf16((dz*u) * (s*(1 + g*(1-s)))),  d_up = bf16(dz*(g*s)).
 __device__ __forceinline__ float dswiglu_gate_bf16(float dz, float g, float u) {

@@ -38,11 +38,6 @@ constexpr int kBlockSkew = 32;
 constexpr int kTileBytes = kTileR * kPitch + 3 * kBlockSkew;
 constexpr int kChunksPerRow = kTileC / 8;  // 16-byte chunks (8 bf16) per tile row
 constexpr int kLoads = kTileR * kChunksPerRow / 256;  // chunks per thread
-// Four workgroups fit a compute unit's LDS (kTileBytes each), so four
-// wavefronts per SIMD: the register budget is held to that occupancy
-// (at most 128 VGPRs), or the prologue packs, whose chunks the compiler
-// interleaves, would take twice that and halve it.
-constexpr int kPackWavesPerSimd = 4;
 static_assert(256 / kChunksPerRow == 16 && kTileR == 16 * kLoads, "a load step is 16 tile rows");
 __device__ __forceinline__ int lds_row(int row) { return row * kPitch + (row >> 5) * kBlockSkew; }
 
@@ -110,11 +105,9 @@ __device__ __forceinline__ Raw<PRO> load_raw(const PackParams& p, const uint16_t
 }
 
 // The prologue on one chunk, each result rounded to bf16 ([P1] commit
-// messages: the activation epilogue becomes the packer's prologue).  DM is
-// how its divisions are done (DivMode); kDivFast sets `slow` for a lane
-// whose chunk needs the IEEE division.
-template <int PRO, int DM>
-__device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<PRO>& q, int64_t c, bool& slow) {
+// messages: the activation epilogue becomes the packer's prologue).
+template <int PRO>
+__device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<PRO>& q, int64_t c) {
   if constexpr (PRO == kIdentity) {
     return as_chunk(q.in[0]);
   } else {
@@ -126,14 +119,14 @@ __device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<
     for (int i = 0; i < 4; ++i) {
       float lo, hi;
       if constexpr (PRO == kGelu) {
-        lo = gelu_bf16<DM>(bf16_lo(x.w[i]), slow);
-        hi = gelu_bf16<DM>(bf16_hi(x.w[i]), slow);
+        lo = gelu_bf16(bf16_lo(x.w[i]));
+        hi = gelu_bf16(bf16_hi(x.w[i]));
       } else if constexpr (PRO == kDGelu) {
-        lo = dgelu_bf16<DM>(bf16_lo(x.w[i]), bf16_lo(y.w[i]), slow);
-        hi = dgelu_bf16<DM>(bf16_hi(x.w[i]), bf16_hi(y.w[i]), slow);
+        lo = dgelu_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]));
+        hi = dgelu_bf16(bf16_hi(x.w[i]), bf16_hi(y.w[i]));
       } else if constexpr (PRO == kSwiglu) {
-        lo = swiglu_bf16<DM>(bf16_lo(x.w[i]), bf16_lo(y.w[i]), slow);
-        hi = swiglu_bf16<DM>(bf16_hi(x.w[i]), bf16_hi(y.w[i]), slow);
+        lo = swiglu_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]));
+        hi = swiglu_bf16(bf16_hi(x.w[i]), bf16_hi(y.w[i]));
       } else {
         if (c < p.C / 2) {
           lo = dswiglu_gate_bf16(bf16_lo(x.w[i]), bf16_lo(y.w[i]), bf16_lo(u.w[i]));
@@ -147,31 +140,6 @@ __device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<
       out.w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
     }
     return out;
-  }
-}
-
-// The prologue on all of a thread's chunks.  The divisions take the
-// reciprocal path with no per-division wavefront test, so the compiler can
-// interleave the eight values of a chunk; one test per chunk sends the
-// lanes that met a divisor outside [1, 2^126) through the IEEE division.
-// The values are those of the per-division test either way.  (One test for
-// all chunks lets the compiler interleave all 64 values, which takes more
-// than the 128 registers of four wavefronts per SIMD and spills.)
-template <int PRO>
-__device__ __forceinline__ void apply_prologue_all(const PackParams& p, const Raw<PRO> (&raw)[kLoads], int64_t c,
-                                                   Chunk8 (&v)[kLoads]) {
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    bool slow = false;
-    v[i] = apply_prologue<PRO, kDivFast>(p, raw[i], c, slow);
-    if constexpr (PRO == kGelu || PRO == kDGelu || PRO == kSwiglu) {
-#if defined(__HIP_DEVICE_COMPILE__)
-      if (__builtin_amdgcn_ballot_w64(slow) != 0) {  // rare: only a wavefront holding such a lane pays
-        bool unused = false;
-        if (slow) v[i] = apply_prologue<PRO, kDivIeee>(p, raw[i], c, unused);
-      }
-#endif
-    }
   }
 }
 
@@ -207,27 +175,27 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
 #pragma unroll
       for (int k = 0; k < Raw<PRO>::kN; ++k) raw[i].in[k] = ld16(a.ptr[k] + 16 * i * a.pitch[k]);
     }
-    Chunk8 v[kLoads];
-    apply_prologue_all<PRO>(p, raw, c_t, v);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v[i].w[0], v[i].w[1], v[i].w[2], v[i].w[3]);
+    for (int i = 0; i < kLoads; ++i) {
+      const Chunk8 v = apply_prologue<PRO>(p, raw[i], c_t);
+      *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+    }
   } else {
-    // chunks past R / C hold zero inputs (no load) and are stored as zero
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int64_t r = r0 + row_t + 16 * i;
-#pragma unroll
-      for (int k = 0; k < Raw<PRO>::kN; ++k) raw[i].in[k] = make_uint4(0u, 0u, 0u, 0u);
       if (r < p.R && c_t < p.C) raw[i] = load_raw<PRO>(p, xb, ab, r, c_t);
     }
-    Chunk8 v[kLoads];
-    apply_prologue_all<PRO>(p, raw, c_t, v);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int64_t r = r0 + row_t + 16 * i;
-      if (!(r < p.R && c_t < p.C)) v[i].w[0] = v[i].w[1] = v[i].w[2] = v[i].w[3] = 0u;
-      *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v[i].w[0], v[i].w[1], v[i].w[2], v[i].w[3]);
+      Chunk8 v;
+      if (r < p.R && c_t < p.C) {
+        v = apply_prologue<PRO>(p, raw[i], c_t);
+      } else {
+        v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u;
+      }
+      *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
     }
   }
   __syncthreads();
@@ -308,7 +276,7 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
 }
 
 template <int FMT, int MODE, int HAD, int PRO, int SR = 0>
-__global__ __launch_bounds__(256, kPackWavesPerSimd) void pack_kernel(PackParams p) {
+__global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
   pack_tile<FMT, MODE, HAD, PRO, SR>(p, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
@@ -317,7 +285,7 @@ __global__ __launch_bounds__(256, kPackWavesPerSimd) void pack_kernel(PackParams
 // item i, with first[i] <= w < first[i + 1]; an item's tiles are ordered
 // column tile fastest, then row tile, then batch entry.
 template <int FMT, int MODE, int HAD, int PRO>
-__global__ __launch_bounds__(256, kPackWavesPerSimd) void pack_many_kernel(PackMany m) {
+__global__ __launch_bounds__(256) void pack_many_kernel(PackMany m) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
   const int64_t w = blockIdx.x;
   int i = 0;
