@@ -128,6 +128,28 @@ def test_quantize_parity_identity_gelu_dgelu(mxl, orc, fmt, mode, had, pro):
     assert_f32_bitwise(got["colsum"], want["colsum"])
 
 
+@pytest.mark.parametrize("fmt,mode,had", FMT_CASES)
+@pytest.mark.parametrize("pro", [0, 1, 2, 3, 4])
+def test_quantize_whole_and_ragged_tiles(mxl, orc, fmt, mode, had, pro):
+    # R x C = 160 x 320: four whole 128 x 128 tiles (loaded with one address
+    # per input and no masks) beside ragged ones (masked per chunk), for every
+    # prologue; special values sit in a whole tile
+    rng = np.random.default_rng(900 + 10 * fmt + pro + (5 if had else 0))
+    R, C = 160, 320
+    if pro == 3:  # SwiGLU: x = H [R][2C]
+        x, aux = with_specials(I.bf16_normal(rng, (R, 2 * C), 2.0), rng), None
+    elif pro == 4:  # dSwiGLU: x = dz [R][C/2], aux = H [R][C]
+        x, aux = I.bf16_normal(rng, (R, C // 2), 1.0), with_specials(I.bf16_normal(rng, (R, C), 2.0), rng)
+    else:
+        x = with_specials(I.bf16_normal(rng, (R, C), 2.0), rng)
+        aux = I.bf16_normal(rng, (R, C), 3.0) if pro == 2 else None
+    got = gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, colsum=True)
+    want = orc.quantize(x, R, C, fmt, mode, had, pro=pro, aux=aux, row=True, col=True, colsum=True)
+    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
+    assert_f32_bitwise(got["colsum"], want["colsum"])
+
+
 @pytest.mark.parametrize("fmt,mode", [(3, 1), (1, 0), (2, 0)])
 def test_quantize_parity_swiglu_dswiglu(mxl, orc, fmt, mode):
     rng = np.random.default_rng(7 + fmt)
