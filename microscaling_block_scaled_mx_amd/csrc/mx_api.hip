@@ -91,7 +91,7 @@ int validate_quantize(const void* x, const void* aux, int64_t batch, int64_t R, 
   const void* ptrs[] = {x, aux, rc, rs, cc, cs, part, sum};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MX_ERR_ALIGN;
-  if (!grid_fits((C + 127) / 128, (R + 63) / 64, batch)) return MX_ERR_INDEX_OVERFLOW;
+  if (!grid_fits((C + 127) / 128, (R + 127) / 128, batch)) return MX_ERR_INDEX_OVERFLOW;
   return MX_OK;
 }
 

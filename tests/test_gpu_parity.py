@@ -118,7 +118,7 @@ def gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, row=True, col=True, col
 @pytest.mark.parametrize("pro", [0, 1, 2])
 def test_quantize_parity_identity_gelu_dgelu(mxl, orc, fmt, mode, had, pro):
     rng = np.random.default_rng(100 + 10 * fmt + pro)
-    R, C = 96, 160  # ragged against the 64 x 128 tile
+    R, C = 96, 160  # ragged against the 128 x 128 tile
     x = with_specials(I.bf16_normal(rng, (R, C), 2.0), rng)
     aux = I.bf16_normal(rng, (R, C), 3.0) if pro == 2 else None
     got = gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, colsum=True)
