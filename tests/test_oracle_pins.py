@@ -641,3 +641,153 @@ def test_quantize_sr_matches_nearest_scales_and_neighbour_codes(orc):
     other = orc.quantize_sr(x, R, C, seed=43, row=True)
     assert np.array_equal(again["row_codes"], sr["row_codes"])
     assert not np.array_equal(other["row_codes"], sr["row_codes"])
+
+
+# ------------------------------------------------------------------ prologues through orc_quantize
+# The prologue tests above pin the scalar functions; these pin the indexing
+# of the tensors the packer reads them from ([gate | up] halves of H, the
+# (da, h) operand order), through the whole orc_quantize path, on inputs
+# whose prologue output is an exact product with a single rounding.
+def _bf16_of(x):
+    return I.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _same_pack(orc, got_x, got_aux, want_v, R, C, fmt, mode, pro):
+    """orc_quantize with prologue `pro` must pack exactly what the identity
+    prologue packs from the expected prologue output want_v (bf16 bits)."""
+    got = orc.quantize(got_x, R, C, fmt, mode, pro=pro, aux=got_aux, row=True, col=True, colsum=True)
+    want = orc.quantize(want_v, R, C, fmt, mode, row=True, col=True, colsum=True)
+    for k in want:
+        assert np.array_equal(got[k].view(np.uint8), want[k].view(np.uint8)), (pro, k)
+
+
+@pytest.mark.parametrize("fmt,mode", [(3, 1), (1, 0)])
+def test_swiglu_prologue_reads_gate_then_up(orc, fmt, mode):
+    # a saturated gate (g >= 20: exp(-g) < 2^-25, so s == 1 exactly) makes
+    # z = bf16(g * u): the product of two bf16 values is exact in binary32
+    rng = np.random.default_rng(41)
+    R, F = 64, 96
+    g = _bf16_of(rng.uniform(20, 100, (R, F)))
+    u = _bf16_of(rng.standard_normal((R, F)))
+    H = np.ascontiguousarray(np.concatenate([g, u], 1))
+    z = _bf16_of(I.bf16_bits_to_f32(g) * I.bf16_bits_to_f32(u))
+    assert np.array_equal(orc.prologue(H, None, R, F, orc.PRO_SWIGLU), z)
+    _same_pack(orc, H, None, z, R, F, fmt, mode, orc.PRO_SWIGLU)
+    # the gate and up halves swapped would give silu(u) * g instead
+    Hs = np.ascontiguousarray(np.concatenate([u, g], 1))
+    assert not np.array_equal(orc.prologue(Hs, None, R, F, orc.PRO_SWIGLU), z)
+
+
+@pytest.mark.parametrize("fmt,mode", [(3, 1), (1, 0)])
+def test_dswiglu_prologue_reads_dz_and_gate_up(orc, fmt, mode):
+    # saturated gate: s == 1, so d_gate = bf16((dz*u) * (1 * (1 + g*0))) =
+    # bf16(dz*u) and d_up = bf16(dz * g), both single roundings of exact
+    # binary32 products; dH = [d_gate | d_up]
+    rng = np.random.default_rng(42)
+    R, F = 64, 64
+    g = _bf16_of(rng.uniform(20, 100, (R, F)))
+    u = _bf16_of(rng.standard_normal((R, F)))
+    dz = _bf16_of(rng.standard_normal((R, F)))
+    H = np.ascontiguousarray(np.concatenate([g, u], 1))
+    gf, uf, dzf = (I.bf16_bits_to_f32(a) for a in (g, u, dz))
+    dH = np.ascontiguousarray(np.concatenate([_bf16_of(dzf * uf), _bf16_of(dzf * gf)], 1))
+    assert np.array_equal(orc.prologue(dz, H, R, 2 * F, orc.PRO_DSWIGLU), dH)
+    _same_pack(orc, dz, H, dH, R, 2 * F, fmt, mode, orc.PRO_DSWIGLU)
+
+
+@pytest.mark.parametrize("fmt,mode,had", [(2, 0, True), (3, 1, False)])
+def test_gelu_and_dgelu_prologues_on_exact_points(orc, fmt, mode, had):
+    # h = 0: u = 0, exp(0) = 1, q = 1, so GELU(0) = 0 and dGELU = 0.5 exactly;
+    # |h| >= 12: exp(2|u|) overflows, q = 0, so GELU(h) = h and dGELU = 1 for
+    # h > 0, GELU(h) = -0 and dGELU = 0 for h < 0.  So a = {0, h, -0} and dh = {da/2, da, 0} exactly; with the
+    # (da, h) operands swapped dh would be dgelu(h) * da evaluated at da.
+    rng = np.random.default_rng(43)
+    R, C = 64, 128
+    pick = rng.integers(0, 3, (R, C))
+    hv = np.where(pick == 0, 0.0, np.where(pick == 1, rng.uniform(12, 60, (R, C)), -rng.uniform(12, 60, (R, C))))
+    h = _bf16_of(hv)
+    da = _bf16_of(rng.standard_normal((R, C)))
+    hf, daf = I.bf16_bits_to_f32(h), I.bf16_bits_to_f32(da)
+    a = np.where(pick == 0, np.uint16(0), np.where(pick == 1, h, np.uint16(0x8000))).astype(np.uint16)
+    dh = _bf16_of(np.where(pick == 0, daf * np.float32(0.5), np.where(pick == 1, daf, np.float32(0) * daf)))
+    assert np.array_equal(orc.prologue(h, None, R, C, orc.PRO_GELU), a)
+    assert np.array_equal(orc.prologue(da, h, R, C, orc.PRO_DGELU), dh)
+    _same_pack(orc, h, None, a, R, C, fmt, mode, orc.PRO_GELU)
+    _same_pack(orc, da, h, dh, R, C, fmt, mode, orc.PRO_DGELU)
+    assert not np.array_equal(orc.prologue(h, da, R, C, orc.PRO_DGELU), dh)
+    assert np.all(np.abs(hf[pick > 0]) >= 12)
+
+
+# ------------------------------------------------------------------ chains against unquantized chains
+def snr_db(ref, got):
+    return 10 * np.log10(np.sum(ref ** 2) / np.sum((ref - got) ** 2))
+
+
+def test_grouped_chain_snr_against_unquantized_chain(orc):
+    # The pages check the grouped SwiGLU MLP against a chain without any
+    # quantization, computed from the original bf16 tensors, and report the
+    # MXFP8 outputs on a band: 28.5 dB for z, the FC1 GEMM output, and
+    # 23.7 dB for y, the FC2 output after a second quantized stage; their
+    # gate is the band minus 6 dB.  The oracle lands on the band.  Backward
+    # reading: dz (FC2 dgrad, one quantized GEMM like z) on z's band; dX,
+    # dW1 and dW2 (through the quantized dH, like y) on y's band.
+    g = GOLDEN["mxfp8_grouped_chain_snr_vs_bf16_db"]
+    R, D, F, G = 1024, 512, 256, 4
+    counts, offsets, X, W1, W2, dY = I.grouped_mlp(17, R, D, F, G, zero_expert=1)
+    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F)
+    bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F)
+    f64 = lambda a: I.bf16_bits_to_f32(a).astype(np.float64)
+    Xf, W1f, W2f, dYf = f64(X), f64(W1), f64(W2), f64(dY)
+    ref = {k: np.zeros(s) for k, s in (("H", (R, 2 * F)), ("Y", (R, D)), ("dz", (R, F)), ("dX", (R, D)),
+                                       ("dW1", (G, 2 * F, D)), ("dW2", (G, D, F)))}
+    for e, (s, t) in enumerate(orc.grouped_ranges(offsets)):
+        if t == s:
+            continue
+        H = Xf[s:t] @ W1f[e].T
+        gate, up = H[:, :F], H[:, F:]
+        sg = 1 / (1 + np.exp(-gate))
+        z = gate * sg * up
+        dz = dYf[s:t] @ W2f[e]
+        dH = np.concatenate([dz * up * sg * (1 + gate * (1 - sg)), dz * gate * sg], 1)
+        ref["H"][s:t], ref["Y"][s:t], ref["dz"][s:t] = H, z @ W2f[e].T, dz
+        ref["dX"][s:t] = dH @ W1f[e]
+        ref["dW1"][e], ref["dW2"][e] = dH.T @ Xf[s:t], dYf[s:t].T @ z
+    got = {"H": fwd["H64"], "Y": fwd["Y64"], "dz": bwd["dz64"], "dX": bwd["dX64"], "dW1": bwd["dW1_64"],
+           "dW2": bwd["dW2_64"]}
+    band = {"H": g["z"], "dz": g["z"], "Y": g["y"], "dX": g["y"], "dW1": g["y"], "dW2": g["y"]}
+    for k in got:
+        s = snr_db(ref[k], got[k])
+        assert s >= band[k] - g["gate_below_band_db"], (k, s)
+        assert abs(s - band[k]) <= g["tolerance_db"], (k, s)
+
+
+def test_mlp_chain_snr_against_unquantized_mlp(orc):
+    # The MXFP6 (+Hadamard) linear lands at about 28 dB SNR against BF16 in
+    # the forward and both gradients (the MXFP6 page).  In the fused MLP, h
+    # (fc1 forward) and da (fc2 data gradient) are such single linears and
+    # must land there; Y, dX, dW1, dW2 and db1 pass a second quantized stage
+    # and are held to the grouped page's gate, the band minus 6 dB.  The
+    # reference is the unquantized tanh-GELU MLP from the same bf16 inputs.
+    g = GOLDEN["mxfp6_linear_snr_vs_bf16_db"]
+    gate = g["value"] - GOLDEN["mxfp8_grouped_chain_snr_vs_bf16_db"]["gate_below_band_db"]
+    M, D, F = 512, 256, 1024
+    X, W1, b1, W2, dY = I.mlp(301, M, D, F)
+    fwd = orc.mlp_fwd_ref(X, W1, b1, W2, M, D, F)
+    bwd = orc.mlp_bwd_ref(dY, fwd, M, D, F)
+    f64 = lambda a: I.bf16_bits_to_f32(a).astype(np.float64)
+    Xf, W1f, b1f, W2f, dYf = f64(X), f64(W1), f64(b1), f64(W2), f64(dY)
+    h = Xf @ W1f.T + b1f
+    k0, k1 = math.sqrt(2 / math.pi), 0.044715
+    t = np.tanh(k0 * (h + k1 * h ** 3))
+    a = 0.5 * h * (1 + t)
+    da = dYf @ W2f
+    dh = da * (0.5 * (1 + t) + 0.5 * h * (1 - t * t) * k0 * (1 + 3 * k1 * h * h))
+    single = {"h": (h, fwd["h64"]), "da": (da, bwd["da64"])}
+    for k, (r, o) in single.items():
+        s = snr_db(r, o)
+        assert abs(s - g["value"]) <= g["tolerance_db"], (k, s)
+    two = {"Y": (a @ W2f.T, fwd["Y64"]), "dX": (dh @ W1f, bwd["dX64"]), "dW1": (dh.T @ Xf, bwd["dW1_64"]),
+           "dW2": (dYf.T @ a, bwd["dW2_64"]), "db1": (dh.sum(0), bwd["db1"].astype(np.float64))}
+    for k, (r, o) in two.items():
+        s = snr_db(r, o)
+        assert gate <= s < g["value"] + g["tolerance_db"], (k, s)
