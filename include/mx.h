@@ -236,9 +236,7 @@ int mx_quantize_many(const mx_quantize_item* items, int n, int fmt, int scale_mo
  *               of 8.
  * Tiling: the output is cut into 256x256, 256x192, 192x256, 192x192 or
  * 256x128 tiles, whichever costs the fewest rounds x tile area with one tile
- * per compute unit; the environment variable MX_DENSE_TILE=<BM>x<BN>
- * restricts the choice to one of these shapes when it divides M x N (a test
- * hook; results agree to the tolerance of the accumulation order only).
+ * per compute unit (mx_gemm_tiled takes the shape from the caller).
  * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
  * MX_ERR_INDEX_OVERFLOW, MX_ERR_DEVICE, MX_ERR_LAUNCH.
  */
@@ -265,6 +263,19 @@ int mx_gemm(const void* a_codes, const void* a_scales, const void* b_codes, cons
 int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales,
                        int64_t M, int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c,
                        int c_dtype, int64_t ldc, void* stream);
+
+/*
+ * mx_gemm_tiled -- mx_gemm with the output tile shape chosen by the caller:
+ * tile_m x tile_n is one of 256x256, 256x192, 192x256, 192x192, 256x128 and
+ * must divide M x N (else MX_ERR_SHAPE); 0 x 0 picks the shape as mx_gemm
+ * does.  For tuning and for tests that cover every tile shape.  The result
+ * differs from mx_gemm's only by the binary32 accumulation order across
+ * the K stages of a tile, i.e. within the GEMM tolerance; with mx_gemm's
+ * own shape it is bitwise mx_gemm's.  Other arguments and errors as mx_gemm.
+ */
+int mx_gemm_tiled(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
+                  int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
+                  int tile_m, int tile_n, void* stream);
 
 /*
  * mx_gemm_many -- several GEMMs of one format in a single launch, with the
@@ -310,7 +321,8 @@ int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream);
  * Summary: one function owns fc1 -> epilogue -> fc2, the packer takes the
  * epilogue as a prologue in both directions, the activation is packed
  * straight from on-chip memory and the pre-activation gradient is never
- * assembled; the fc1 bias gradient comes back as a per-column sum).
+ * assembled; db1 is finished from the column sums of dh that the packer
+ * accumulates).
  * All packs use fmt / scale_mode / hadamard (MXFP6: MX_E2M3, FLOOR, 1).
  * M, D, F multiples of 256.  Packed buffers: rows x K as named.
  * The backward's weight gradients may be the caller's main_grad buffers
@@ -366,8 +378,8 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* args, void* stream);
  * messages).  offsets: device int32 [G], cumulative group ends: group g owns
  * ragged indices [offsets[g-1], offsets[g]) (offsets[-1] := 0).  Contract
  * (caller invariant): non-decreasing, multiples of 128 ([P4] first commit
- * message: per-expert row counts are multiples of 128, so no 32-row
- * quantization block straddles two experts), offsets[G-1] <= R.  Indices at
+ * message: expert sizes are 128-row multiples, which keeps every 32-row
+ * quantization block and every tile inside one expert), offsets[G-1] <= R.  Indices at
  * or past offsets[G-1] are neither read nor written.  validate_offsets = 1
  * copies offsets to the host, synchronizing `stream`, and checks them
  * (MX_ERR_OFFSETS).  Counts that are multiples of 256 (the alignment another

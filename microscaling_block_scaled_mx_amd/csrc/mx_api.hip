@@ -128,14 +128,15 @@ int validate_gemm(const void* ac, const void* as, const void* bc, const void* bs
   const void* ptrs[] = {ac, as, bc, bs, bias, c};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MX_ERR_ALIGN;
-  if (!grid_fits(N / 256, M / 128, 1)) return MX_ERR_INDEX_OVERFLOW;
+  // the dense launch's 1-D grid of output tiles (none is smaller than 128 x 128)
+  if (!grid_fits((M / 128) * (N / 128), 1, 1)) return MX_ERR_INDEX_OVERFLOW;
   if (!operand_fits(fmt, M, K) || !operand_fits(fmt, N, K)) return MX_ERR_INDEX_OVERFLOW;
   return MX_OK;
 }
 
 int gemm_launch(const void* ac, const void* as, const void* bc, const void* bs, int64_t M, int64_t N, int64_t K,
                 int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc, int accumulate,
-                hipStream_t s) {
+                hipStream_t s, int tile_shape = 0) {
   if (M == 0 || N == 0) return MX_OK;
   GemmParams p;
   memset(&p, 0, sizeof p);
@@ -152,6 +153,7 @@ int gemm_launch(const void* ac, const void* as, const void* bc, const void* bs, 
   p.c = c;
   p.ldc = ldc;
   p.c_f32 = c_dtype == MX_F32;
+  p.tile_shape = tile_shape;
   return launched(mx::launch_gemm(p, fmt, mx::kDense, accumulate ? mx::kEpiAccum : mx::kEpiStore, s));
 }
 
@@ -262,6 +264,22 @@ int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_
                      static_cast<hipStream_t>(stream));
 }
 
+int mx_gemm_tiled(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
+                  int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
+                  int tile_m, int tile_n, void* stream) {
+  int st = validate_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc);
+  if (st != MX_OK) return st;
+  int tile = 0;
+  if (tile_m != 0 || tile_n != 0) {
+    const int i = mx::dense_tile_index(tile_m, tile_n, M, N);
+    if (i < 0) return MX_ERR_SHAPE;
+    tile = i + 1;
+  }
+  if ((st = check_device()) != MX_OK) return st;
+  return gemm_launch(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc, 0,
+                     static_cast<hipStream_t>(stream), tile);
+}
+
 int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream) {
   if (!items) return MX_ERR_NULL;
   if (n < 1 || n > MX_GEMM_MANY_MAX) return MX_ERR_SHAPE;
@@ -318,12 +336,29 @@ int mx_fused_mlp_fwd(const mx_mlp_fwd_args* a, void* stream) {
     if (q && !aligned16(q)) return MX_ERR_ALIGN;
   for (const mx_packed* q : packs)
     if (!packed_aligned(*q)) return MX_ERR_ALIGN;
-  if (!grid_fits(F / 128 + D / 128, M / 64, 1)) return MX_ERR_INDEX_OVERFLOW;
-  int st = check_device();
-  if (st != MX_OK) return st;
+  const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
+  // every pack and GEMM of the composition passes the checks of its own
+  // entry point (grid and 32-bit offset limits included)
+  int st;
+  if ((st = validate_quantize(a->X, nullptr, 1, M, D, fmt, mode, had, MX_PRO_IDENTITY, a->Xr.codes, a->Xr.scales,
+                              a->Xc.codes, a->Xc.scales, nullptr, nullptr)) ||
+      (st = validate_quantize(a->W1, nullptr, 1, F, D, fmt, mode, had, MX_PRO_IDENTITY, a->W1r.codes,
+                              a->W1r.scales, a->W1c.codes, a->W1c.scales, nullptr, nullptr)) ||
+      (st = validate_quantize(a->W2, nullptr, 1, D, F, fmt, mode, had, MX_PRO_IDENTITY, a->W2r.codes,
+                              a->W2r.scales, a->W2c.codes, a->W2c.scales, nullptr, nullptr)) ||
+      (st = validate_quantize(a->h, nullptr, 1, M, F, fmt, mode, had, MX_PRO_GELU_TANH, a->ar.codes, a->ar.scales,
+                              a->ac.codes, a->ac.scales, nullptr, nullptr)) ||
+      (st = validate_gemm(a->Xr.codes, a->Xr.scales, a->W1r.codes, a->W1r.scales, M, F, D, fmt, a->b1, MX_BF16,
+                          a->h, MX_BF16, F)) ||
+      (st = validate_gemm(a->ar.codes, a->ar.scales, a->W2r.codes, a->W2r.scales, M, D, F, fmt, nullptr, MX_BF16,
+                          a->Y, MX_BF16, D)) ||
+      (st = operand_fits(fmt, D, M) && operand_fits(fmt, D, F) && operand_fits(fmt, F, D) && operand_fits(fmt, F, M)
+                ? MX_OK
+                : MX_ERR_INDEX_OVERFLOW))
+    return st;
+  if ((st = check_device()) != MX_OK) return st;
   if (M == 0 || D == 0 || F == 0) return MX_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
   // packs of X, W1, W2 (rows for the forward, columns kept for the
   // backward), in one launch: the same tile body as one launch each, so
   // the same bytes, without two launch boundaries and their drained tails
@@ -381,12 +416,27 @@ int mx_fused_mlp_bwd(const mx_mlp_bwd_args* a, void* stream) {
     if (q && !aligned16(q)) return MX_ERR_ALIGN;
   for (const mx_packed* q : packs)
     if (!packed_aligned(*q)) return MX_ERR_ALIGN;
-  if (!grid_fits(F / 128 + D / 128, M / 64 + F / 64, 1)) return MX_ERR_INDEX_OVERFLOW;
-  int st = check_device();
-  if (st != MX_OK) return st;
+  const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
+  // every pack and GEMM of the composition passes the checks of its own
+  // entry point (grid and 32-bit offset limits included)
+  int st;
+  float* part = a->db1 ? a->db1_partials : nullptr;
+  if ((st = validate_quantize(a->dY, nullptr, 1, M, D, fmt, mode, had, MX_PRO_IDENTITY, a->dYr.codes,
+                              a->dYr.scales, a->dYc.codes, a->dYc.scales, nullptr, nullptr)) ||
+      (st = validate_quantize(a->da, a->h, 1, M, F, fmt, mode, had, MX_PRO_DGELU_TANH, a->dhr.codes, a->dhr.scales,
+                              a->dhc.codes, a->dhc.scales, part, a->db1)) ||
+      (st = validate_gemm(a->dYr.codes, a->dYr.scales, a->W2c.codes, a->W2c.scales, M, F, D, fmt, nullptr, MX_BF16,
+                          a->da, MX_BF16, F)) ||
+      (st = validate_gemm(a->dhr.codes, a->dhr.scales, a->W1c.codes, a->W1c.scales, M, D, F, fmt, nullptr, MX_BF16,
+                          a->dX, MX_BF16, D)) ||
+      (st = validate_gemm(a->dhc.codes, a->dhc.scales, a->Xc.codes, a->Xc.scales, F, D, M, fmt, nullptr, MX_BF16,
+                          a->dW1, MX_BF16, D)) ||
+      (st = validate_gemm(a->dYc.codes, a->dYc.scales, a->ac.codes, a->ac.scales, D, F, M, fmt, nullptr, MX_BF16,
+                          a->dW2, MX_BF16, F)))
+    return st;
+  if ((st = check_device()) != MX_OK) return st;
   if (M == 0 || D == 0 || F == 0) return MX_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int fmt = a->fmt, mode = a->scale_mode, had = a->hadamard;
   if ((st = quantize_launch(a->dY, nullptr, 1, M, D, fmt, mode, had, MX_PRO_IDENTITY, a->dYr.codes, a->dYr.scales,
                             a->dYc.codes, a->dYc.scales, nullptr, nullptr, s)))
     return st;
@@ -427,7 +477,7 @@ int mx_grouped_gemm(const mx_grouped_args* a, void* stream) {
   if (a->epilogue != MX_EPI_DSWIGLU && !a->C) return MX_ERR_NULL;
   if (a->G < 1 || a->G > 65535 || a->R < 0 || a->R % 128) return MX_ERR_SHAPE;
   if (a->mode == MX_GROUPED_RAGGED_M) {
-    if (a->N <= 0 || a->K < 0 || a->N % 256 || a->K % 128) return MX_ERR_SHAPE;
+    if (a->N <= 0 || a->K < 0 || a->N % 256 || a->K % 256) return MX_ERR_SHAPE;
   } else {
     if (a->M < 0 || a->N < 0 || a->M % 256 || a->N % 256) return MX_ERR_SHAPE;
   }

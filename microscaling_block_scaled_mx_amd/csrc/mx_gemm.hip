@@ -10,8 +10,8 @@
 //      (Troubleshooting); 256x256 tiles at the Flux QKV shape (Tuned GEMMs).
 // [P4] "MXFP8 cudnn-fe Swiglu fused Grouped MLP fwd/bwd and wgrad group
 //      gemm": ragged grouped GEMM with the expert picked from the tile
-//      coordinate (counts are multiples of 128, so no tile straddles two
-//      experts), SwiGLU / dSwiGLU epilogues that quantize rowwise 1x32 and
+//      coordinate (expert sizes are 128-row multiples, so a tile never
+//      spans two experts), SwiGLU / dSwiGLU epilogues that quantize rowwise 1x32 and
 //      columnwise 32x1 in the same launch, ragged-K weight gradient writing
 //      zeros for empty experts (commit messages).
 //
@@ -50,7 +50,6 @@
 // 8*(i/4) + 4*(l/32) + {0..3} for each i/4 -- 8 contiguous bytes of bf16.
 #include <atomic>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -1027,23 +1026,14 @@ int cu_count() {
 // tile per compute unit cost the least output area (rounds x BM x BN),
 // larger tiles first on ties -- e.g. 4096 x 3072 takes 256 tiles of
 // 256 x 192 in one round instead of 192 tiles of 256 x 256 on 192 of the 256
-// compute units.  MX_DENSE_TILE=<BM>x<BN> restricts the choice to that shape
-// (tests use it to cover every shape at small sizes); unset, or not dividing
-// M x N, it has no effect.  -1: no shape divides M x N.
+// compute units.  -1: no shape divides M x N.
 int dense_shape(int64_t M, int64_t N) {
   const int64_t cus = cu_count();
-  int force = -1;
-  if (const char* env = getenv("MX_DENSE_TILE")) {
-    int fm = 0, fn = 0;
-    if (sscanf(env, "%dx%d", &fm, &fn) == 2)
-      for (int i = 0; i < 5; ++i)
-        if (kDenseShapes[i][0] == fm && kDenseShapes[i][1] == fn && M % fm == 0 && N % fn == 0) force = i;
-  }
   int best = -1;
   int64_t best_cost = 0;
   for (int i = 0; i < 5; ++i) {
     const int bm = kDenseShapes[i][0], bn = kDenseShapes[i][1];
-    if (M % bm || N % bn || (force >= 0 && i != force)) continue;
+    if (M % bm || N % bn) continue;
     const int64_t tiles = (M / bm) * (N / bn);
     const int64_t cost = ((tiles + cus - 1) / cus) * bm * bn;
     if (best < 0 || cost < best_cost) {
@@ -1054,9 +1044,15 @@ int dense_shape(int64_t M, int64_t N) {
   return best;
 }
 
+// The shape a dense launch uses: the caller's (p.tile_shape = 1 + its
+// index), else the one dense_shape picks.
+int dense_shape_of(const GemmParams& p) {
+  return p.tile_shape > 0 && p.tile_shape <= 5 ? p.tile_shape - 1 : dense_shape(p.M, p.N);
+}
+
 template <int FMT, int EPI>
 hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
-  switch (dense_shape(p.M, p.N)) {
+  switch (dense_shape_of(p)) {
     case 0: return launch_one<FMT, 256, 256, kDense, EPI>(p, stream);
     case 1: return launch_one<FMT, 256, 192, kDense, EPI>(p, stream);
     case 2: return launch_one<FMT, 192, 256, kDense, EPI>(p, stream);
@@ -1140,10 +1136,16 @@ hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
 
 }  // namespace
 
+int dense_tile_index(int bm, int bn, int64_t M, int64_t N) {
+  for (int i = 0; i < 5; ++i)
+    if (kDenseShapes[i][0] == bm && kDenseShapes[i][1] == bn) return (M % bm || N % bn) ? -1 : i;
+  return -1;
+}
+
 hipError_t launch_gemm_many(GemmMany m, int fmt, hipStream_t stream) {
   if (m.n < 1 || m.n > kGemmManyMax) return hipErrorInvalidValue;
   for (int i = 0; i < m.n; ++i)
-    if ((m.shape[i] = dense_shape(m.p[i].M, m.p[i].N)) < 0) return hipErrorInvalidValue;
+    if ((m.shape[i] = dense_shape_of(m.p[i])) < 0) return hipErrorInvalidValue;
   switch (fmt) {
     case kE2M1: return launch_many_fmt<kE2M1>(m, stream);
     case kE2M3: return launch_many_fmt<kE2M3>(m, stream);

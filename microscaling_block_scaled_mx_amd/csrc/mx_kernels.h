@@ -97,9 +97,15 @@ struct GemmParams {
   uint8_t* q_col_codes;
   uint8_t* q_col_scales;
   int q_mode;            // scale mode for the epilogue's quantization
+  // dense: 0 lets the launch pick the output tile shape; 1 + i forces entry
+  // i of the dense shape table (see dense_tile_index)
+  int tile_shape;
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream);
+// Index of the dense output tile shape bm x bn for an M x N output, or -1 if
+// it is not one of the dense shapes or does not divide M x N.
+int dense_tile_index(int bm, int bn, int64_t M, int64_t N);
 
 // Up to kGemmManyMax dense GEMMs (kDense, kEpiStore) of one format in one
 // launch; each takes the tile shape launch_gemm would give it.  shape and

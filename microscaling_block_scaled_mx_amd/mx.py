@@ -104,6 +104,8 @@ def lib():
         L.mx_gemm_many.argtypes = [ctypes.POINTER(GemmItem), ci, ci, vp]
         L.mx_gemm.restype = ci
         L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
+        L.mx_gemm_tiled.restype = ci
+        L.mx_gemm_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, ci, ci, vp]
         L.mx_gemm_accumulate.restype = ci
         L.mx_gemm_accumulate.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_fused_mlp_fwd.restype = ci
@@ -127,10 +129,22 @@ def lib():
 
 
 def _ptr(t):
+    """Device address of a tensor argument.  The C ABI reads and writes
+    every buffer as a dense row-major array on the current device, so a
+    host tensor, a tensor on another device or a strided view is refused
+    here (a host pointer would reach the kernels, a view would be read with
+    the wrong pitch).  Plain integers pass through as addresses."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise MXError(2, "tensor argument is a strided view; pass a contiguous tensor")
+    if not t.is_cuda:
+        raise MXError(7, "tensor argument is not on a GPU (the kernels take device memory)")
+    if t.device.index != torch.cuda.current_device():
+        raise MXError(7, f"tensor argument is on cuda:{t.device.index}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     return t.data_ptr()
 
 
@@ -255,6 +269,20 @@ def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int =
     st = lib().mx_gemm(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
                        _ptr(c), c_dtype, N if ldc is None else ldc, _stream(stream))
     _check(st, "mx_gemm")
+
+
+def gemm_tiled(a, b, M: int, N: int, K: int, fmt: int, c, tile, bias=None, bias_dtype: int = BF16,
+               c_dtype: int = BF16, ldc: int | None = None, stream=None):
+    """mx_gemm_tiled: mx_gemm with the output tile shape tile = (tile_m,
+    tile_n), or (0, 0) for mx_gemm's own choice."""
+    _need_packed(a, M, K, fmt, "gemm_tiled A")
+    _need_packed(b, N, K, fmt, "gemm_tiled B")
+    _need(c, (4 if c_dtype == F32 else 2) * M * (N if ldc is None else ldc), "gemm_tiled C")
+    _need(bias, (4 if bias_dtype == F32 else 2) * N, "gemm_tiled bias")
+    st = lib().mx_gemm_tiled(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
+                             _ptr(c), c_dtype, N if ldc is None else ldc, int(tile[0]), int(tile[1]),
+                             _stream(stream))
+    _check(st, "mx_gemm_tiled")
 
 
 def gemm_accumulate(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16,

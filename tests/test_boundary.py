@@ -171,6 +171,7 @@ def grouped(**kw):
     (dict(mode=mx.RAGGED_K, epilogue=mx.EPI_SWIGLU, out_row=(P7, P8), out_col=(P7, P8)), FORMAT),
     (dict(epilogue=mx.EPI_SWIGLU, fmt=mx.E2M1, scale_mode=mx.RCEIL, out_row=(P7, P8), out_col=(P7, P8)), FORMAT),
     (dict(G=0), SHAPE), (dict(G=-1), SHAPE), (dict(R=1000), SHAPE), (dict(N=1000), SHAPE), (dict(K=100), SHAPE),
+    (dict(K=384), SHAPE),                                          # K a multiple of 128 but not of 256
     (dict(mode=mx.RAGGED_K, M=100, N=256), SHAPE),
     (dict(offsets=P + 4), ALIGN), (dict(C=P6 + 2), ALIGN),
 ])
@@ -208,8 +209,85 @@ def test_fused_mlp_rejections():
     assert L.mx_fused_mlp_fwd(ctypes.byref(a), None) == ALIGN
     st = L.mx_fused_mlp_fwd(ctypes.byref(mlp_fwd_args()), None)
     assert st in (OK, DEVICE)
+    # X rows [M] x K=D in E4M3 past 2^31 bytes: the GEMM's 32-bit offsets cannot reach them
+    assert L.mx_fused_mlp_fwd(ctypes.byref(mlp_fwd_args(M=1 << 20, D=4096, fmt=mx.E4M3, mode=mx.RCEIL, had=0)),
+                              None) == OVERFLOW
     b = mx.MlpBwdArgs()
     assert L.mx_fused_mlp_bwd(ctypes.byref(b), None) == NULL
+
+
+def mlp_bwd_args(**kw):
+    base = dict(M=256, D=256, F=512, fmt=mx.E2M3, mode=mx.FLOOR, had=1, acc=0, db1=P6, part=P7)
+    base.update(kw)
+    packs = [mx.Packed(P * (10 + 2 * i), P * (11 + 2 * i)) for i in range(8)]
+    return mx.MlpBwdArgs(base["M"], base["D"], base["F"], base["fmt"], base["mode"], base["had"], base["acc"],
+                         P, P2, *packs[:4], P3, P4, P5, P8, base["db1"], base["part"], *packs[4:])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=100), SHAPE), (dict(D=0, F=300), SHAPE), (dict(F=-256), SHAPE),
+    (dict(fmt=mx.E2M1, had=1), FORMAT), (dict(fmt=mx.E2M3, mode=mx.RCEIL), FORMAT), (dict(fmt=7), FORMAT),
+    (dict(acc=2), FORMAT),
+    (dict(part=None), NULL),                                  # a bias gradient needs its partials buffer
+    (dict(db1=P6 + 4), ALIGN), (dict(part=P7 + 8), ALIGN),
+    (dict(M=1 << 20, D=4096, fmt=mx.E4M3, mode=mx.RCEIL, had=0), OVERFLOW),
+])
+def test_fused_mlp_bwd_rejections(kw, want):
+    assert mx.lib().mx_fused_mlp_bwd(ctypes.byref(mlp_bwd_args(**kw)), None) == want
+
+
+def test_fused_mlp_bwd_rejects_each_missing_pointer_and_misaligned_pack():
+    L = mx.lib()
+    for name in ("dY", "h", "da", "dX", "dW1", "dW2"):
+        a = mlp_bwd_args()
+        setattr(a, name, None)
+        assert L.mx_fused_mlp_bwd(ctypes.byref(a), None) == NULL, name
+    for name in ("Xc", "W1c", "W2c", "ac", "dYr", "dYc", "dhr", "dhc"):
+        a = mlp_bwd_args()
+        setattr(a, name, mx.Packed(P, None))
+        assert L.mx_fused_mlp_bwd(ctypes.byref(a), None) == NULL, name
+        a = mlp_bwd_args()
+        setattr(a, name, mx.Packed(P + 4, P2))
+        assert L.mx_fused_mlp_bwd(ctypes.byref(a), None) == ALIGN, name
+
+
+def test_fused_mlp_bwd_valid_args_need_the_device():
+    for kw in (dict(), dict(db1=None, part=None), dict(acc=1), dict(M=0)):
+        st = mx.lib().mx_fused_mlp_bwd(ctypes.byref(mlp_bwd_args(**kw)), None)
+        assert st in (OK, DEVICE), kw
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def gt(tile_m, tile_n, M=768, N=768, K=512):
+    return mx.lib().mx_gemm_tiled(P, P2, P3, P4, M, N, K, mx.E2M1, None, mx.BF16, P5, mx.BF16, N, tile_m, tile_n, None)
+
+
+def test_gemm_tiled_rejects_shapes_it_cannot_serve():
+    assert gt(128, 128) == SHAPE                  # not one of the tile shapes
+    assert gt(256, 192, M=512, N=768) == OK or gt(256, 192, M=512, N=768) == DEVICE
+    assert gt(192, 256, M=512, N=768) == SHAPE    # 192 does not divide M = 512
+    assert gt(256, 64) == SHAPE
+    for tile in ((0, 0), (256, 256), (256, 192), (192, 256), (192, 192), (256, 128)):
+        st = gt(*tile)
+        assert st in (OK, DEVICE), tile
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def test_binding_refuses_host_tensors_and_strided_views():
+    # buffers of sufficient size that the kernels could not read correctly:
+    # a host tensor (its address is not device memory) and a strided view
+    import torch
+    M, N, K = 256, 256, 256
+    a, b = mx.alloc_packed(M, K, mx.E2M1, device="cpu"), mx.alloc_packed(N, K, mx.E2M1, device="cpu")
+    C = torch.empty(M, N, dtype=torch.int16)
+    with pytest.raises(mx.MXError) as e:
+        mx.gemm(a, b, M, N, K, mx.E2M1, C)
+    assert e.value.status == DEVICE and "not on a GPU" in str(e.value)
+    with pytest.raises(mx.MXError) as e:
+        mx.quantize(torch.empty(K, M, dtype=torch.int16).t(), M, K, mx.E2M1, mx.FLOOR, row=a)
+    assert e.value.status == SHAPE and "strided view" in str(e.value)
 
 
 def test_binding_rejects_short_buffers_before_the_call():

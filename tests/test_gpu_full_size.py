@@ -27,6 +27,7 @@ import torch
 
 from microscaling_block_scaled_mx_amd import inputs as I
 from packed_layout import unblocked, untiled
+from parity_checks import REL, bf16_close, bf16_rel_err
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
@@ -34,7 +35,6 @@ if ROOT not in sys.path:
 
 pytestmark = pytest.mark.gpu
 
-REL = 2e-3
 NS = 64  # sampled rows / columns per checked tensor (a multiple of 32)
 
 
@@ -107,11 +107,7 @@ def assert_rows_equal(got, want, what):
 
 
 def assert_close(got_bf16, ref64, what):
-    g = I.bf16_bits_to_f32(got_bf16).astype(np.float64)
-    bound = REL * np.max(np.abs(ref64)) + np.abs(ref64) * 2.0 ** -8
-    bad = np.abs(g - ref64) > bound
-    assert not np.any(bad), f"{what}: {bad.sum()} outputs outside the bound, worst " \
-                            f"{np.max(np.abs(g - ref64) / np.max(np.abs(ref64))):.3g}"
+    assert bf16_close(got_bf16, ref64), f"{what}: outside the bound, worst {bf16_rel_err(got_bf16, ref64):.3g}"
 
 
 def gemm_grid(orc, a, b, K, fmt, bias=None):

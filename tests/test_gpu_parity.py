@@ -14,10 +14,10 @@ import torch
 
 from microscaling_block_scaled_mx_amd import inputs as I
 from packed_layout import blocked, blocked_shape, tiled, tiled_shape, unblocked, untiled
+from parity_checks import REL, assert_packs_equal, bf16_close, bf16_rel_err, gemm_rel_err
 
 pytestmark = pytest.mark.gpu
 
-REL = 2e-3
 FMT_CASES = [(1, 0, False), (2, 0, True), (2, 0, False), (3, 1, False), (3, 0, False)]
 
 
@@ -61,15 +61,6 @@ def with_specials(x: np.ndarray, rng) -> np.ndarray:
     x[5, 96:128] = 0x0080               # smallest normal
     x[35, 3] = 0xFF80                   # -Inf (second row block for the col pass)
     return x
-
-
-def assert_packs_equal(got: dict, want: dict, fmt, keys):
-    for k in keys:
-        g, w = got[k], want[k]
-        assert g.shape == w.shape, (k, g.shape, w.shape)
-        if not np.array_equal(g, w):
-            bad = np.argwhere(g != w)
-            raise AssertionError(f"{k}: {len(bad)} mismatching bytes, first at {bad[:5].tolist()}")
 
 
 def assert_f32_bitwise(got: np.ndarray, want: np.ndarray):
@@ -123,7 +114,7 @@ def test_quantize_parity_identity_gelu_dgelu(mxl, orc, fmt, mode, had, pro):
     aux = I.bf16_normal(rng, (R, C), 3.0) if pro == 2 else None
     got = gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, colsum=True)
     want = orc.quantize(x, R, C, fmt, mode, had, pro=pro, aux=aux, row=True, col=True, colsum=True)
-    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
     assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
     assert_f32_bitwise(got["colsum"], want["colsum"])
 
@@ -145,7 +136,7 @@ def test_quantize_whole_and_ragged_tiles(mxl, orc, fmt, mode, had, pro):
         aux = I.bf16_normal(rng, (R, C), 3.0) if pro == 2 else None
     got = gpu_quantize(mxl, x, aux, R, C, fmt, mode, had, pro, colsum=True)
     want = orc.quantize(x, R, C, fmt, mode, had, pro=pro, aux=aux, row=True, col=True, colsum=True)
-    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
     assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
     assert_f32_bitwise(got["colsum"], want["colsum"])
 
@@ -158,11 +149,11 @@ def test_quantize_parity_swiglu_dswiglu(mxl, orc, fmt, mode):
     H[0, 0] = 0x7FC0
     got = gpu_quantize(mxl, H, None, R, F, fmt, mode, False, 3)
     want = orc.quantize(H, R, F, fmt, mode, False, pro=3, row=True, col=True)
-    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
     dz = I.bf16_normal(rng, (R, F), 1.0)
     got = gpu_quantize(mxl, dz, H, R, 2 * F, fmt, mode, False, 4, colsum=True)
     want = orc.quantize(dz, R, 2 * F, fmt, mode, False, pro=4, aux=H, row=True, col=True, colsum=True)
-    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
     assert_f32_bitwise(got["colsum"], want["colsum"])
 
 
@@ -210,7 +201,19 @@ def test_quantize_many_matches_quantize_and_oracle(mxl, orc, fmt, mode, had, pro
     want = orc.quantize(xs[1], R, C, fmt, mode, had, pro=pro, row=True, col=True)
     got = {"row_codes": untiled(host(many[1][0]), C, bits), "row_scales": unblocked(host(many[1][1]), C // 32),
            "col_codes": untiled(host(many[1][2]), R, bits), "col_scales": unblocked(host(many[1][3]), R // 32)}
-    assert_packs_equal(got, want, fmt, ["row_codes", "row_scales", "col_codes", "col_scales"])
+    assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
+
+
+def test_binding_refuses_strided_device_views(mxl):
+    # a transposed or column-sliced view has the wrong row pitch for the
+    # kernels' dense row-major reads and writes: refused before the call
+    M, N, K = 256, 256, 256
+    a, b = mxl.alloc_packed(M, K, mxl.E2M1), mxl.alloc_packed(N, K, mxl.E2M1)
+    C = bf16_empty(M, 2 * N)
+    with pytest.raises(mxl.MXError, match="strided view"):
+        mxl.gemm(a, b, M, N, K, mxl.E2M1, C[:, :N])
+    with pytest.raises(mxl.MXError, match="strided view"):
+        mxl.quantize(bf16_empty(K, M).t(), M, K, mxl.E2M1, mxl.FLOOR, row=a)
 
 
 def test_quantize_zero_size_is_a_noop(mxl):
@@ -221,7 +224,7 @@ def test_quantize_zero_size_is_a_noop(mxl):
 
 
 # ------------------------------------------------------------------ GEMM
-def gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed, bias=False):
+def gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed, bias=False, tile=None):
     rng = np.random.default_rng(seed)
     A = I.bf16_normal(rng, (M, K), 1.0)
     B = I.bf16_normal(rng, (N, K), 0.02)
@@ -235,8 +238,12 @@ def gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed, bias=False):
     c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     c16 = bf16_empty(M, N)
     bd = dev(b) if b is not None else None
-    mxl.gemm(a, bb, M, N, K, fmt, c32, bias=bd, c_dtype=mxl.F32)
-    mxl.gemm(a, bb, M, N, K, fmt, c16, bias=bd, c_dtype=mxl.BF16)
+    if tile is None:
+        mxl.gemm(a, bb, M, N, K, fmt, c32, bias=bd, c_dtype=mxl.F32)
+        mxl.gemm(a, bb, M, N, K, fmt, c16, bias=bd, c_dtype=mxl.BF16)
+    else:
+        mxl.gemm_tiled(a, bb, M, N, K, fmt, c32, tile, bias=bd, c_dtype=mxl.F32)
+        mxl.gemm_tiled(a, bb, M, N, K, fmt, c16, tile, bias=bd, c_dtype=mxl.BF16)
     return ref, host(c32), host(c16)
 
 
@@ -247,21 +254,20 @@ def test_gemm_parity(mxl, orc, fmt, mode, had, shape):
     if M % 256:
         M = 256 * ((M + 255) // 256)
     ref, c32, c16 = gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed=M + N + K + fmt, bias=(K == 768))
-    err = np.max(np.abs(c32.astype(np.float64) - ref)) / np.max(np.abs(ref))
+    err = gemm_rel_err(c32, ref)
     assert err <= REL, err
     want16 = I.f32_to_bf16_bits(c32)
     assert np.array_equal(c16, want16)
 
 
 @pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
-@pytest.mark.parametrize("tile", ["256x256", "256x192", "192x256", "192x192", "256x128"])
-def test_gemm_parity_every_tile_shape(mxl, orc, fmt, mode, had, tile, monkeypatch):
+@pytest.mark.parametrize("tile", [(256, 256), (256, 192), (192, 256), (192, 192), (256, 128)])
+def test_gemm_parity_every_tile_shape(mxl, orc, fmt, mode, had, tile):
     # the dense GEMM picks its tile shape from M, N and the compute-unit
-    # count; force each shape at a size all of them divide
-    monkeypatch.setenv("MX_DENSE_TILE", tile)
+    # count; mx_gemm_tiled forces each shape at a size all of them divide
     M, N, K = 768, 768, 512
-    ref, c32, c16 = gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed=900 + fmt, bias=True)
-    err = np.max(np.abs(c32.astype(np.float64) - ref)) / np.max(np.abs(ref))
+    ref, c32, c16 = gemm_case(mxl, orc, fmt, mode, had, M, N, K, seed=900 + fmt, bias=True, tile=tile)
+    err = gemm_rel_err(c32, ref)
     assert err <= REL, err
     assert np.array_equal(c16, I.f32_to_bf16_bits(c32))
 
@@ -390,18 +396,6 @@ def run_mlp(mxl, X, W1, b1, W2, dY, M, D, F, fmt=2, mode=0, had=True):
                       t["dW2"], t["db1"], t["part"], t["dYr"], t["dYc"], t["dhr"], t["dhc"], fmt=fmt,
                       scale_mode=mode, hadamard=had)
     return t
-
-
-def rel_err(got_bf16, ref64):
-    g = I.bf16_bits_to_f32(got_bf16).astype(np.float64)
-    return np.max(np.abs(g - ref64)) / max(np.max(np.abs(ref64)), 1e-300)
-
-
-def bf16_close(got_bf16, ref64):
-    """|gpu - ref| <= 2e-3 max|ref| + half a bf16 ulp of ref (one rounding of the store)."""
-    g = I.bf16_bits_to_f32(got_bf16).astype(np.float64)
-    half_ulp = np.abs(ref64) * 2.0 ** -8
-    return np.all(np.abs(g - ref64) <= REL * np.max(np.abs(ref64)) + half_ulp)
 
 
 @pytest.mark.parametrize("fmt,mode,had", [(2, 0, True), (1, 0, False), (3, 1, False)])
@@ -653,7 +647,7 @@ def test_quantize_sr_parity(mxl, orc):
     cc, cs = untiled(host(colp[0]), R, 4), unblocked(host(colp[1]), R // 32)
     for z in range(B):
         want = orc.quantize_sr(xs[z], R, C, seed, row=True, col=True, index_base=z * R * C)
-        assert_packs_equal(dict(row_codes=rc[z], row_scales=rs[z], col_codes=cc[z], col_scales=cs[z]), want, 1,
+        assert_packs_equal(dict(row_codes=rc[z], row_scales=rs[z], col_codes=cc[z], col_scales=cs[z]), want,
                            ("row_codes", "row_scales", "col_codes", "col_scales"))
         rn = orc.quantize(xs[z], R, C, 1, 0, row=False, col=False, colsum=True)
         assert_f32_bitwise(host(part)[z], rn["colsum_partials"])
@@ -775,7 +769,7 @@ def test_prologue_pack_over_every_bf16_input(mxl, orc, pro):
         x, aux = np.ascontiguousarray(np.concatenate([allb, I.bf16_normal(rng, (R, C))], 1)), None
     got = gpu_quantize(mxl, x, aux, R, C, 2, 0, True, pro, colsum=True)
     want = orc.quantize(x, R, C, 2, 0, True, pro=pro, aux=aux, row=True, col=True, colsum=True)
-    assert_packs_equal(got, want, 2, ("row_codes", "row_scales", "col_codes", "col_scales"))
+    assert_packs_equal(got, want, ("row_codes", "row_scales", "col_codes", "col_scales"))
     assert_f32_bitwise(got["colsum_partials"], want["colsum_partials"])
 
 
