@@ -71,7 +71,8 @@ typedef enum {
   MX_ERR_OFFSETS = 5,        /* group offsets break their contract (checked only when asked to) */
   MX_ERR_INDEX_OVERFLOW = 6, /* a tensor exceeds 2^31 bytes (the kernels use 32-bit offsets) */
   MX_ERR_DEVICE = 7,         /* no current device, or the current device is not gfx950 */
-  MX_ERR_LAUNCH = 8          /* the HIP runtime reported an error when enqueuing */
+  MX_ERR_LAUNCH = 8,         /* the HIP runtime reported an error when enqueuing */
+  MX_ERR_SCRATCH = 9         /* the call needs more than the library's static scratch holds (mx_quantize_noalloc) */
 } mx_status;
 
 /* ---------------------------------------------------------------- enums */
@@ -158,6 +159,34 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
                 int scale_mode, int hadamard, int prologue, void* row_codes, void* row_scales,
                 void* col_codes, void* col_scales, float* colsum_partials, float* colsum,
                 void* stream);
+
+/*
+ * mx_quantize_noalloc -- mx_quantize for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  The column-sum partials, the one work buffer of
+ * mx_quantize, live in a static device array of the library instead of a
+ * caller buffer; the caller passes only inputs and outputs.  Arguments and
+ * results are those of mx_quantize with colsum_partials taken away: colsum
+ * (fp32 [batch][C], or NULL for none) is bitwise what mx_quantize returns.
+ *
+ * Limit: batch * (R/32) * C * 4 bytes of partials must fit the static array
+ * of MX_NOALLOC_SCRATCH_BYTES (16 MiB: 4M partials, e.g. R = 8192 tokens at
+ * C = 16384 columns); a larger call returns MX_ERR_SCRATCH and enqueues
+ * nothing.  The array is allocated once per GPU when the library is loaded
+ * and stays until the process ends.  The call itself never allocates: no
+ * hipMalloc, hipFree or allocating library routine, on any path.
+ *
+ * Every call on one GPU uses that GPU's one array.  Each call writes every
+ * partial it reads before reading it, in stream order, so nothing needs
+ * clearing; but two calls whose work overlaps in time on one GPU (different
+ * streams, or host threads) race on the array and give wrong column sums.
+ * Order such calls on one stream, or use mx_quantize with separate buffers.
+ * Errors: those of mx_quantize, plus MX_ERR_SCRATCH.
+ */
+#define MX_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mx_quantize_noalloc(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt,
+                        int scale_mode, int hadamard, int prologue, void* row_codes, void* row_scales,
+                        void* col_codes, void* col_scales, float* colsum, void* stream);
 
 /*
  * mx_quantize_sr -- mx_quantize for MXFP4 gradient packs with stochastic

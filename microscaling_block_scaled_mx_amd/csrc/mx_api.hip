@@ -157,6 +157,38 @@ int gemm_launch(const void* ac, const void* as, const void* bc, const void* bs, 
   return launched(mx::launch_gemm(p, fmt, mx::kDense, accumulate ? mx::kEpiAccum : mx::kEpiStore, s));
 }
 
+// ---------------------------------------------------------------- static scratch
+// The work buffer of mx_quantize_noalloc: one copy per GPU, allocated with
+// the code object and kept until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+static_assert(MX_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, or nullptr until looked up
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device), or nullptr if the runtime cannot give it.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 bool packed_ok(const mx_packed& q) { return q.codes && q.scales; }
 bool packed_aligned(const mx_packed& q) { return aligned16(q.codes) && aligned16(q.scales); }
 
@@ -173,6 +205,27 @@ int mx_quantize(const void* x, const void* aux, int64_t batch, int64_t R, int64_
   if ((st = check_device()) != MX_OK) return st;
   return quantize_launch(x, aux, batch, R, C, fmt, scale_mode, hadamard, prologue, row_codes, row_scales,
                          col_codes, col_scales, colsum_partials, colsum, static_cast<hipStream_t>(stream));
+}
+
+int mx_quantize_noalloc(const void* x, const void* aux, int64_t batch, int64_t R, int64_t C, int fmt,
+                        int scale_mode, int hadamard, int prologue, void* row_codes, void* row_scales,
+                        void* col_codes, void* col_scales, float* colsum, void* stream) {
+  // the partials pointer only stands for "present" in the checks below; it
+  // is replaced by the scratch address before any launch
+  float* const marker = colsum ? colsum : nullptr;
+  int st = validate_quantize(x, aux, batch, R, C, fmt, scale_mode, hadamard, prologue, row_codes, row_scales,
+                             col_codes, col_scales, marker, colsum);
+  if (st != MX_OK) return st;
+  if (colsum && (batch * (R / 32) * C > (int64_t)(MX_NOALLOC_SCRATCH_BYTES / sizeof(float))))
+    return MX_ERR_SCRATCH;
+  if ((st = check_device()) != MX_OK) return st;
+  float* part = nullptr;
+  if (colsum) {
+    part = static_cast<float*>(scratch_ptr());
+    if (!part) return MX_ERR_DEVICE;
+  }
+  return quantize_launch(x, aux, batch, R, C, fmt, scale_mode, hadamard, prologue, row_codes, row_scales,
+                         col_codes, col_scales, part, colsum, static_cast<hipStream_t>(stream));
 }
 
 int mx_quantize_sr(const void* x, int64_t batch, int64_t R, int64_t C, void* row_codes, void* row_scales,
@@ -558,6 +611,7 @@ const char* mx_status_str(int status) {
     case MX_ERR_INDEX_OVERFLOW: return "MX_ERR_INDEX_OVERFLOW: a size exceeds what one launch can index";
     case MX_ERR_DEVICE: return "MX_ERR_DEVICE: no gfx950 device is current";
     case MX_ERR_LAUNCH: return "MX_ERR_LAUNCH: the HIP runtime failed to enqueue";
+    case MX_ERR_SCRATCH: return "MX_ERR_SCRATCH: the call needs more than the library's static scratch holds";
     default: return "unknown mx status";
   }
 }

@@ -22,7 +22,9 @@ EPI_NONE, EPI_SWIGLU, EPI_DSWIGLU = 0, 1, 2
 BITS = {E2M1: 4, E2M3: 6, E4M3: 8}
 
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_FORMAT",
-          5: "MX_ERR_OFFSETS", 6: "MX_ERR_INDEX_OVERFLOW", 7: "MX_ERR_DEVICE", 8: "MX_ERR_LAUNCH"}
+          5: "MX_ERR_OFFSETS", 6: "MX_ERR_INDEX_OVERFLOW", 7: "MX_ERR_DEVICE", 8: "MX_ERR_LAUNCH",
+          9: "MX_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MX_NOALLOC_SCRATCH_BYTES
 
 
 class MXError(RuntimeError):
@@ -96,6 +98,8 @@ def lib():
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.mx_quantize.restype = ci
         L.mx_quantize.argtypes = [vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.mx_quantize_noalloc.restype = ci
+        L.mx_quantize_noalloc.argtypes = [vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp]
         L.mx_quantize_sr.restype = ci
         L.mx_quantize_sr.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
         L.mx_quantize_many.restype = ci
@@ -218,6 +222,25 @@ def quantize(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = Fals
                            _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
                            _ptr(colsum_partials), _ptr(colsum), _stream(stream))
     _check(st, "mx_quantize")
+
+
+def quantize_noalloc(x, R: int, C: int, fmt: int, scale_mode: int, hadamard: bool = False,
+                     prologue: int = PRO_IDENTITY, aux=None, row=None, col=None, colsum=None, batch: int = 1,
+                     stream=None):
+    """mx_quantize_noalloc: mx_quantize whose column-sum partials live in the
+    library's static device scratch (the call allocates nothing)."""
+    in_cols = 2 * C if prologue == PRO_SWIGLU else (C // 2 if prologue == PRO_DSWIGLU else C)
+    _need(x, 2 * batch * R * in_cols, "quantize_noalloc input")
+    if prologue in (PRO_DGELU_TANH, PRO_DSWIGLU):
+        _need(aux, 2 * batch * R * C, "quantize_noalloc aux")
+    _need_packed(row, R, C, fmt, "quantize_noalloc row", batch)
+    _need_packed(col, C, R, fmt, "quantize_noalloc col", batch)
+    _need(colsum, 4 * batch * C, "colsum")
+    st = lib().mx_quantize_noalloc(_ptr(x), _ptr(aux), batch, R, C, fmt, scale_mode, int(hadamard), prologue,
+                                   _ptr(row[0]) if row else None, _ptr(row[1]) if row else None,
+                                   _ptr(col[0]) if col else None, _ptr(col[1]) if col else None,
+                                   _ptr(colsum), _stream(stream))
+    _check(st, "mx_quantize_noalloc")
 
 
 def quantize_sr(x, R: int, C: int, seed: int, row=None, col=None, colsum_partials=None, colsum=None,

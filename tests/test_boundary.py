@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_sizes():
     assert mx.status_str(0) == "MX_OK"
-    for st in range(1, 9):
+    for st in range(1, 10):
         assert mx.status_str(st).startswith(mx.STATUS[st])
     L = mx.lib()
     assert L.mx_codes_bytes(mx.E2M1, 256, 256) == 256 * 128
@@ -340,6 +340,37 @@ def test_gemm_many_valid_args_need_the_device():
                        ([{}, dict(accumulate=1)], mx.E2M1)):
         st = gmany(items, fmt=fmt)
         assert st in (OK, DEVICE)
+        if not mx.lib().mx_device_supported(0):
+            assert st == DEVICE
+
+
+def qna(**kw):
+    a = dict(x=P, aux=None, batch=1, R=64, C=128, fmt=mx.E2M1, mode=mx.FLOOR, had=0, pro=mx.PRO_IDENTITY,
+             rc=P2, rs=P3, cc=P4, cs=P5, sum=P6)
+    a.update(kw)
+    return mx.lib().mx_quantize_noalloc(a["x"], a["aux"], a["batch"], a["R"], a["C"], a["fmt"], a["mode"],
+                                        a["had"], a["pro"], a["rc"], a["rs"], a["cc"], a["cs"], a["sum"], None)
+
+
+SCRATCH = 9
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(rc=None), NULL), (dict(rc=None, rs=None, cc=None, cs=None, sum=None), NULL),
+    (dict(pro=mx.PRO_DGELU_TANH), NULL), (dict(fmt=mx.E2M1, had=1), FORMAT), (dict(R=48), SHAPE),
+    (dict(sum=P6 + 4), ALIGN),
+    # partials of (R/32) * C * batch floats past the 16 MiB static array
+    (dict(R=8192, C=16384 + 32), SCRATCH), (dict(batch=3, R=4096, C=16384), SCRATCH),
+])
+def test_quantize_noalloc_rejections(kw, want):
+    assert qna(**kw) == want
+
+
+def test_quantize_noalloc_valid_args_need_the_device():
+    # the largest call the array holds, no colsum (no scratch), and R = 0
+    for kw in (dict(), dict(R=8192, C=16384), dict(sum=None), dict(R=0), dict(batch=2, R=4096, C=16384)):
+        st = qna(**kw)
+        assert st in (OK, DEVICE), (kw, st)
         if not mx.lib().mx_device_supported(0):
             assert st == DEVICE
 
