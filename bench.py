@@ -553,17 +553,46 @@ def only(mx, spec, steps, warmup, T):
         C = torch.empty((M, N), dtype=torch.int16, device="cuda")
         us = graph_time(lambda r: mx.gemm(pa, pb, M, N, K, fmt, C), reps=steps)
         print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
-    elif kind == "gemms":  # the linear step's three GEMMs in one launch (FMT:M:N:K as the step)
-        M, N, K = (int(v) for v in dims)
+    elif kind == "gemmt":  # one GEMM with a forced tiling: FMT:M:N:K:BM:BN:WG_PER_CU[:rand|zero]
+        M, N, K, bm, bn, occ = (int(v) for v in dims[:6])
+        data = dims[6] if len(dims) > 6 else "rand"
         g = torch.Generator(device="cuda").manual_seed(7)
-        P = lambda r, k: tuple(torch.randint(118 if i else 0, 130 if i else 256, t.shape, dtype=torch.uint8,
-                                             device="cuda", generator=g)
-                               for i, t in enumerate(mx.alloc_packed(r, k, fmt)))
+
+        def fill(i, t):
+            if i:
+                return torch.randint(118, 130, t.shape, dtype=torch.uint8, device="cuda", generator=g)
+            if data == "zero":
+                return torch.zeros_like(t)
+            return torch.randint(0, 256, t.shape, dtype=torch.uint8, device="cuda", generator=g)
+        pa, pb = (tuple(fill(i, t) for i, t in enumerate(mx.alloc_packed(r, K, fmt))) for r in (M, N))
+        C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        us = graph_time(lambda r: mx.gemm_tiled(pa, pb, M, N, K, fmt, C, (bm, bn, occ)), reps=steps)
+        print(json.dumps({"only": spec, "data": data, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}),
+              flush=True)
+    elif kind == "gemms":  # the linear step's three GEMMs in one launch (FMT:M:N:K as the step)
+        # optional 5th field: operand data -- rand (random code bytes, the
+        # default), zero (all codes +0) or const (one non-zero code byte
+        # everywhere): the matrix cores' clock under load depends on how
+        # many operand bits toggle, so the three bound what data costs
+        M, N, K = (int(v) for v in dims[:3])
+        data = dims[3] if len(dims) > 3 else "rand"
+        g = torch.Generator(device="cuda").manual_seed(7)
+
+        def fill(i, t):
+            if i:  # scales: E8M0 bytes near 2^0
+                return torch.randint(118, 130, t.shape, dtype=torch.uint8, device="cuda", generator=g)
+            if data == "zero":
+                return torch.zeros_like(t)
+            if data == "const":
+                return torch.full_like(t, 0x5A)
+            return torch.randint(0, 256, t.shape, dtype=torch.uint8, device="cuda", generator=g)
+        P = lambda r, k: tuple(fill(i, t) for i, t in enumerate(mx.alloc_packed(r, k, fmt)))
         trio = [(P(M, K), P(N, K), M, N, K), (P(M, N), P(K, N), M, K, N), (P(N, M), P(K, M), N, K, M)]
         items = [dict(a=a, b=b, M=m, N=n, K=k, c=torch.empty((m, n), dtype=torch.int16, device="cuda"))
                  for a, b, m, n, k in trio]
         us = graph_time(lambda r: mx.gemm_many(items, fmt), reps=steps)
-        print(json.dumps({"only": spec, "us": us, "tflops": 3 * 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
+        print(json.dumps({"only": spec, "data": data, "us": us, "tflops": 3 * 2.0 * M * N * K / (us * 1e-6) / 1e12}),
+              flush=True)
     elif kind == "packs":  # the linear step's fused pack: X [M,K], W [N,K], dY [M,N] in one launch
         M, N, K = (int(v) for v in dims)
         rng = np.random.default_rng(7)

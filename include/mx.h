@@ -294,17 +294,21 @@ int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_
                        int c_dtype, int64_t ldc, void* stream);
 
 /*
- * mx_gemm_tiled -- mx_gemm with the output tile shape chosen by the caller:
- * tile_m x tile_n is one of 256x256, 256x192, 192x256, 192x192, 256x128 and
- * must divide M x N (else MX_ERR_SHAPE); 0 x 0 picks the shape as mx_gemm
- * does.  For tuning and for tests that cover every tile shape.  The result
- * differs from mx_gemm's only by the binary32 accumulation order across
- * the K stages of a tile, i.e. within the GEMM tolerance; with mx_gemm's
- * own shape it is bitwise mx_gemm's.  Other arguments and errors as mx_gemm.
+ * mx_gemm_tiled -- mx_gemm with the output tiling chosen by the caller:
+ * tile_m x tile_n output tiles with wg_per_cu workgroups resident per
+ * compute unit, one of
+ *   256x256, 256x192, 192x256, 192x192, 256x128 at wg_per_cu = 1, and
+ *   256x128, 128x256, 192x192 at wg_per_cu = 2 (each workgroup then takes at
+ *   most half the LDS and registers, and keeps a ring of two K stages);
+ * the tile must divide M x N, else MX_ERR_SHAPE.  0, 0, 0 picks the tiling
+ * as mx_gemm does.  For tuning and for tests that cover every tiling.  The
+ * result differs from mx_gemm's only by the binary32 accumulation order of
+ * the K steps, i.e. within the GEMM tolerance; with mx_gemm's own tiling it
+ * is bitwise mx_gemm's.  Other arguments and errors as mx_gemm.
  */
 int mx_gemm_tiled(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
                   int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
-                  int tile_m, int tile_n, void* stream);
+                  int tile_m, int tile_n, int wg_per_cu, void* stream);
 
 /*
  * mx_gemm_many -- several GEMMs of one format in a single launch, with the

@@ -319,12 +319,12 @@ int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_
 
 int mx_gemm_tiled(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
                   int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
-                  int tile_m, int tile_n, void* stream) {
+                  int tile_m, int tile_n, int wg_per_cu, void* stream) {
   int st = validate_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc);
   if (st != MX_OK) return st;
   int tile = 0;
-  if (tile_m != 0 || tile_n != 0) {
-    const int i = mx::dense_tile_index(tile_m, tile_n, M, N);
+  if (tile_m != 0 || tile_n != 0 || wg_per_cu != 0) {
+    const int i = mx::dense_tile_index(tile_m, tile_n, wg_per_cu, M, N);
     if (i < 0) return MX_ERR_SHAPE;
     tile = i + 1;
   }

@@ -437,5 +437,12 @@ __device__ __forceinline__ float dswiglu_up_bf16(float dz, float g) {
   float s = sigmoid_ieee(g);
   return round_bf16(dz * (g * s));
 }
+// Both of one element, the sigmoid formed once (bitwise the two above: the
+// reciprocal division equals the IEEE quotient for every divisor it sees).
+__device__ __forceinline__ void dswiglu_pair_bf16(float dz, float g, float u, float& d_gate, float& d_up) {
+  const float s = sigmoid_mx(g);
+  d_up = round_bf16(dz * (g * s));
+  d_gate = round_bf16((dz * u) * (s * (1.0f + g * (1.0f - s))));
+}
 
 }  // namespace mx

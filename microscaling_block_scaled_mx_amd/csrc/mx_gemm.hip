@@ -71,24 +71,38 @@ template <> struct MfmaFmt<kE4M3> { static constexpr int kCode = 0; };
 template <> struct MfmaFmt<kE2M3> { static constexpr int kCode = 2; };
 template <> struct MfmaFmt<kE2M1> { static constexpr int kCode = 4; };
 
-// Threads per workgroup of a BM x BN tile: 8 wavefronts for 256 x 256, else 4.
-constexpr int tile_threads(int bm, int bn) { return (bm == 256 && bn == 256) ? 512 : 256; }
+// Threads per workgroup of a BM x BN tile: 8 wavefronts for 256 x 256 and
+// for the dSwiGLU epilogue's 128 x 256 (two per SIMD, so that the
+// epilogue's long VALU dependency chains of one wavefront interleave with
+// another's), else 4.
+constexpr int tile_threads(int bm, int bn, int epi = 0) {
+  return ((bm == 256 && bn == 256) || (bm == 128 && bn == 256 && epi == 2)) ? 512 : 256;
+}
 
-template <int FMT, int BM, int BN, int MODE, int EPI>
+// OCC: workgroups resident per compute unit (1 or 2).  With 2, each takes at
+// most half the LDS and, per wavefront, half the register file, so that one
+// workgroup's MFMAs run while the other waits on its loads, its barrier or
+// its prologue and epilogue.
+template <int FMT, int BM, int BN, int MODE, int EPI, int OCC = 1>
 struct Cfg {
+  static_assert(OCC == 1 || OCC == 2, "workgroups per compute unit");
+  static constexpr int kLds = 163840 / OCC;              // LDS bytes one workgroup may take
   static constexpr int kBits = FmtTraits<FMT>::kBits;
   // 256 x 256 tiles run 8 wavefronts (2 per SIMD, 2 x 4 over the tile, 128
   // accumulator registers each), so that one wavefront's MFMAs can cover
   // the other's LDS and barrier waits (measured 2-4% faster than 4
   // wavefronts of 256 accumulators each); the other shapes run 4 (2 x 2)
-  static constexpr int kThreads = tile_threads(BM, BN);
+  static constexpr int kThreads = tile_threads(BM, BN, EPI);
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kWavesN = kWaves / 2;  // wavefronts across N (2 across M)
-  // K elements per stage: one 128-element K group (64 / 96 bytes per row)
-  // for E2M1 / E2M3, half of one (64 bytes) for E4M3, so that every stage
-  // fits a ring of three or four in the LDS
-  static constexpr int kBK = FMT == kE4M3 ? 64 : 128;
-  static constexpr int kRowBytes = kBK * kBits / 8;      // 64 / 96 / 64 bytes per row per stage
+  // K elements per stage: one 128-element K group (64 / 96 / 128 bytes per
+  // row); E4M3 tiles whose 128-element stages would not fit a ring of two in
+  // the LDS take half a group (64 bytes) per stage.  Every stage ends in a
+  // workgroup barrier: at 256 x 256, two 128-element E4M3 stages measured
+  // 4-8% faster than four of 64 (MXFP8 16384 x 9216 x 3072: 504 -> 466 us;
+  // the grouped step 954 -> 899 us, same box).
+  static constexpr int kBK = FMT == kE4M3 && 2 * ((BM + BN) * 128 + 2048) > kLds ? 64 : 128;
+  static constexpr int kRowBytes = kBK * kBits / 8;      // 64 / 96 / 128 (or 64) bytes per row per stage
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
   static constexpr int kScaleDw = 1;                     // scale dword (4 blocks of 32 along K) per row per stage
   static constexpr int kSJ = 512 / kThreads;            // scale-dword loads per thread per stage (512 slots)
@@ -111,8 +125,8 @@ struct Cfg {
   static constexpr int kSRegion = kScaleDw * 512 * 4;
   static constexpr int kJunk = (kARem || kBRem) ? 1024 : 0;
   static constexpr int kStage = kARegion + kBRegion + kSRegion;  // bytes per stage
-  static constexpr int kStages = (4 * kStage + kJunk <= 160 * 1024) ? 4 : 3;
-  static_assert(kStages * kStage + kJunk <= 160 * 1024, "three stages fit the LDS");
+  static constexpr int kStages = (4 * kStage + kJunk <= kLds) ? 4 : (3 * kStage + kJunk <= kLds) ? 3 : 2;
+  static_assert(kStages * kStage + kJunk <= kLds, "two stages fit the LDS");
   static constexpr int aoff(int b) { return b * kARegion; }
   static constexpr int boff(int b) { return kStages * kARegion + b * kBRegion; }
   static constexpr int soff(int b) { return kStages * (kARegion + kBRegion) + b * kSRegion; }
@@ -125,12 +139,12 @@ struct Cfg {
   // epilogue staging
   static constexpr int kCPitch = kWN * 2 + 8;         // bf16 store: per-wave kWM x kWN tile
   static constexpr int kZPitch = (BN / 2) * 2 + 8;    // SwiGLU: z tile BM x BN/2
-  static constexpr int kDPitch = BN * 2 + 8;          // dSwiGLU: two BM x BN tiles
+  static constexpr int kDPitch = BN * 2 + 16;         // dSwiGLU: two BM x BN tiles, 16-byte rows
   static constexpr int kEpiBytes = EPI == kEpiSwiglu    ? BM * kZPitch
                                    : EPI == kEpiDSwiglu ? 2 * BM * kDPitch
                                                         : kWaves * kWM * kCPitch;
   static constexpr int kSmem = (kJOff + kJunk > kEpiBytes) ? kJOff + kJunk : kEpiBytes;
-  static_assert(kSmem <= 163840, "LDS budget");
+  static_assert(kSmem <= kLds, "LDS budget");
 };
 
 // Position of logical 16-byte chunk c of row r among the row's NCH stored
@@ -281,9 +295,9 @@ __device__ __forceinline__ void dense_tile(int bid, int tiles_m, int tiles_n, in
   tn = r / gsize;
 }
 
-template <int FMT, int BM, int BN, int MODE, int EPI>
+template <int FMT, int BM, int BN, int MODE, int EPI, int OCC = 1>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, int bz, uint8_t* smem) {
-  using CF = Cfg<FMT, BM, BN, MODE, EPI>;
+  using CF = Cfg<FMT, BM, BN, MODE, EPI, OCC>;
   constexpr int kBits = CF::kBits;
 
   const int t = threadIdx.x;
@@ -503,7 +517,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   constexpr int kMf = CF::kMI * CF::kNJ;  // MFMAs per step
   constexpr int kWin = KS * kMf;          // MFMA slots in a stage's load window
   constexpr int kPart0 = (CF::kLoads + KS - 1) / KS;  // loads in the window's first step
-  static_assert(CF::kLoads <= kWin, "one load per MFMA slot at most");
+  static_assert(CF::kLoads <= 2 * kWin, "two loads per MFMA slot at most");
   static_assert(KS == 1 || KS == 2, "steps per stage");
   // fragment reads (and, across a stage boundary, the scale reads) go in
   // the first three quarters of a step's MFMA slots where the registers
@@ -626,7 +640,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     for (int it0 = 0; it0 < nk; it0 += S) {
       stage(it0, std::integral_constant<int, 0>{});
       if (it0 + 1 < nk) stage(it0 + 1, std::integral_constant<int, 1>{});
-      if (it0 + 2 < nk) stage(it0 + 2, std::integral_constant<int, 2>{});
+      if constexpr (S > 2) {
+        if (it0 + 2 < nk) stage(it0 + 2, std::integral_constant<int, 2 % S>{});
+      }
       if constexpr (S > 3) {
         if (it0 + 3 < nk) stage(it0 + 3, std::integral_constant<int, 3 % S>{});
       }
@@ -881,41 +897,66 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
                                     p.q_col_scales + scale_offset(cz, m / 32, p.F));
     }
   } else {  // kEpiDSwiglu
-    // dz = bf16(acc); with H: d_gate -> tile 0, d_up -> tile 1 (LDS only).
+    // dz = bf16(acc) is staged in LDS tile tg first.  Then each thread takes
+    // 8-column chunks of the tile in row order: H's gate and up chunks of
+    // that row arrive as coalesced 16-byte loads (a wavefront reads whole
+    // 512-byte row segments), dz comes from LDS, d_gate replaces dz in tg
+    // and d_up goes to tile tu.  Both tiles are then quantized rowwise and
+    // columnwise out of LDS.
     uint8_t* tg = smem;
     uint8_t* tu = smem + BM * CF::kDPitch;
     const uint16_t* H = p.aux;
 #pragma unroll
-    for (int j = 0; j < CF::kNJ; ++j)
+    for (int i = 0; i < CF::kMI; ++i)
 #pragma unroll
-      for (int i = 0; i < CF::kMI; ++i)
+      for (int j = 0; j < CF::kNJ; ++j)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int ml = wm * CF::kWM + 32 * i + lrow;
           const int nl = wn * CF::kWN + 32 * j + 8 * e4 + 4 * g;
-          const int64_t m = m0 + ml, n = n0 + nl;
-          // rows past the group's end read the group's last row (loads stay
-          // unconditional, so the compiler need not wait for each at a join)
-          const bool live = m < m_end;
-          const int64_t mh = live ? m : m_end - 1;
-          const uint2 gw = *reinterpret_cast<const uint2*>(H + mh * 2 * p.F + n);
-          const uint2 uw = *reinterpret_cast<const uint2*>(H + mh * 2 * p.F + p.F + n);
-          const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-          const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
-          uint32_t dzb[4], dg[4], du[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float dz = round_bf16(acc[i][j][4 * e4 + q]);
-            dzb[q] = __float_as_uint(dz) >> 16;
-            dg[q] = __float_as_uint(dswiglu_gate_bf16(dz, gv[q], uv[q])) >> 16;
-            du[q] = __float_as_uint(dswiglu_up_bf16(dz, gv[q])) >> 16;
-          }
-          if (p.c && live)
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.F + n) =
-                make_uint2(dzb[0] | (dzb[1] << 16), dzb[2] | (dzb[3] << 16));
-          *reinterpret_cast<uint2*>(tg + ml * CF::kDPitch + nl * 2) = make_uint2(dg[0] | (dg[1] << 16), dg[2] | (dg[3] << 16));
-          *reinterpret_cast<uint2*>(tu + ml * CF::kDPitch + nl * 2) = make_uint2(du[0] | (du[1] << 16), du[2] | (du[3] << 16));
+          const v16f& a = acc[i][j];
+          *reinterpret_cast<uint2*>(tg + ml * CF::kDPitch + nl * 2) =
+              make_uint2(pack_bf16x2(a[4 * e4 + 0], a[4 * e4 + 1]), pack_bf16x2(a[4 * e4 + 2], a[4 * e4 + 3]));
         }
+    constexpr int kChunksRow = BN / 8;                    // 8-column chunks per tile row
+    constexpr int kPer = BM * kChunksRow / kThreads;      // chunks per thread
+    static_assert(BM * kChunksRow % kThreads == 0, "whole chunks per thread");
+    // every H load of this thread in flight at once; rows past the group's
+    // end (none while groups are 128-row multiples and BM = 128) read its
+    // last row and are never stored
+    uint4 hg[kPer], hu[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int q = t + kThreads * k, row = q / kChunksRow, ch = q % kChunksRow;
+      const int64_t m = m0 + row;
+      const uint16_t* hrow = H + (m < m_end ? m : m_end - 1) * 2 * p.F + n0 + 8 * ch;
+      hg[k] = *reinterpret_cast<const uint4*>(hrow);
+      hu[k] = *reinterpret_cast<const uint4*>(hrow + p.F);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int q = t + kThreads * k, row = q / kChunksRow, ch = q % kChunksRow;
+      uint4* zp = reinterpret_cast<uint4*>(tg + row * CF::kDPitch + 16 * ch);
+      const uint4 zw = *zp;
+      const uint32_t zs[4] = {zw.x, zw.y, zw.z, zw.w};
+      const uint32_t gs[4] = {hg[k].x, hg[k].y, hg[k].z, hg[k].w};
+      const uint32_t us[4] = {hu[k].x, hu[k].y, hu[k].z, hu[k].w};
+      uint32_t dg[4], du[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float g0, g1, u0, u1;
+        dswiglu_pair_bf16(bf16_lo(zs[w]), bf16_lo(gs[w]), bf16_lo(us[w]), g0, u0);
+        dswiglu_pair_bf16(bf16_hi(zs[w]), bf16_hi(gs[w]), bf16_hi(us[w]), g1, u1);
+        dg[w] = (__float_as_uint(g0) >> 16) | (__float_as_uint(g1) & 0xffff0000u);
+        du[w] = (__float_as_uint(u0) >> 16) | (__float_as_uint(u1) & 0xffff0000u);
+      }
+      const int64_t m = m0 + row;
+      if (p.c && m < m_end)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.c) + m * p.F + n0 + 8 * ch) = zw;
+      *zp = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+      *reinterpret_cast<uint4*>(tu + row * CF::kDPitch + 16 * ch) = make_uint4(du[0], du[1], du[2], du[3]);
+    }
     __syncthreads();
     constexpr int QB = FmtTraits<FMT>::kBits;
     const int64_t W = 2 * p.F;  // dH width
@@ -952,21 +993,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
 
 // One launch, one GEMM (or one grouped GEMM): workgroup (x, y, z) computes
 // tile (x, y) of group z.
-template <int FMT, int BM, int BN, int MODE, int EPI>
-__global__ __launch_bounds__(tile_threads(BM, BN), 1) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg<FMT, BM, BN, MODE, EPI>::kSmem];
-  gemm_tile<FMT, BM, BN, MODE, EPI>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+template <int FMT, int BM, int BN, int MODE, int EPI, int OCC = 1>
+__global__ __launch_bounds__(tile_threads(BM, BN, EPI), OCC) void gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg<FMT, BM, BN, MODE, EPI, OCC>::kSmem];
+  gemm_tile<FMT, BM, BN, MODE, EPI, OCC>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
 
-// The dense tile shapes, in the order of GemmMany::shape.
-constexpr int kDenseShapes[5][2] = {{256, 256}, {256, 192}, {192, 256}, {192, 192}, {256, 128}};
+// The dense tile shapes {BM, BN, workgroups per compute unit}, in the order
+// of GemmMany::shape.
+constexpr int kNumDense = 8;
+constexpr int kDenseShapes[kNumDense][3] = {{256, 256, 1}, {256, 192, 1}, {192, 256, 1}, {192, 192, 1},
+                                            {256, 128, 1}, {256, 128, 2}, {128, 256, 2}, {192, 192, 2}};
 
 template <int FMT, int SH>
-using DenseCfg = Cfg<FMT, kDenseShapes[SH][0], kDenseShapes[SH][1], kDense, kEpiStore>;
+using DenseCfg = Cfg<FMT, kDenseShapes[SH][0], kDenseShapes[SH][1], kDense, kEpiStore, kDenseShapes[SH][2]>;
 
 template <int FMT, int SH>
 __device__ __forceinline__ void dense_tile_sh(const GemmParams& p, int local, uint8_t* smem) {
-  gemm_tile<FMT, kDenseShapes[SH][0], kDenseShapes[SH][1], kDense, kEpiStore>(p, local, 0, 0, smem);
+  gemm_tile<FMT, kDenseShapes[SH][0], kDenseShapes[SH][1], kDense, kEpiStore, kDenseShapes[SH][2]>(p, local, 0, 0,
+                                                                                                    smem);
 }
 
 // Several dense GEMMs in one launch: workgroup w computes tile
@@ -974,8 +1019,9 @@ __device__ __forceinline__ void dense_tile_sh(const GemmParams& p, int local, ui
 // tile shape, SA or SB (indices into kDenseShapes); the branch is uniform
 // across the workgroup.  Both shapes run the same number of wavefronts.
 template <int FMT, int SA, int SB>
-__global__ __launch_bounds__(tile_threads(kDenseShapes[SA][0], kDenseShapes[SA][1]), 1) void gemm_many_kernel(GemmMany m) {
+__global__ __launch_bounds__(tile_threads(kDenseShapes[SA][0], kDenseShapes[SA][1]), kDenseShapes[SA][2]) void gemm_many_kernel(GemmMany m) {
   static_assert(DenseCfg<FMT, SA>::kThreads == DenseCfg<FMT, SB>::kThreads, "one workgroup size per launch");
+  static_assert(kDenseShapes[SA][2] == kDenseShapes[SB][2], "one residency per launch");
   constexpr int kA = DenseCfg<FMT, SA>::kSmem, kB = DenseCfg<FMT, SB>::kSmem;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kA > kB ? kA : kB];
   const int w = blockIdx.x;
@@ -986,7 +1032,7 @@ __global__ __launch_bounds__(tile_threads(kDenseShapes[SA][0], kDenseShapes[SA][
   else dense_tile_sh<FMT, SB>(m.p[i], local, smem);
 }
 
-template <int FMT, int BM, int BN, int MODE, int EPI>
+template <int FMT, int BM, int BN, int MODE, int EPI, int OCC = 1>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   dim3 grid;
   if (MODE == kDense) {
@@ -1002,8 +1048,8 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
     grid = dim3((unsigned)(p.N / BN), (unsigned)(p.M / BM), (unsigned)p.G);
   }
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE, EPI>), grid, dim3(Cfg<FMT, BM, BN, MODE, EPI>::kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE, EPI, OCC>), grid, dim3(Cfg<FMT, BM, BN, MODE, EPI, OCC>::kThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 
@@ -1031,9 +1077,9 @@ int dense_shape(int64_t M, int64_t N) {
   const int64_t cus = cu_count();
   int best = -1;
   int64_t best_cost = 0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < kNumDense; ++i) {
     const int bm = kDenseShapes[i][0], bn = kDenseShapes[i][1];
-    if (M % bm || N % bn) continue;
+    if (kDenseShapes[i][2] != 1 || M % bm || N % bn) continue;
     const int64_t tiles = (M / bm) * (N / bn);
     const int64_t cost = ((tiles + cus - 1) / cus) * bm * bn;
     if (best < 0 || cost < best_cost) {
@@ -1047,7 +1093,7 @@ int dense_shape(int64_t M, int64_t N) {
 // The shape a dense launch uses: the caller's (p.tile_shape = 1 + its
 // index), else the one dense_shape picks.
 int dense_shape_of(const GemmParams& p) {
-  return p.tile_shape > 0 && p.tile_shape <= 5 ? p.tile_shape - 1 : dense_shape(p.M, p.N);
+  return p.tile_shape > 0 && p.tile_shape <= kNumDense ? p.tile_shape - 1 : dense_shape(p.M, p.N);
 }
 
 template <int FMT, int EPI>
@@ -1058,6 +1104,9 @@ hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
     case 2: return launch_one<FMT, 192, 256, kDense, EPI>(p, stream);
     case 3: return launch_one<FMT, 192, 192, kDense, EPI>(p, stream);
     case 4: return launch_one<FMT, 256, 128, kDense, EPI>(p, stream);
+    case 5: return launch_one<FMT, 256, 128, kDense, EPI, 2>(p, stream);
+    case 6: return launch_one<FMT, 128, 256, kDense, EPI, 2>(p, stream);
+    case 7: return launch_one<FMT, 192, 192, kDense, EPI, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1067,8 +1116,8 @@ hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream
   if (mode == kDense)
     return epi == kEpiAccum ? launch_dense<FMT, kEpiAccum>(p, stream) : launch_dense<FMT, kEpiStore>(p, stream);
   if (mode == kRaggedM) {
-    // 256-row tiles; dSwiGLU keeps 128 rows, its two bf16 LDS tiles of the
-    // epilogue would not fit at 256 x 256
+    // 256-row tiles; dSwiGLU keeps 128 rows (its two bf16 LDS tiles of the
+    // epilogue would not fit at 256), with 8 wavefronts
     if (epi == kEpiSwiglu) return launch_one<FMT, 256, 256, kRaggedM, kEpiSwiglu>(p, stream);
     if (epi == kEpiDSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiDSwiglu>(p, stream);
     return launch_one<FMT, 256, 256, kRaggedM, kEpiStore>(p, stream);
@@ -1104,7 +1153,10 @@ hipError_t launch_many_single(const GemmMany& m, int sh, hipStream_t stream) {
     case 1: return launch_many_k<FMT, 1, 1>(m, stream);
     case 2: return launch_many_k<FMT, 2, 2>(m, stream);
     case 3: return launch_many_k<FMT, 3, 3>(m, stream);
-    default: return launch_many_k<FMT, 4, 4>(m, stream);
+    case 4: return launch_many_k<FMT, 4, 4>(m, stream);
+    case 5: return launch_many_k<FMT, 5, 5>(m, stream);
+    case 6: return launch_many_k<FMT, 6, 6>(m, stream);
+    default: return launch_many_k<FMT, 7, 7>(m, stream);
   }
 }
 
@@ -1113,12 +1165,14 @@ hipError_t launch_many_single(const GemmMany& m, int sh, hipStream_t stream) {
 // weight-gradient GEMMs at the Flux shapes); otherwise one launch per shape.
 template <int FMT>
 hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
-  bool used[5] = {false, false, false, false, false};
+  bool used[kNumDense] = {};
   for (int i = 0; i < all.n; ++i) used[all.shape[i]] = true;
   int nused = 0;
-  for (int k = 0; k < 5; ++k) nused += used[k];
+  for (int k = 0; k < kNumDense; ++k) nused += used[k];
   if (nused == 2 && used[1] && used[3]) return launch_many_k<FMT, 1, 3>(all, stream);
-  for (int k = 0; k < 5; ++k) {
+  if (nused == 2 && used[5] && used[7]) return launch_many_k<FMT, 5, 7>(all, stream);
+  if (nused == 2 && used[6] && used[7]) return launch_many_k<FMT, 6, 7>(all, stream);
+  for (int k = 0; k < kNumDense; ++k) {
     if (!used[k]) continue;
     GemmMany m;
     memset(&m, 0, sizeof m);
@@ -1136,9 +1190,10 @@ hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
 
 }  // namespace
 
-int dense_tile_index(int bm, int bn, int64_t M, int64_t N) {
-  for (int i = 0; i < 5; ++i)
-    if (kDenseShapes[i][0] == bm && kDenseShapes[i][1] == bn) return (M % bm || N % bn) ? -1 : i;
+int dense_tile_index(int bm, int bn, int wg_per_cu, int64_t M, int64_t N) {
+  for (int i = 0; i < kNumDense; ++i)
+    if (kDenseShapes[i][0] == bm && kDenseShapes[i][1] == bn && kDenseShapes[i][2] == wg_per_cu)
+      return (M % bm || N % bn) ? -1 : i;
   return -1;
 }
 

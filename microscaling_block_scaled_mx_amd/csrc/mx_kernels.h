@@ -103,9 +103,10 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream);
-// Index of the dense output tile shape bm x bn for an M x N output, or -1 if
-// it is not one of the dense shapes or does not divide M x N.
-int dense_tile_index(int bm, int bn, int64_t M, int64_t N);
+// Index of the dense output tile shape bm x bn at wg_per_cu workgroups per
+// compute unit for an M x N output, or -1 if it is not one of the dense
+// shapes or does not divide M x N.
+int dense_tile_index(int bm, int bn, int wg_per_cu, int64_t M, int64_t N);
 
 // Up to kGemmManyMax dense GEMMs (kDense, kEpiStore) of one format in one
 // launch; each takes the tile shape launch_gemm would give it.  shape and

@@ -109,7 +109,7 @@ def lib():
         L.mx_gemm.restype = ci
         L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_gemm_tiled.restype = ci
-        L.mx_gemm_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, ci, ci, vp]
+        L.mx_gemm_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, ci, ci, ci, vp]
         L.mx_gemm_accumulate.restype = ci
         L.mx_gemm_accumulate.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_fused_mlp_fwd.restype = ci
@@ -296,14 +296,16 @@ def gemm(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int =
 
 def gemm_tiled(a, b, M: int, N: int, K: int, fmt: int, c, tile, bias=None, bias_dtype: int = BF16,
                c_dtype: int = BF16, ldc: int | None = None, stream=None):
-    """mx_gemm_tiled: mx_gemm with the output tile shape tile = (tile_m,
-    tile_n), or (0, 0) for mx_gemm's own choice."""
+    """mx_gemm_tiled: mx_gemm with the output tiling tile = (tile_m, tile_n,
+    workgroups per compute unit), or (0, 0, 0) for mx_gemm's own choice; a
+    pair (tile_m, tile_n) means one workgroup per compute unit."""
     _need_packed(a, M, K, fmt, "gemm_tiled A")
     _need_packed(b, N, K, fmt, "gemm_tiled B")
     _need(c, (4 if c_dtype == F32 else 2) * M * (N if ldc is None else ldc), "gemm_tiled C")
     _need(bias, (4 if bias_dtype == F32 else 2) * N, "gemm_tiled bias")
     st = lib().mx_gemm_tiled(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
                              _ptr(c), c_dtype, N if ldc is None else ldc, int(tile[0]), int(tile[1]),
+                             int(tile[2]) if len(tile) > 2 else (0 if tuple(tile) == (0, 0) else 1),
                              _stream(stream))
     _check(st, "mx_gemm_tiled")
 

@@ -259,8 +259,9 @@ def test_fused_mlp_bwd_valid_args_need_the_device():
             assert st == DEVICE
 
 
-def gt(tile_m, tile_n, M=768, N=768, K=512):
-    return mx.lib().mx_gemm_tiled(P, P2, P3, P4, M, N, K, mx.E2M1, None, mx.BF16, P5, mx.BF16, N, tile_m, tile_n, None)
+def gt(tile_m, tile_n, occ=1, M=768, N=768, K=512):
+    return mx.lib().mx_gemm_tiled(P, P2, P3, P4, M, N, K, mx.E2M1, None, mx.BF16, P5, mx.BF16, N, tile_m, tile_n, occ,
+                                  None)
 
 
 def test_gemm_tiled_rejects_shapes_it_cannot_serve():
@@ -268,7 +269,9 @@ def test_gemm_tiled_rejects_shapes_it_cannot_serve():
     assert gt(256, 192, M=512, N=768) == OK or gt(256, 192, M=512, N=768) == DEVICE
     assert gt(192, 256, M=512, N=768) == SHAPE    # 192 does not divide M = 512
     assert gt(256, 64) == SHAPE
-    for tile in ((0, 0), (256, 256), (256, 192), (192, 256), (192, 192), (256, 128)):
+    assert gt(256, 256, 2) == SHAPE and gt(256, 128, 3) == SHAPE and gt(0, 0, 1) == SHAPE
+    for tile in ((0, 0, 0), (256, 256, 1), (256, 192, 1), (192, 256, 1), (192, 192, 1), (256, 128, 1),
+                 (256, 128, 2), (128, 256, 2), (192, 192, 2)):
         st = gt(*tile)
         assert st in (OK, DEVICE), tile
         if not mx.lib().mx_device_supported(0):

@@ -261,7 +261,8 @@ def test_gemm_parity(mxl, orc, fmt, mode, had, shape):
 
 
 @pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
-@pytest.mark.parametrize("tile", [(256, 256), (256, 192), (192, 256), (192, 192), (256, 128)])
+@pytest.mark.parametrize("tile", [(256, 256, 1), (256, 192, 1), (192, 256, 1), (192, 192, 1), (256, 128, 1),
+                                  (256, 128, 2), (128, 256, 2), (192, 192, 2)])
 def test_gemm_parity_every_tile_shape(mxl, orc, fmt, mode, had, tile):
     # the dense GEMM picks its tile shape from M, N and the compute-unit
     # count; mx_gemm_tiled forces each shape at a size all of them divide
