@@ -72,11 +72,11 @@ template <> struct MfmaFmt<kE2M3> { static constexpr int kCode = 2; };
 template <> struct MfmaFmt<kE2M1> { static constexpr int kCode = 4; };
 
 // Threads per workgroup of a BM x BN tile: 8 wavefronts for 256 x 256 and
-// for the dSwiGLU epilogue's 128 x 256 (two per SIMD, so that the
+// for the SwiGLU / dSwiGLU epilogues' 128 x 256 (two per SIMD, so that the
 // epilogue's long VALU dependency chains of one wavefront interleave with
 // another's), else 4.
 constexpr int tile_threads(int bm, int bn, int epi = 0) {
-  return ((bm == 256 && bn == 256) || (bm == 128 && bn == 256 && epi == 2)) ? 512 : 256;
+  return ((bm == 256 && bn == 256) || (bm == 128 && bn == 256 && (epi == 1 || epi == 2))) ? 512 : 256;
 }
 
 // OCC: workgroups resident per compute unit (1 or 2).  With 2, each takes at
@@ -138,7 +138,7 @@ struct Cfg {
   static_assert(BM + BN <= 512, "scale slots");
   // epilogue staging
   static constexpr int kCPitch = kWN * 2 + 8;         // bf16 store: per-wave kWM x kWN tile
-  static constexpr int kZPitch = (BN / 2) * 2 + 8;    // SwiGLU: z tile BM x BN/2
+  static constexpr int kZPitch = BN * 2 + 16;         // SwiGLU: gate | up tile BM x BN, then z in its gate half
   static constexpr int kDPitch = BN * 2 + 16;         // dSwiGLU: two BM x BN tiles, 16-byte rows
   static constexpr int kEpiBytes = EPI == kEpiSwiglu    ? BM * kZPitch
                                    : EPI == kEpiDSwiglu ? 2 * BM * kDPitch
@@ -835,10 +835,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
       }
     }
   } else if constexpr (EPI == kEpiSwiglu) {
-    // Lane holds gate (j < NJ/2) and up (j + NJ/2) of the same (row, z columns).
-    // H [R][2F] is stored; z = SwiGLU(bf16 gate, bf16 up) goes to LDS only.
+    // A lane holds gate (j < NJ/2) and up (j + NJ/2) of the same (row, z
+    // columns).  Both are staged in LDS as bf16, the gate half in columns
+    // [0, BN/2) of the tile and the up half in [BN/2, BN).  Then each thread
+    // takes 8-column chunks of z in row order: H's gate and up chunks go out
+    // as coalesced 16-byte stores (a wavefront writes whole 256-byte row
+    // segments of each half), and z = SwiGLU(gate, up) replaces the gate
+    // chunk; z is then quantized rowwise and columnwise out of LDS.
     constexpr int H2 = CF::kNJ / 2;
-    uint8_t* zt = smem;
+    uint8_t* zt = smem;  // pitch kZPitch: the staged gate | up tile, then z in the gate half
     const int64_t zb = (int64_t)tn * (BN / 2);
     uint16_t* Hc = reinterpret_cast<uint16_t*>(p.c);
 #pragma unroll
@@ -849,24 +854,38 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
         for (int e4 = 0; e4 < 4; ++e4) {
           const int ml = wm * CF::kWM + 32 * i + lrow;
           const int zc = wn * (CF::kWN / 2) + 32 * j + 8 * e4 + 4 * g;
-          const int64_t m = m0 + ml;
-          uint32_t hg[4], hu[4], z[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float g0 = round_bf16(acc[i][j][4 * e4 + q]);
-            const float u0 = round_bf16(acc[i][j + H2][4 * e4 + q]);
-            hg[q] = __float_as_uint(g0) >> 16;
-            hu[q] = __float_as_uint(u0) >> 16;
-            z[q] = __float_as_uint(swiglu_bf16(g0, u0)) >> 16;
-          }
-          if (m < m_end) {
-            *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + zb + zc) =
-                make_uint2(hg[0] | (hg[1] << 16), hg[2] | (hg[3] << 16));
-            *reinterpret_cast<uint2*>(Hc + m * 2 * p.F + p.F + zb + zc) =
-                make_uint2(hu[0] | (hu[1] << 16), hu[2] | (hu[3] << 16));
-          }
-          *reinterpret_cast<uint2*>(zt + ml * CF::kZPitch + zc * 2) = make_uint2(z[0] | (z[1] << 16), z[2] | (z[3] << 16));
+          const v16f& ag = acc[i][j];
+          const v16f& au = acc[i][j + H2];
+          *reinterpret_cast<uint2*>(zt + ml * CF::kZPitch + zc * 2) =
+              make_uint2(pack_bf16x2(ag[4 * e4 + 0], ag[4 * e4 + 1]), pack_bf16x2(ag[4 * e4 + 2], ag[4 * e4 + 3]));
+          *reinterpret_cast<uint2*>(zt + ml * CF::kZPitch + BN + zc * 2) =
+              make_uint2(pack_bf16x2(au[4 * e4 + 0], au[4 * e4 + 1]), pack_bf16x2(au[4 * e4 + 2], au[4 * e4 + 3]));
         }
+    __syncthreads();
+    {
+      constexpr int kChunksRow = BN / 16;                // 8-column chunks of z per tile row
+      constexpr int kPer = BM * kChunksRow / kThreads;   // chunks per thread
+      static_assert(BM * kChunksRow % kThreads == 0, "whole chunks per thread");
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int q = t + kThreads * k, row = q / kChunksRow, ch = q % kChunksRow;
+        uint4* gp = reinterpret_cast<uint4*>(zt + row * CF::kZPitch + 16 * ch);
+        const uint4 gw = *gp;
+        const uint4 uw = *reinterpret_cast<const uint4*>(zt + row * CF::kZPitch + BN + 16 * ch);
+        const int64_t m = m0 + row;
+        if (m < m_end) {
+          *reinterpret_cast<uint4*>(Hc + m * 2 * p.F + zb + 8 * ch) = gw;
+          *reinterpret_cast<uint4*>(Hc + m * 2 * p.F + p.F + zb + 8 * ch) = uw;
+        }
+        const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, us[4] = {uw.x, uw.y, uw.z, uw.w};
+        uint32_t z[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          z[w] = (__float_as_uint(swiglu_bf16(bf16_lo(gs[w]), bf16_lo(us[w]))) >> 16) |
+                 (__float_as_uint(swiglu_bf16(bf16_hi(gs[w]), bf16_hi(us[w]))) & 0xffff0000u);
+        *gp = make_uint4(z[0], z[1], z[2], z[3]);
+      }
+    }
     __syncthreads();
     constexpr int QB = FmtTraits<FMT>::kBits;
     constexpr int ZC = BN / 2;  // z columns in the tile
@@ -1116,9 +1135,12 @@ hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream
   if (mode == kDense)
     return epi == kEpiAccum ? launch_dense<FMT, kEpiAccum>(p, stream) : launch_dense<FMT, kEpiStore>(p, stream);
   if (mode == kRaggedM) {
-    // 256-row tiles; dSwiGLU keeps 128 rows (its two bf16 LDS tiles of the
-    // epilogue would not fit at 256), with 8 wavefronts
-    if (epi == kEpiSwiglu) return launch_one<FMT, 256, 256, kRaggedM, kEpiSwiglu>(p, stream);
+    // 256-row tiles for the plain store.  The epilogues that quantize take
+    // 128 rows with 8 wavefronts: dSwiGLU's two bf16 LDS tiles would not fit
+    // at 256, and SwiGLU measured 8-9% faster (at expert sizes that are
+    // multiples of 128, every 128-row tile is full, so no round ends part
+    // empty; the plain store gained nothing from it)
+    if (epi == kEpiSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiSwiglu>(p, stream);
     if (epi == kEpiDSwiglu) return launch_one<FMT, 128, 256, kRaggedM, kEpiDSwiglu>(p, stream);
     return launch_one<FMT, 256, 256, kRaggedM, kEpiStore>(p, stream);
   }
