@@ -97,11 +97,14 @@ struct Cfg {
   static constexpr int kWavesN = kWaves / 2;  // wavefronts across N (2 across M)
   // K elements per stage: one 128-element K group (64 / 96 / 128 bytes per
   // row); E4M3 tiles whose 128-element stages would not fit a ring of two in
-  // the LDS take half a group (64 bytes) per stage.  Every stage ends in a
+  // the LDS, or whose accumulators take more than 144 registers (leaving too
+  // few for double-buffered 8-register fragments), take half a group (64
+  // bytes) per stage.  Every stage ends in a
   // workgroup barrier: at 256 x 256, two 128-element E4M3 stages measured
   // 4-8% faster than four of 64 (MXFP8 16384 x 9216 x 3072: 504 -> 466 us;
   // the grouped step 954 -> 899 us, same box).
-  static constexpr int kBK = FMT == kE4M3 && 2 * ((BM + BN) * 128 + 2048) > kLds ? 64 : 128;
+  static constexpr int kAccRegs = (BM / 64) * (BN / kWavesN / 32) * 16;  // accumulator registers per lane
+  static constexpr int kBK = FMT == kE4M3 && (2 * ((BM + BN) * 128 + 2048) > kLds || kAccRegs > 144) ? 64 : 128;
   static constexpr int kRowBytes = kBK * kBits / 8;      // 64 / 96 / 128 (or 64) bytes per row per stage
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
   static constexpr int kScaleDw = 1;                     // scale dword (4 blocks of 32 along K) per row per stage
@@ -1176,9 +1179,9 @@ hipError_t launch_many_single(const GemmMany& m, int sh, hipStream_t stream) {
     case 2: return launch_many_k<FMT, 2, 2>(m, stream);
     case 3: return launch_many_k<FMT, 3, 3>(m, stream);
     case 4: return launch_many_k<FMT, 4, 4>(m, stream);
-    case 5: return launch_many_k<FMT, 5, 5>(m, stream);
-    case 6: return launch_many_k<FMT, 6, 6>(m, stream);
-    default: return launch_many_k<FMT, 7, 7>(m, stream);
+    // the two-per-CU tilings are never chosen for a many-launch (only
+    // mx_gemm_tiled asks for them)
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -1192,8 +1195,6 @@ hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
   int nused = 0;
   for (int k = 0; k < kNumDense; ++k) nused += used[k];
   if (nused == 2 && used[1] && used[3]) return launch_many_k<FMT, 1, 3>(all, stream);
-  if (nused == 2 && used[5] && used[7]) return launch_many_k<FMT, 5, 7>(all, stream);
-  if (nused == 2 && used[6] && used[7]) return launch_many_k<FMT, 6, 7>(all, stream);
   for (int k = 0; k < kNumDense; ++k) {
     if (!used[k]) continue;
     GemmMany m;
