@@ -267,6 +267,48 @@ def graph_time(launch, reps=10, replays=4, warm=None):
     return ev[0].elapsed_time(ev[replays]) * 1e3 / (reps * replays)
 
 
+def sclk_under_load(launch, sample_us=1000, load_ms=6.0):
+    """Shader clock (MHz) while `launch(r)` runs back to back: a graph of
+    ten launches is replayed for about `load_ms` on the current stream, and
+    one wavefront on a second (default-priority) stream counts shader-clock
+    cycles against the wall clock for `sample_us` meanwhile (mx_clock_sample).
+    That is the clock the kernel actually ran at; random operand data pulls
+    it below the 2.4 GHz the datasheet peaks assume."""
+    import torch
+    from microscaling_block_scaled_mx_amd import mx
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(10):
+            launch(r)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(10):
+            launch(r)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev[0].record()
+    g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    reps = max(2, int(load_ms / max(ev[0].elapsed_time(ev[1]), 1e-3)) + 1)
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    g.replay()  # the load is running before the sample starts
+    with torch.cuda.stream(side):
+        mx.clock_sample(sample_us, out, stream=side)
+    for _ in range(reps - 1):
+        g.replay()
+    torch.cuda.synchronize()
+    cycles, ticks = (int(v) for v in out.cpu())
+    khz = mx.wall_clock_khz()
+    if ticks <= 0 or khz <= 0:
+        return None
+    return round(cycles / ticks * khz / 1e3, 1)
+
+
 KERNEL_STATS = {}  # median / min per launch name from kernel_times
 
 
@@ -308,6 +350,57 @@ def cpu_baseline(step: LinearStep, repeats=3):
             "seconds_measured": round(total, 2)}
 
 
+def cpu_baseline_per_config():
+    """The oracle on bounded samples of the other workloads (part of the
+    CPU-baseline leg): per workload, one pack on a row slice of its largest
+    input (algorithmic bytes / s) and its largest GEMM on a 512-row sample
+    of A against all of B (TFLOP/s; the oracle dequantizes B once per call,
+    which the rate includes).  About 20 s in all on 16 cores."""
+    from microscaling_block_scaled_mx_amd import inputs as I
+    from oracle import oracle as orc
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    def sample(name, x, rows, C, fmt, mode, had, pro, aux, B, N, K, extra_in, what):
+        xs = np.ascontiguousarray(x[:rows])
+        auxs = None if aux is None else np.ascontiguousarray(aux[:rows])
+        _, tp = timed(lambda: orc.quantize(xs, rows, C, fmt, mode, had, pro=pro, aux=auxs, row=True, col=True))
+        bits = {orc.E2M1: 4, orc.E2M3: 6, orc.E4M3: 8}[fmt]
+        pack_bytes = rows * C * (2 + 2 * extra_in + 2 * (bits / 8 + 1 / 32))
+        qa = orc.quantize(I.bf16_normal(np.random.default_rng(5), (512, K)), 512, K, fmt, mode, had)
+        qb = orc.quantize(B, N, K, fmt, mode, had)
+        _, tg = timed(lambda: orc.gemm(qa["row_codes"], qa["row_scales"], qb["row_codes"], qb["row_scales"], 512, N,
+                                       K, fmt))
+        out[name] = {"pack_gbs": round(pack_bytes / tp / 1e9, 3), "gemm_tflops": round(2.0 * 512 * N * K / tg / 1e12, 4),
+                     "sample": what, "seconds": round(tp + tg, 2)}
+
+    A, Bm = I.gemm_pair(101, 256, 256, 256)
+    _, t1 = timed(lambda: orc.gemm(*(lambda a, b: (a["row_codes"], a["row_scales"], b["row_codes"], b["row_scales"]))(
+        orc.quantize(A, 256, 256, orc.E2M1, orc.FLOOR), orc.quantize(Bm, 256, 256, orc.E2M1, orc.FLOOR)),
+        256, 256, 256, orc.E2M1))
+    out["mxfp4_256"] = {"us_per_step": round(t1 * 1e6, 1), "sample": "the whole step (packs of A, B and the GEMM)"}
+    M, D, F = 8192, 3072, 12288
+    X, W1, b1, W2, dY = I.mlp(301, M, D, F)
+    # da and h of the backward's dGELU pack (the step computes them; here N(0,1) stand-ins of their shape)
+    h = I.bf16_normal(np.random.default_rng(3), (1024, F))
+    da = I.bf16_normal(np.random.default_rng(4), (1024, F))
+    sample("fused_mlp_mxfp6", da, 1024, F, orc.E2M3, orc.FLOOR, True, orc.PRO_DGELU, h, W1, F, D, 1,
+           "dGELU dual pack of (da, h) rows 0-1023 of [8192, 12288]; fc1 GEMM on 512 rows of A (512 x 12288 x 3072)")
+    name, K, N = I.FLUX_LINEARS[0]
+    Xq, Wq, _ = I.linear(401, 1024, N, K)
+    sample("mxfp4_flux_sweep", Xq, 1024, K, orc.E2M1, orc.FLOOR, False, orc.PRO_IDENTITY, None, Wq, N, K, 0,
+           "QKV: dual pack of X rows 0-1023 of [16384, 3072]; fwd GEMM on 512 rows of X (512 x 9216 x 3072)")
+    counts, offsets, Xg, W1g, W2g, dYg = I.grouped_mlp(501, 32768, 2048, 768, 8)
+    sample("grouped_mxfp8", Xg, 1024, 2048, orc.E4M3, orc.RCEIL, False, orc.PRO_IDENTITY, None,
+           np.ascontiguousarray(W1g[0]), 1536, 2048, 0,
+           "dual pack of X rows 0-1023 of [32768, 2048]; FC1 GEMM of expert 0 on 512 rows (512 x 1536 x 2048)")
+    return out
+
+
 # ------------------------------------------------------------------ other workloads
 def bench_cfg1(mx, T, iters=20):
     """The 256^3 MXFP4 case: packs of A and B (one launch) and the GEMM with an
@@ -336,30 +429,45 @@ def bench_cfg1(mx, T, iters=20):
 
 
 def bench_cfg3(mx, T, iters=5):
+    """Fused MXFP6 MLP (config 3): forward + backward per step, timed as
+    replays of a HIP graph of two steps over two copies of the inputs (X,
+    W1, b1, W2, dY: 250 MB per copy, so a step does not find its inputs in
+    the 256 MB Infinity Cache), after warm-up steps."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     M, D, F = 8192, 3072, 12288
     X, W1, b1, W2, dY = I.mlp(301, M, D, F)
     P = lambda r, k: mx.alloc_packed(r, k, mx.E2M3)
     e16 = lambda *s: torch.empty(s, dtype=torch.int16, device="cuda")
-    t = dict(X=dev(X), W1=dev(W1), b1=dev(b1), W2=dev(W2), dY=dev(dY), h=e16(M, F), Y=e16(M, D), Xr=P(M, D),
+    ins = [dict(X=dev(X), W1=dev(W1), b1=dev(b1), W2=dev(W2), dY=dev(dY)) for _ in range(2)]
+    t = dict(h=e16(M, F), Y=e16(M, D), Xr=P(M, D),
              Xc=P(D, M), W1r=P(F, D), W1c=P(D, F), W2r=P(D, F), W2c=P(F, D), ar=P(M, F), ac=P(F, M),
              da=e16(M, F), dX=e16(M, D), dW1=e16(F, D), dW2=e16(D, F),
              db1=torch.empty(F, dtype=torch.float32, device="cuda"),
              part=torch.empty((M // 32, F), dtype=torch.float32, device="cuda"), dYr=P(M, D), dYc=P(D, M),
              dhr=P(M, F), dhc=P(F, M))
 
-    def one(i):
-        T.run("c3_fwd", mx.fused_mlp_fwd, M, D, F, t["X"], t["W1"], t["b1"], t["W2"], t["h"], t["Y"], t["Xr"],
-              t["Xc"], t["W1r"], t["W1c"], t["W2r"], t["W2c"], t["ar"], t["ac"])
-        T.run("c3_bwd", mx.fused_mlp_bwd, M, D, F, t["dY"], t["h"], t["Xc"], t["W1c"], t["W2c"], t["ac"], t["da"],
-              t["dX"], t["dW1"], t["dW2"], t["db1"], t["part"], t["dYr"], t["dYc"], t["dhr"], t["dhc"])
-    sec = time_steps(one, iters, 2, T)
-    k = T.summary()
+    def fwd(c):
+        i = ins[c % 2]
+        mx.fused_mlp_fwd(M, D, F, i["X"], i["W1"], i["b1"], i["W2"], t["h"], t["Y"], t["Xr"], t["Xc"], t["W1r"],
+                         t["W1c"], t["W2r"], t["W2c"], t["ar"], t["ac"])
+
+    def bwd(c):
+        i = ins[c % 2]
+        mx.fused_mlp_bwd(M, D, F, i["dY"], t["h"], t["Xc"], t["W1c"], t["W2c"], t["ac"], t["da"], t["dX"], t["dW1"],
+                         t["dW2"], t["db1"], t["part"], t["dYr"], t["dYc"], t["dhr"], t["dhc"])
+
+    def step(c):
+        fwd(c)
+        bwd(c)
+    per_step = graph_time(step, reps=2, replays=iters)
+    fwd_us = graph_time(fwd, reps=2, replays=iters)
+    bwd_us = graph_time(bwd, reps=2, replays=iters)
     fl = 6 * 2.0 * M * D * F
     return {"workload": "fused MXFP6 MLP M=8192 3072->12288->3072 tanh-GELU fwd+bwd (+db1)",
-            "ms_per_step": sec * 1e3, "fwd_ms": k["c3_fwd"] / 1e3, "bwd_ms": k["c3_bwd"] / 1e3,
-            "tflops": fl / sec / 1e12, "frac_of_fp6_peak": fl / sec / 1e12 / PEAK_TFLOPS["fp6"]}
+            "launch": "hip_graph (2 steps over 2 input copies per replay)",
+            "ms_per_step": per_step / 1e3, "fwd_ms": fwd_us / 1e3, "bwd_ms": bwd_us / 1e3,
+            "tflops": fl / (per_step * 1e-6) / 1e12, "frac_of_fp6_peak": fl / (per_step * 1e-6) / 1e12 / PEAK_TFLOPS["fp6"]}
 
 
 def bench_cfg4(mx, T, iters=3):
@@ -368,7 +476,10 @@ def bench_cfg4(mx, T, iters=3):
     out = {"workload": "MXFP4 Flux-12B block linears at M=16384, fwd+dgrad+wgrad", "linears": {}}
     tot_fl = tot_gemm_us = tot_us = 0.0
     for i, (name, K, N) in enumerate(I.FLUX_LINEARS):
-        st = LinearStep(mx, 16384, N, K, mx.E2M1, mx.FLOOR, False, 401 + i, copies=1)
+        # one input set (X, W, dY) under 256 MB would stay in the Infinity
+        # Cache across back-to-back launches: rotate two copies of it then
+        copies = 2 if 2 * (16384 * K + N * K + 16384 * N) < 256e6 else 1
+        st = LinearStep(mx, 16384, N, K, mx.E2M1, mx.FLOOR, False, 401 + i, copies=copies)
         k = kernel_times(st)  # device time of the step's two launches
         g = k["gemm_fwd_dgrad_wgrad"]
         step_us = g + k["pack_XWdY"]
@@ -591,8 +702,9 @@ def only(mx, spec, steps, warmup, T):
         items = [dict(a=a, b=b, M=m, N=n, K=k, c=torch.empty((m, n), dtype=torch.int16, device="cuda"))
                  for a, b, m, n, k in trio]
         us = graph_time(lambda r: mx.gemm_many(items, fmt), reps=steps)
-        print(json.dumps({"only": spec, "data": data, "us": us, "tflops": 3 * 2.0 * M * N * K / (us * 1e-6) / 1e12}),
-              flush=True)
+        sclk = sclk_under_load(lambda r: mx.gemm_many(items, fmt))
+        print(json.dumps({"only": spec, "data": data, "us": us, "tflops": 3 * 2.0 * M * N * K / (us * 1e-6) / 1e12,
+                          "sclk_mhz": sclk}), flush=True)
     elif kind == "packs":  # the linear step's fused pack: X [M,K], W [N,K], dY [M,N] in one launch
         M, N, K = (int(v) for v in dims)
         rng = np.random.default_rng(7)
@@ -660,6 +772,10 @@ def main():
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
     # algorithmic bytes of the fused pack: X [M,K], W [N,K], dY [M,N], each read once (bf16) and written twice
     pack_bytes = (M * K + N * K + M * N) * (2 + 2 * PACK_OUT[6])
+    # the shader clock while each launch runs back to back (amdsmi)
+    def call_of(name):
+        return lambda r: (lambda fn, a, kw: fn(*a, **kw))(*step.calls(r)[name])
+    sclk = {n: sclk_under_load(call_of(n)) for n in ("gemm_fwd_dgrad_wgrad", "pack_XWdY")}
     kernels = {n: {"us": round(v, 2), "median_us": round(KERNEL_STATS[n]["median"], 2),
                    "min_us": round(KERNEL_STATS[n]["min"], 2)} for n, v in k.items()}
     kernels["gemm_fwd_dgrad_wgrad"]["tflops"] = round(achieved, 1)
@@ -679,17 +795,22 @@ def main():
                                                 "in one launch, 231.9 GFLOP)",
                      "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp6"], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS["fp6"], 4), "traffic": measured_traffic(GEMM_TRAFFIC),
-                     "traffic_unit": "bytes per launch (HBM read + write)"},
+                     "traffic_unit": "bytes per launch (HBM read + write)",
+                     "sclk_mhz": sclk["gemm_fwd_dgrad_wgrad"],
+                     "peak_at_sclk": (round(PEAK_TFLOPS["fp6"] * sclk["gemm_fwd_dgrad_wgrad"] / 2400.0, 1)
+                                      if sclk["gemm_fwd_dgrad_wgrad"] else None)},
         "quantizer": {"kernel": "pack_many_kernel<E2M3, Hadamard>: dual packs of X, W and dY in one launch",
                       "achieved_gbs": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9, 1), "peak_gbs": HBM_GBS,
                       "frac": round(pack_bytes / (k["pack_XWdY"] * 1e-6) / 1e9 / HBM_GBS, 4),
                       "algorithmic_bytes": pack_bytes, "traffic": measured_traffic(PACK_TRAFFIC),
-                      "alu": alu_roofline(k["pack_XWdY"])},
+                      "alu": alu_roofline(k["pack_XWdY"]), "sclk_mhz": sclk["pack_XWdY"]},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(step)
+        if args.extra == "all":
+            line["cpu_baseline"]["per_workload"] = cpu_baseline_per_config()
     if args.extra == "all":
         extra = {}
         for name, fn in (("mxfp4_256", bench_cfg1), ("fused_mlp_mxfp6", bench_cfg3), ("mxfp4_flux_sweep", bench_cfg4),

@@ -473,6 +473,18 @@ int64_t mx_codes_bytes(int fmt, int64_t rows, int64_t K);
 int64_t mx_scales_bytes(int64_t rows, int64_t K);
 /* Library version string. */
 const char* mx_version(void);
+/* Measurement helper: enqueue on `stream` one wavefront that spins for
+ * `microseconds` of wall-clock time (1 .. 10^6) and writes, to the device
+ * array out[2] (16-byte aligned), the shader-clock cycles (s_memtime) and
+ * the wall-clock ticks (s_memrealtime, mx_wall_clock_khz() kHz) it saw:
+ * the shader clock in kHz is out[0] / out[1] * mx_wall_clock_khz().  Run
+ * beside another stream's kernels, it reads the clock they run at (which
+ * operand data can pull below the rated 2.4 GHz).  The wait is bounded by
+ * the wall clock.  Errors: MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_SHAPE,
+ * MX_ERR_DEVICE, MX_ERR_LAUNCH. */
+int mx_clock_sample(int64_t microseconds, uint64_t* out, void* stream);
+/* Wall-clock rate of the current device in kHz (0 if unknown). */
+int64_t mx_wall_clock_khz(void);
 
 #ifdef __cplusplus
 }

@@ -189,6 +189,22 @@ void* scratch_ptr() {
   return g_scratch_ptr[dev];
 }
 
+// Shader clock over a wall-clock interval: one wavefront reads the shader
+// cycle counter (s_memtime) and the constant-rate wall clock (s_memrealtime)
+// before and after spinning until `wall_ticks` wall-clock ticks have passed
+// (a bounded wait: the wall clock always advances).  out[0] = shader
+// cycles, out[1] = wall-clock ticks.
+__global__ __launch_bounds__(64) void clock_sample_kernel(uint64_t wall_ticks, uint64_t* out) {
+  const uint64_t r0 = wall_clock64(), c0 = clock64();
+  uint64_t r1 = r0;
+  while (r1 - r0 < wall_ticks) r1 = wall_clock64();
+  const uint64_t c1 = clock64();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+  }
+}
+
 bool packed_ok(const mx_packed& q) { return q.codes && q.scales; }
 bool packed_aligned(const mx_packed& q) { return aligned16(q.codes) && aligned16(q.scales); }
 
@@ -630,5 +646,31 @@ int64_t mx_scales_bytes(int64_t rows, int64_t K) {
 }
 
 const char* mx_version(void) { return "libmx 0.1 (gfx950)"; }
+
+int mx_clock_sample(int64_t microseconds, uint64_t* out, void* stream) {
+  if (!out) return MX_ERR_NULL;
+  if (!aligned16(out)) return MX_ERR_ALIGN;
+  if (microseconds <= 0 || microseconds > 1000000) return MX_ERR_SHAPE;
+  int st = check_device();
+  if (st != MX_OK) return st;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      khz <= 0) {
+    (void)hipGetLastError();
+    return MX_ERR_DEVICE;
+  }
+  const uint64_t ticks = (uint64_t)microseconds * (uint64_t)khz / 1000u;
+  hipLaunchKernelGGL(clock_sample_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), ticks, out);
+  return launched(hipGetLastError());
+}
+
+int64_t mx_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return khz;
+}
 
 }  // extern "C"

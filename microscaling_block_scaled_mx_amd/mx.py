@@ -128,6 +128,10 @@ def lib():
         L.mx_scales_bytes.argtypes = [i64, i64]
         L.mx_version.restype = ctypes.c_char_p
         L.mx_version.argtypes = []
+        L.mx_clock_sample.restype = ci
+        L.mx_clock_sample.argtypes = [i64, vp, vp]
+        L.mx_wall_clock_khz.restype = i64
+        L.mx_wall_clock_khz.argtypes = []
         _lib = L
     return _lib
 
@@ -402,6 +406,17 @@ def device_supported(device: int = 0) -> bool:
 
 def status_str(st: int) -> str:
     return lib().mx_status_str(st).decode()
+
+
+def clock_sample(microseconds: int, out, stream=None):
+    """mx_clock_sample: out (uint64/int64 device tensor of 2) <- shader
+    cycles and wall-clock ticks over `microseconds` of wall-clock time."""
+    _need(out, 16, "clock_sample out")
+    _check(lib().mx_clock_sample(int(microseconds), _ptr(out), _stream(stream)), "mx_clock_sample")
+
+
+def wall_clock_khz() -> int:
+    return int(lib().mx_wall_clock_khz())
 
 
 def version() -> str:

@@ -410,3 +410,14 @@ def test_binding_quantize_sr_rejects_short_buffers():
     small = (torch.empty(8, dtype=torch.uint8), torch.empty(8, dtype=torch.uint8))
     with pytest.raises(mx.MXError, match="quantize_sr row"):
         mx.quantize_sr(torch.empty(R, C, dtype=torch.int16), R, C, 1, row=small)
+
+
+def test_clock_sample_rejections():
+    L = mx.lib()
+    assert L.mx_clock_sample(100, None, None) == NULL
+    assert L.mx_clock_sample(100, P + 8, None) == ALIGN
+    assert L.mx_clock_sample(0, P, None) == SHAPE and L.mx_clock_sample(2_000_000, P, None) == SHAPE
+    st = L.mx_clock_sample(100, P, None)
+    assert st in (OK, DEVICE)
+    if not L.mx_device_supported(0):
+        assert st == DEVICE

@@ -216,6 +216,18 @@ def test_binding_refuses_strided_device_views(mxl):
         mxl.quantize(bf16_empty(K, M).t(), M, K, mxl.E2M1, mxl.FLOOR, row=a)
 
 
+def test_clock_sample_reads_a_plausible_shader_clock(mxl):
+    # the measurement helper bench.py uses: shader cycles over ~200 us of
+    # wall clock give the clock in MHz, which is within the chip's range
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    mxl.clock_sample(200, out)
+    cycles, ticks = (int(v) for v in out.cpu())
+    khz = mxl.wall_clock_khz()
+    assert khz > 0 and ticks >= 200 * khz // 1000
+    mhz = cycles / ticks * khz / 1e3
+    assert 50 < mhz < 3000, mhz
+
+
 def test_quantize_zero_size_is_a_noop(mxl):
     x = torch.zeros(1, dtype=torch.int16, device="cuda")
     rc = torch.full((4,), 7, dtype=torch.uint8, device="cuda")
