@@ -44,16 +44,18 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # (scaled by what they read for a plain copy), valid while the kernel
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6, "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "7064e466da9550e8fbf37380133117ce32270323"}
+                "sources_sha1": "935b16fb669fe21e16883df2fe2585dd889fa5cc"}
 # VALU wavefront-instructions per launch of the fused pack (rocprofv3
 # SQ_INSTS_VALU), valid while the pack sources are those it was counted with
-PACK_VALU = {"instructions_per_launch": 1.0284e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-             "sources_sha1": "17474bbbeab7e4b6f7c3dbaa303c8354a0605fea"}
-# peak VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per 4
-# cycles on a 16-lane SIMD (G wavefront-instructions per second)
-VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
+PACK_VALU = {"instructions_per_launch": 1.028e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
+             "sources_sha1": "70e5578874d507074e0fa600e2c4e77f7a802a3c"}
+# peak VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, two wave64 instructions per
+# four cycles on each SIMD (gfx950 issues two VALU instructions of different
+# wavefronts together), i.e. the chip's 157.3 TFLOP/s of fp32 vector FMA
+# counted in wave64 instructions (G wavefront-instructions per second)
+VALU_PEAK_GIPS = 256 * 4 * 2.4 * 2 / 4
 PACK_TRAFFIC = {"bytes_per_launch": 123.5e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "17474bbbeab7e4b6f7c3dbaa303c8354a0605fea"}
+                "sources_sha1": "70e5578874d507074e0fa600e2c4e77f7a802a3c"}
 
 
 def measured_traffic(rec):
@@ -74,7 +76,7 @@ PACK_OUT = {4: 0.5 + 1 / 32, 6: 0.75 + 1 / 32, 8: 1.0 + 1 / 32}
 
 
 def alu_roofline(pack_us):
-    """The fused pack against its bound, VALU issue: the counted VALU
+    """The fused pack against the VALU issue roofline: the counted VALU
     wavefront-instructions per launch over the launch time, against the
     chip's issue peak.  None when the pack sources changed since the count."""
     n = measured_traffic(PACK_VALU)

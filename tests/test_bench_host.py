@@ -36,11 +36,14 @@ def test_traffic_records_are_keyed_to_their_kernel_sources():
 
 
 def test_alu_roofline_arithmetic(monkeypatch):
-    # 614.4 G wavefront-instructions/s = 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles
-    assert bench.VALU_PEAK_GIPS == pytest.approx(614.4)
-    monkeypatch.setattr(bench, "measured_traffic", lambda rec: 6.144e6)
-    r = bench.alu_roofline(20.0)  # 6.144e6 instructions in 20 us = 307.2 G/s
-    assert r["bound"] == "alu" and r["achieved"] == pytest.approx(307.2)
+    # 1228.8 G wavefront-instructions/s = 256 CUs x 4 SIMDs x 2.4 GHz x 2
+    # instructions per 4 cycles: the fp32 vector 157.3 TFLOP/s over the 128
+    # flops of one wave64 FMA
+    assert bench.VALU_PEAK_GIPS == pytest.approx(1228.8)
+    assert bench.VALU_PEAK_GIPS == pytest.approx(157.3e12 / 128 / 1e9, rel=1e-3)
+    monkeypatch.setattr(bench, "measured_traffic", lambda rec: 1.2288e7)
+    r = bench.alu_roofline(20.0)  # 1.2288e7 instructions in 20 us = 614.4 G/s
+    assert r["bound"] == "alu" and r["achieved"] == pytest.approx(614.4)
     assert r["frac"] == pytest.approx(0.5)
     monkeypatch.setattr(bench, "measured_traffic", lambda rec: None)
     assert bench.alu_roofline(20.0) is None
