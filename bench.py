@@ -632,21 +632,141 @@ def bench_sr_pack(mx, T):
             "nearest_us": rn, "sr_us": sr, "nearest_gbs": b / (rn * 1e-6) / 1e9, "sr_gbs": b / (sr * 1e-6) / 1e9}
 
 
+# the dense tilings mx_gemm_tiled serves: (tile_m, tile_n, workgroups per CU)
+DENSE_TILES = ((256, 256, 1), (256, 192, 1), (192, 256, 1), (192, 192, 1), (256, 128, 1), (256, 128, 2),
+               (128, 256, 2), (192, 192, 2))
+SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
+# Flux-12B (hidden 3072) block linears: name -> (N, K) of the forward GEMM
+FLUX_LINEARS = {"qkv": (9216, 3072), "out": (3072, 3072), "mlp_up": (12288, 3072), "mlp_down": (3072, 12288),
+                "adaln": (18432, 3072)}
+
+
+def random_packed(mx, rows, K, fmt, gen):
+    """A packed operand of random code bytes and E8M0 scales near 2^0."""
+    import torch
+    codes, scales = mx.alloc_packed(rows, K, fmt)
+    codes.copy_(torch.randint(0, 256, codes.shape, dtype=torch.uint8, device="cuda", generator=gen))
+    scales.copy_(torch.randint(118, 130, scales.shape, dtype=torch.uint8, device="cuda", generator=gen))
+    return codes, scales
+
+
+def time_plan(mx, pa, pb, M, N, K, fmt, C, tile, split, ws, reps):
+    return graph_time(lambda r: mx.gemm_splitk(pa, pb, M, N, K, fmt, C, tile, split, ws if split > 1 else None),
+                      reps=reps, replays=3)
+
+
+def tune_shape(mx, M, N, K, fmt, gen, reps=5, cus=256):
+    """Every dense tiling and K split of one GEMM shape, timed; returns the
+    rule's plan and time and the best plan and time.  K splits are tried
+    only where the tiling has fewer than two rounds of tiles."""
+    import torch
+    pa, pb = random_packed(mx, M, K, fmt, gen), random_packed(mx, N, K, fmt, gen)
+    C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    cands = []
+    for tile in DENSE_TILES:
+        if M % tile[0] or N % tile[1]:
+            continue
+        tiles = (M // tile[0]) * (N // tile[1])
+        for split in SPLITS:
+            if K % (128 * split) or (split > 1 and tiles * tile[2] >= 2 * cus):
+                continue
+            cands.append((tile, split))
+    ws_elems = max(sp * M * N for _, sp in cands)
+    ws = torch.empty((ws_elems,), dtype=torch.float32, device="cuda") if ws_elems > M * N else None
+    times = {}
+    for tile, split in cands:
+        times[(tile, split)] = time_plan(mx, pa, pb, M, N, K, fmt, C, tile, split, ws, reps)
+    rule = time_plan(mx, pa, pb, M, N, K, fmt, C, (0, 0, 0), 1, None, reps)
+    best = min(times, key=times.get)
+    return {"M": M, "N": N, "K": K, "fmt": fmt, "rule_us": rule, "best": [list(best[0]), best[1]],
+            "best_us": times[best], "candidates": len(cands)}
+
+
+def tune_gemms(mx, fmts, tokens, reps=5):
+    """The tuned-table sweep: the fwd, dgrad and wgrad GEMMs of every
+    Flux-12B block linear at each token count, in each format.  Prints one
+    JSON line per shape and, for those where the best plan beat the rule by
+    more than 5%, the initializer line of the tuned table."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    shapes = []
+    for T in tokens:
+        for name, (N, K) in FLUX_LINEARS.items():
+            for M_, N_, K_ in ((T, N, K), (T, K, N), (N, K, T)):
+                if (M_, N_, K_) not in shapes:
+                    shapes.append((M_, N_, K_))
+    lines = []
+    for fmt in fmts:
+        for M, N, K in shapes:
+            r = tune_shape(mx, M, N, K, fmt, gen, reps, cus)
+            if r["best_us"] < 0.95 * r["rule_us"]:
+                # confirm: the best plan and the rule timed alternately three
+                # more times; kept if the median gain still exceeds 5%
+                pa, pb = random_packed(mx, M, K, fmt, gen), random_packed(mx, N, K, fmt, gen)
+                C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+                (tm, tn, wg), sp = r["best"]
+                ws = torch.empty((sp * M * N,), dtype=torch.float32, device="cuda") if sp > 1 else None
+                pairs = [(time_plan(mx, pa, pb, M, N, K, fmt, C, (tm, tn, wg), sp, ws, reps),
+                          time_plan(mx, pa, pb, M, N, K, fmt, C, (0, 0, 0), 1, None, reps)) for _ in range(3)]
+                r["confirm_best_us"] = float(np.median([b for b, _ in pairs]))
+                r["confirm_rule_us"] = float(np.median([a for _, a in pairs]))
+                if r["confirm_best_us"] < 0.95 * r["confirm_rule_us"]:
+                    lines.append(f"    {{{cus}, {fmt}, {M}, {N}, {K}, {{{tm}, {tn}, {wg}, {sp}}}}},  "
+                                 f"// {r['confirm_rule_us']:.1f} -> {r['confirm_best_us']:.1f} us")
+                del pa, pb, C, ws
+            print(json.dumps({"tune": r}), flush=True)
+            torch.cuda.empty_cache()
+    for ln in lines:
+        print(ln, flush=True)
+
+
+def bench_tuned_plans(mx, T):
+    """The tuned table's split-K plans against mx_gemm's rule: the dgrad
+    GEMMs of the Flux-12B QKV, MLP and adaLN linears at 512 tokens (few
+    output tiles, long K) in each format, random code bytes.  Each time is a
+    graph of back-to-back calls; the planned call includes its reduction."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    out = {"workload": "dgrad GEMMs of the Flux-12B QKV / MLP / adaLN linears at 512 tokens (M=512, N=3072, "
+                       "K=9216/12288/18432): mx_gemm (rule) vs mx_gemm_splitk under mx_gemm_plan", "shapes": {}}
+    for fbits, fmt in (("4", mx.E2M1), ("6", mx.E2M3), ("8", mx.E4M3)):
+        for K in (9216, 12288, 18432):
+            M, N = 512, 3072
+            pa, pb = random_packed(mx, M, K, fmt, gen), random_packed(mx, N, K, fmt, gen)
+            C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+            tile, split, wsb = mx.gemm_plan(M, N, K, fmt)
+            ws = torch.empty((max(wsb // 4, 1),), dtype=torch.float32, device="cuda")
+            rule = graph_time(lambda r: mx.gemm(pa, pb, M, N, K, fmt, C), reps=10)
+            plan = graph_time(lambda r: mx.gemm_planned(pa, pb, M, N, K, fmt, C, workspace=ws), reps=10)
+            fl = 2.0 * M * N * K
+            out["shapes"][f"mxfp{fbits}_{M}x{N}x{K}"] = {
+                "plan": {"tile": list(tile), "split_k": split}, "rule_us": round(rule, 2), "plan_us": round(plan, 2),
+                "speedup": round(rule / plan, 3), "plan_tflops": round(fl / (plan * 1e-6) / 1e12, 1)}
+            del pa, pb, C, ws
+    return out
+
+
 def only(mx, spec, steps, warmup, T):
     """One kernel configuration, for profilers: gemm:FMT:M:N:K, pack:FMT:R:C
     (dual pack), packs:FMT:M:N:K (the linear step's fused dual packs of X,
     W and dY), gemms:FMT:M:N:K (its three GEMMs in one launch; random
     codes) or copy:BYTES; or one whole other workload: linear256, mlp,
-    sweep, grouped, main_grad or sr_pack.  Prints one JSON line with its
-    average time."""
+    sweep, grouped, main_grad, sr_pack or tuned.  Prints one JSON line with
+    its average time."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     workloads = {"linear256": bench_cfg1, "mlp": bench_cfg3, "sweep": bench_cfg4, "grouped": bench_cfg5,
-                 "main_grad": bench_main_grad, "sr_pack": bench_sr_pack}
+                 "main_grad": bench_main_grad, "sr_pack": bench_sr_pack, "tuned": bench_tuned_plans}
     if spec in workloads:  # one of the other workloads, as in the full run
         print(json.dumps({"only": spec, **workloads[spec](mx, T)}), flush=True)
         return
     kind, fbits, *dims = spec.split(":")
+    if kind == "tune":  # tune:FMTS:TOKENS, e.g. tune:4,6,8:512,1024 -- the tuned-table sweep
+        fmts = [{"4": mx.E2M1, "6": mx.E2M3, "8": mx.E4M3}[f] for f in fbits.split(",")]
+        tune_gemms(mx, fmts, [int(t) for t in dims[0].split(",")] if dims else [512, 1024, 2048, 4096, 8192,
+                                                                                16384])
+        return
     if kind == "copy":  # plain device copy of fbits bytes: the reference for the traffic counters
         n = int(fbits)
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -665,6 +785,14 @@ def only(mx, spec, steps, warmup, T):
         mx.quantize(dev(B), N, K, fmt, mode, had, row=pb)
         C = torch.empty((M, N), dtype=torch.int16, device="cuda")
         us = graph_time(lambda r: mx.gemm(pa, pb, M, N, K, fmt, C), reps=steps)
+        print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
+    elif kind == "gemmk":  # one GEMM with a forced tiling and K split: FMT:M:N:K:BM:BN:WG_PER_CU:SPLIT
+        M, N, K, bm, bn, occ, split = (int(v) for v in dims[:7])
+        g = torch.Generator(device="cuda").manual_seed(7)
+        pa, pb = random_packed(mx, M, K, fmt, g), random_packed(mx, N, K, fmt, g)
+        C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        ws = torch.empty((split * M * N,), dtype=torch.float32, device="cuda") if split > 1 else None
+        us = time_plan(mx, pa, pb, M, N, K, fmt, C, (bm, bn, occ), split, ws, steps)
         print(json.dumps({"only": spec, "us": us, "tflops": 2.0 * M * N * K / (us * 1e-6) / 1e12}), flush=True)
     elif kind == "gemmt":  # one GEMM with a forced tiling: FMT:M:N:K:BM:BN:WG_PER_CU[:rand|zero]
         M, N, K, bm, bn, occ = (int(v) for v in dims[:6])
@@ -737,9 +865,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--only", default=None,
                     help="profile one kernel config instead: gemm:FMT:M:N:K, pack:FMT:R:C, packs:FMT:M:N:K, "
-                         "gemms:FMT:M:N:K "
-                         "(FMT = 4, 6 or 8), copy:BYTES (a plain device copy), or one workload: "
-                         "linear256, mlp, sweep, grouped, main_grad, sr_pack")
+                         "gemms:FMT:M:N:K, gemmt:FMT:M:N:K:BM:BN:WG, gemmk:FMT:M:N:K:BM:BN:WG:SPLIT "
+                         "(FMT = 4, 6 or 8), copy:BYTES (a plain device copy), tune:FMTS:TOKENS (the tuned "
+                         "GEMM table's sweep), or one workload: "
+                         "linear256, mlp, sweep, grouped, main_grad, sr_pack, tuned")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
@@ -774,7 +903,7 @@ def main():
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
     # algorithmic bytes of the fused pack: X [M,K], W [N,K], dY [M,N], each read once (bf16) and written twice
     pack_bytes = (M * K + N * K + M * N) * (2 + 2 * PACK_OUT[6])
-    # the shader clock while each launch runs back to back (amdsmi)
+    # the shader clock while each launch runs back to back (mx_clock_sample)
     def call_of(name):
         return lambda r: (lambda fn, a, kw: fn(*a, **kw))(*step.calls(r)[name])
     sclk = {n: sclk_under_load(call_of(n)) for n in ("gemm_fwd_dgrad_wgrad", "pack_XWdY")}
@@ -817,7 +946,7 @@ def main():
         extra = {}
         for name, fn in (("mxfp4_256", bench_cfg1), ("fused_mlp_mxfp6", bench_cfg3), ("mxfp4_flux_sweep", bench_cfg4),
                          ("grouped_mxfp8", bench_cfg5), ("wgrad_main_grad", bench_main_grad),
-                         ("mxfp4_sr_pack", bench_sr_pack)):
+                         ("mxfp4_sr_pack", bench_sr_pack), ("tuned_splitk_512_tokens", bench_tuned_plans)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = fn(mx, T)
             torch.cuda.empty_cache()

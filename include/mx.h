@@ -265,7 +265,9 @@ int mx_quantize_many(const mx_quantize_item* items, int n, int fmt, int scale_mo
  *               of 8.
  * Tiling: the output is cut into 256x256, 256x192, 192x256, 192x192 or
  * 256x128 tiles, whichever costs the fewest rounds x tile area with one tile
- * per compute unit (mx_gemm_tiled takes the shape from the caller).
+ * per compute unit, unless the tuned table (mx_gemm_plan) holds a measured
+ * tiling without a K split for this device, format and shape
+ * (mx_gemm_tiled takes the shape from the caller).
  * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
  * MX_ERR_INDEX_OVERFLOW, MX_ERR_DEVICE, MX_ERR_LAUNCH.
  */
@@ -309,6 +311,61 @@ int mx_gemm_accumulate(const void* a_codes, const void* a_scales, const void* b_
 int mx_gemm_tiled(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
                   int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype, int64_t ldc,
                   int tile_m, int tile_n, int wg_per_cu, void* stream);
+
+/*
+ * mx_gemm_plan -- the launch plan of a dense GEMM: output tile, workgroups
+ * per compute unit and K split.  [P3] Tuned GEMMs: a table keyed by the
+ * compute-unit count and the GEMM's M, N and K names the kernel (its tile)
+ * and a split-K factor for each tuned shape.  Here the table holds the best
+ * of a measured sweep over every dense tiling and K split of the Flux-12B
+ * block linears (fwd, dgrad, wgrad) at 512 to 4096 tokens, where it beat
+ * the rule; any other shape gets the rule of mx_gemm with no split.
+ *
+ *  M, N, K, fmt     as mx_gemm.
+ *  plan             out, int[4]: tile_m, tile_n, wg_per_cu, split_k (the
+ *                   arguments mx_gemm_splitk takes).
+ *  workspace_bytes  out (may be NULL): the workspace mx_gemm_splitk needs
+ *                   for this plan, split_k * M * N * 4 bytes (0 if
+ *                   split_k = 1).
+ * Host only; nothing is enqueued.  Errors: MX_ERR_NULL (plan NULL),
+ * MX_ERR_FORMAT, MX_ERR_SHAPE (M, N or K not multiples of 256).
+ */
+int mx_gemm_plan(int64_t M, int64_t N, int64_t K, int fmt, int* plan, int64_t* workspace_bytes);
+
+/*
+ * mx_gemm_splitk -- mx_gemm with the K range cut into split_k equal parts
+ * computed by separate workgroups, then summed in a fixed order.  [P3]
+ * Tuned GEMMs (the split-K column of the tuned table): where a GEMM has
+ * fewer output tiles than compute units -- few tokens, long K -- the split
+ * parts fill the idle ones.
+ *
+ * The GEMM writes part s (the binary32 product over K elements
+ * [s*K/split_k, (s+1)*K/split_k), what mx_gemm_tiled with c_dtype = MX_F32
+ * and no bias stores for that K slice) to workspace + s*M*N (row pitch N);
+ * a second launch on the same stream then sets
+ *   c[m][n] = round(fl32(...fl32(fl32(p_0 + p_1) + p_2)... + p_{S-1}) + bias[n])
+ * with one rounding to c_dtype (nearest even for bf16).  The order is fixed
+ * and no atomics are used, so repeated calls are bitwise identical; the
+ * result differs from mx_gemm's by the binary32 summation order only.
+ *
+ *  tile_m, tile_n, wg_per_cu   the tiling, as mx_gemm_tiled (0, 0, 0: the
+ *               tiling mx_gemm would take).
+ *  split_k      1 .. MX_SPLIT_K_MAX; K must be a multiple of 128 * split_k.
+ *               split_k = 1 is mx_gemm_tiled (workspace unused).
+ *  workspace    device buffer of at least split_k * M * N * 4 bytes,
+ *               16-byte aligned, owned by the caller; overwritten; it must
+ *               not overlap A, B, bias or C.  Calls that share a workspace
+ *               must be ordered (same stream).
+ * Other arguments as mx_gemm.  Errors: as mx_gemm_tiled, plus MX_ERR_SHAPE
+ * (split_k out of range, K not a multiple of 128 * split_k, workspace too
+ * small), MX_ERR_NULL / MX_ERR_ALIGN (workspace missing or misaligned when
+ * split_k > 1).
+ */
+#define MX_SPLIT_K_MAX 16
+int mx_gemm_splitk(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
+                   int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype,
+                   int64_t ldc, int tile_m, int tile_n, int wg_per_cu, int split_k, void* workspace,
+                   int64_t workspace_bytes, void* stream);
 
 /*
  * mx_gemm_many -- several GEMMs of one format in a single launch, with the

@@ -349,6 +349,66 @@ int mx_gemm_tiled(const void* a_codes, const void* a_scales, const void* b_codes
                      static_cast<hipStream_t>(stream), tile);
 }
 
+int mx_gemm_plan(int64_t M, int64_t N, int64_t K, int fmt, int* plan, int64_t* workspace_bytes) {
+  if (!plan) return MX_ERR_NULL;
+  if (bits_of(fmt) == 0) return MX_ERR_FORMAT;
+  if (M < 0 || N < 0 || K < 0 || M % 256 || N % 256 || K % 256) return MX_ERR_SHAPE;
+  mx::GemmPlan g;
+  if (!mx::plan_gemm(fmt, M, N, K, &g)) return MX_ERR_SHAPE;
+  plan[0] = g.tile_m;
+  plan[1] = g.tile_n;
+  plan[2] = g.wg_per_cu;
+  plan[3] = g.split_k;
+  if (workspace_bytes) *workspace_bytes = g.split_k > 1 ? (int64_t)g.split_k * M * N * 4 : 0;
+  return MX_OK;
+}
+
+int mx_gemm_splitk(const void* a_codes, const void* a_scales, const void* b_codes, const void* b_scales, int64_t M,
+                   int64_t N, int64_t K, int fmt, const void* bias, int bias_dtype, void* c, int c_dtype,
+                   int64_t ldc, int tile_m, int tile_n, int wg_per_cu, int split_k, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+  int st = validate_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc);
+  if (st != MX_OK) return st;
+  if (split_k < 1 || split_k > MX_SPLIT_K_MAX || K % (128 * (int64_t)split_k)) return MX_ERR_SHAPE;
+  int tile = 0;
+  if (tile_m != 0 || tile_n != 0 || wg_per_cu != 0) {
+    const int i = mx::dense_tile_index(tile_m, tile_n, wg_per_cu, M, N);
+    if (i < 0) return MX_ERR_SHAPE;
+    tile = i + 1;
+  }
+  if (split_k > 1) {
+    if (!workspace) return MX_ERR_NULL;
+    if (!aligned16(workspace)) return MX_ERR_ALIGN;
+    if (workspace_bytes < (int64_t)split_k * M * N * 4) return MX_ERR_SHAPE;
+    if (!grid_fits((M / 128) * (N / 128) * split_k, 1, 1) || !grid_fits(M * (N / 4) / 256 + 1, 1, 1))
+      return MX_ERR_INDEX_OVERFLOW;
+  }
+  if ((st = check_device()) != MX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (split_k == 1)
+    return gemm_launch(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt, bias, bias_dtype, c, c_dtype, ldc, 0, s,
+                       tile);
+  if (M == 0 || N == 0) return MX_OK;
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  p.a_codes = static_cast<const uint8_t*>(a_codes);
+  p.a_scales = static_cast<const uint8_t*>(a_scales);
+  p.b_codes = static_cast<const uint8_t*>(b_codes);
+  p.b_scales = static_cast<const uint8_t*>(b_scales);
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ktot = K;
+  p.c = workspace;  // part s at workspace + s * M * N, binary32, no bias
+  p.ldc = N;
+  p.c_f32 = 1;
+  p.tile_shape = tile;
+  p.split_k = split_k;
+  if ((st = launched(mx::launch_gemm(p, fmt, mx::kDense, mx::kEpiSplit, s))) != MX_OK) return st;
+  return launched(mx::launch_splitk_reduce(static_cast<const float*>(workspace), split_k, M, N, bias,
+                                           bias_dtype == MX_F32, c, c_dtype == MX_F32, ldc, s));
+}
+
 int mx_gemm_many(const mx_gemm_item* items, int n, int fmt, void* stream) {
   if (!items) return MX_ERR_NULL;
   if (n < 1 || n > MX_GEMM_MANY_MAX) return MX_ERR_SHAPE;

@@ -311,8 +311,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
 
   // ---------------------------------------------------------------- tile
   int tm, tn;
+  int split = 0;  // split K: this workgroup's part of the K range
   if constexpr (MODE == kDense) {
-    dense_tile(bx, (int)(p.M / BM), (int)(p.N / BN), tm, tn);
+    const int tiles_m = (int)(p.M / BM), tiles_n = (int)(p.N / BN);
+    int local = bx;
+    if constexpr (EPI == kEpiSplit) {  // workgroups [s * T, (s + 1) * T) compute part s
+      split = bx / (tiles_m * tiles_n);
+      local = bx - split * (tiles_m * tiles_n);
+    }
+    dense_tile(local, tiles_m, tiles_n, tm, tn);
   } else if constexpr (MODE == kRaggedM) {
     // 1-D grid of (row tile, column tile) pairs, column tiles fastest.  Each
     // XCD takes a contiguous range, so the tiles of one row panel (and of
@@ -366,6 +373,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     b_row0 = (int64_t)gi * p.b_group_rows;
     b_soff = (int64_t)gi * scale_bytes(p.b_group_rows, p.ktot);
     b_coff = (int64_t)gi * code_bytes(p.b_group_rows, p.ktot, kBits);
+  }
+  if constexpr (MODE == kDense && EPI == kEpiSplit) {
+    {
+      const int64_t part = p.K / p.split_k;
+      kbeg = split * part;
+      kend = kbeg + part;
+      c_off = split * p.M * p.ldc;
+    }
   }
   if constexpr (MODE == kRaggedK) {
     const int gi = bz;
@@ -614,7 +629,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   pin_arg(p.c);
   pin_arg(p.ldc);
   pin_arg(p.c_f32);
-  if constexpr (EPI == kEpiStore || EPI == kEpiAccum) {
+  if constexpr (EPI == kEpiStore || EPI == kEpiAccum || EPI == kEpiSplit) {
     pin_arg(p.bias);
     pin_arg(p.bias_f32);
   } else {
@@ -659,10 +674,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   // ---------------------------------------------------------------- epilogues
   // Lane (row lrow, column group q = 8 * (e / 4) + 4 * g) of MFMA tile (i, j)
   // holds acc[i][j][4 * (e / 4) + 0..3] = C[row][col + 0..3].
-  if constexpr (EPI == kEpiStore || EPI == kEpiAccum) {
-    // bias of this lane's columns, read once (one uniform branch)
+  if constexpr (EPI == kEpiStore || EPI == kEpiAccum || EPI == kEpiSplit) {
+    // bias of this lane's columns, read once (one uniform branch); a split
+    // part is binary32 without the bias, which the reduction adds
+    constexpr bool kPart = EPI == kEpiSplit;
     float bv[CF::kNJ][16];
-    if (p.bias == nullptr) {
+    if (kPart || p.bias == nullptr) {
 #pragma unroll
       for (int j = 0; j < CF::kNJ; ++j)
 #pragma unroll
@@ -739,7 +756,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
       }
     };
     // value of element e of MFMA tile (i, j): fl32(acc + bias) (+ old)
-    if (p.c_f32) {
+    if (kPart || p.c_f32) {
       float* C = reinterpret_cast<float*>(p.c) + c_off;
       auto store_f32 = [&](auto with_old) {
         constexpr bool kOld = decltype(with_old)::value;
@@ -1058,7 +1075,10 @@ template <int FMT, int BM, int BN, int MODE, int EPI, int OCC = 1>
 hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   dim3 grid;
   if (MODE == kDense) {
-    grid = dim3((unsigned)((p.M / BM) * (p.N / BN)), 1, 1);
+    const int64_t parts = EPI == kEpiSplit ? p.split_k : 1;
+    if (parts < 1) return hipErrorInvalidValue;
+    if ((p.M / BM) * (p.N / BN) * parts >= (1ll << 31)) return hipErrorInvalidValue;
+    grid = dim3((unsigned)((p.M / BM) * (p.N / BN) * parts), 1, 1);
   } else if (MODE == kRaggedM) {
     // column tiles x an upper bound on the row tiles: sum over groups of
     // ceil(count / BM) <= R / BM + G; the surplus workgroups exit at once
@@ -1112,15 +1132,93 @@ int dense_shape(int64_t M, int64_t N) {
   return best;
 }
 
+// Measured launch plans (tile, workgroups per CU, K split) for the shapes
+// of the Flux-12B block linears where the best of a sweep over every dense
+// tiling and K split beat the rounds x tile-area rule: compute units,
+// format, M, N, K, then the plan.  A plan with split_k > 1 needs a
+// workspace, so mx_gemm (which has none) takes the rule for those shapes.
+struct Tuned {
+  int cus, fmt;
+  int64_t M, N, K;
+  GemmPlan plan;
+};
+constexpr Tuned kTuned[] = {
+#include "mx_tuned.inc"
+    {0, 0, 0, 0, 0, {0, 0, 0, 0}},  // end (no device has 0 compute units)
+};
+
+const Tuned* tuned(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int cus = cu_count();
+  for (const Tuned& t : kTuned)
+    if (t.cus == cus && t.fmt == fmt && t.M == M && t.N == N && t.K == K) return &t;
+  return nullptr;
+}
+
+int shape_index(int bm, int bn, int wg) {
+  for (int i = 0; i < kNumDense; ++i)
+    if (kDenseShapes[i][0] == bm && kDenseShapes[i][1] == bn && kDenseShapes[i][2] == wg) return i;
+  return -1;
+}
+
 // The shape a dense launch uses: the caller's (p.tile_shape = 1 + its
-// index), else the one dense_shape picks.
-int dense_shape_of(const GemmParams& p) {
-  return p.tile_shape > 0 && p.tile_shape <= kNumDense ? p.tile_shape - 1 : dense_shape(p.M, p.N);
+// index), else a tuned plan's without a K split, else the one dense_shape
+// picks.
+int dense_shape_of(int fmt, const GemmParams& p) {
+  if (p.tile_shape > 0 && p.tile_shape <= kNumDense) return p.tile_shape - 1;
+  const Tuned* t = tuned(fmt, p.M, p.N, p.K);
+  if (t && t->plan.split_k <= 1) {
+    const int i = shape_index(t->plan.tile_m, t->plan.tile_n, t->plan.wg_per_cu);
+    if (i >= 0 && p.M % kDenseShapes[i][0] == 0 && p.N % kDenseShapes[i][1] == 0) return i;
+  }
+  return dense_shape(p.M, p.N);
+}
+
+// Split-K reduction: thread q sums 4 consecutive columns of one row over the
+// parts in order, adds the bias and rounds once.
+template <int S>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int64_t M, int64_t N,
+                                                            const void* __restrict__ bias, int bias_f32,
+                                                            void* __restrict__ c, int c_f32, int64_t ldc) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n4 = N / 4;
+  if (q >= M * n4) return;
+  const int64_t m = q / n4, n = (q - m * n4) * 4;
+  const float* src = ws + m * N + n;
+  float4 v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const float4*>(src + s * (M * N));
+  float4 a = v[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) {
+    a.x = a.x + v[s].x;
+    a.y = a.y + v[s].y;
+    a.z = a.z + v[s].z;
+    a.w = a.w + v[s].w;
+  }
+  if (bias != nullptr) {
+    float4 b;
+    if (bias_f32) {
+      b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(bias) + n);
+    } else {
+      const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(bias) + n);
+      b = make_float4(bf16_lo(h.x), bf16_hi(h.x), bf16_lo(h.y), bf16_hi(h.y));
+    }
+    a.x = a.x + b.x;
+    a.y = a.y + b.y;
+    a.z = a.z + b.z;
+    a.w = a.w + b.w;
+  }
+  if (c_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + m * ldc + n) = a;
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + m * ldc + n) =
+        make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+  }
 }
 
 template <int FMT, int EPI>
 hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
-  switch (dense_shape_of(p)) {
+  switch (dense_shape_of(FMT, p)) {
     case 0: return launch_one<FMT, 256, 256, kDense, EPI>(p, stream);
     case 1: return launch_one<FMT, 256, 192, kDense, EPI>(p, stream);
     case 2: return launch_one<FMT, 192, 256, kDense, EPI>(p, stream);
@@ -1135,8 +1233,11 @@ hipError_t launch_dense(const GemmParams& p, hipStream_t stream) {
 
 template <int FMT>
 hipError_t launch_fmt(const GemmParams& p, int mode, int epi, hipStream_t stream) {
-  if (mode == kDense)
-    return epi == kEpiAccum ? launch_dense<FMT, kEpiAccum>(p, stream) : launch_dense<FMT, kEpiStore>(p, stream);
+  if (mode == kDense) {
+    if (epi == kEpiAccum) return launch_dense<FMT, kEpiAccum>(p, stream);
+    if (epi == kEpiSplit) return launch_dense<FMT, kEpiSplit>(p, stream);
+    return launch_dense<FMT, kEpiStore>(p, stream);
+  }
   if (mode == kRaggedM) {
     // 256-row tiles for the plain store.  The epilogues that quantize take
     // 128 rows with 8 wavefronts: dSwiGLU's two bf16 LDS tiles would not fit
@@ -1179,8 +1280,9 @@ hipError_t launch_many_single(const GemmMany& m, int sh, hipStream_t stream) {
     case 2: return launch_many_k<FMT, 2, 2>(m, stream);
     case 3: return launch_many_k<FMT, 3, 3>(m, stream);
     case 4: return launch_many_k<FMT, 4, 4>(m, stream);
-    // the two-per-CU tilings are never chosen for a many-launch (only
-    // mx_gemm_tiled asks for them)
+    case 5: return launch_many_k<FMT, 5, 5>(m, stream);
+    case 6: return launch_many_k<FMT, 6, 6>(m, stream);
+    case 7: return launch_many_k<FMT, 7, 7>(m, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1223,13 +1325,57 @@ int dense_tile_index(int bm, int bn, int wg_per_cu, int64_t M, int64_t N) {
 hipError_t launch_gemm_many(GemmMany m, int fmt, hipStream_t stream) {
   if (m.n < 1 || m.n > kGemmManyMax) return hipErrorInvalidValue;
   for (int i = 0; i < m.n; ++i)
-    if ((m.shape[i] = dense_shape_of(m.p[i])) < 0) return hipErrorInvalidValue;
+    if ((m.shape[i] = dense_shape_of(fmt, m.p[i])) < 0) return hipErrorInvalidValue;
   switch (fmt) {
     case kE2M1: return launch_many_fmt<kE2M1>(m, stream);
     case kE2M3: return launch_many_fmt<kE2M3>(m, stream);
     case kE4M3: return launch_many_fmt<kE4M3>(m, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GemmPlan* out) {
+  if (const Tuned* t = tuned(fmt, M, N, K)) {
+    *out = t->plan;
+    return true;
+  }
+  const int sh = dense_shape(M, N);
+  if (sh < 0) return false;
+  *out = GemmPlan{kDenseShapes[sh][0], kDenseShapes[sh][1], kDenseShapes[sh][2], 1};
+  return true;
+}
+
+hipError_t launch_splitk_reduce(const float* ws, int split_k, int64_t M, int64_t N, const void* bias, int bias_f32,
+                                void* c, int c_f32, int64_t ldc, hipStream_t stream) {
+  const int64_t threads = M * (N / 4);
+  if (threads == 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+#define MX_REDUCE(S)                                                                                         \
+  case S:                                                                                                    \
+    hipLaunchKernelGGL(splitk_reduce_kernel<S>, dim3((unsigned)blocks), dim3(256), 0, stream, ws, M, N, bias, \
+                       bias_f32, c, c_f32, ldc);                                                             \
+    break;
+  switch (split_k) {
+    MX_REDUCE(2)
+    MX_REDUCE(3)
+    MX_REDUCE(4)
+    MX_REDUCE(5)
+    MX_REDUCE(6)
+    MX_REDUCE(7)
+    MX_REDUCE(8)
+    MX_REDUCE(9)
+    MX_REDUCE(10)
+    MX_REDUCE(11)
+    MX_REDUCE(12)
+    MX_REDUCE(13)
+    MX_REDUCE(14)
+    MX_REDUCE(15)
+    MX_REDUCE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MX_REDUCE
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream) {

@@ -68,8 +68,10 @@ hipError_t launch_colsum_finish(const float* partials, int64_t nb, int64_t C, fl
                                 hipStream_t stream);
 
 enum GemmMode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
-// kEpiAccum (dense only): the store of kEpiStore, adding into the previous C
-enum Epilogue { kEpiStore = 0, kEpiSwiglu = 1, kEpiDSwiglu = 2, kEpiAccum = 3 };
+// kEpiAccum (dense only): the store of kEpiStore, adding into the previous C.
+// kEpiSplit (dense only): the K range cut into split_k parts, each stored in
+// binary32 without the bias (see GemmParams::split_k).
+enum Epilogue { kEpiStore = 0, kEpiSwiglu = 1, kEpiDSwiglu = 2, kEpiAccum = 3, kEpiSplit = 4 };
 
 struct GemmParams {
   const uint8_t* a_codes;
@@ -100,9 +102,28 @@ struct GemmParams {
   // dense: 0 lets the launch pick the output tile shape; 1 + i forces entry
   // i of the dense shape table (see dense_tile_index)
   int tile_shape;
+  // kEpiSplit: the K range cut into split_k >= 2 equal parts; part s is
+  // computed by its own workgroups into C + s * M * ldc (binary32, no bias),
+  // for launch_splitk_reduce to sum
+  int split_k;
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, int mode, int epi, hipStream_t stream);
+// c[m][n] = round(((ws_0 + ws_1) + ... + ws_{S-1}) + bias[n]) over the
+// split_k binary32 partial results ws_s = ws + s * M * N (row pitch N), in
+// that order, rounded once to bf16 (nearest even) or stored as binary32.
+hipError_t launch_splitk_reduce(const float* ws, int split_k, int64_t M, int64_t N, const void* bias, int bias_f32,
+                                void* c, int c_f32, int64_t ldc, hipStream_t stream);
+
+// A dense GEMM's launch plan: output tile, workgroups per compute unit and
+// K split.  plan_gemm gives the measured best of the tuned table for this
+// compute-unit count, format and M x N x K, else the rounds x tile-area
+// rule with no split; split_k > 1 needs a workspace of split_k * M * N
+// binary32 values.
+struct GemmPlan {
+  int tile_m, tile_n, wg_per_cu, split_k;
+};
+bool plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GemmPlan* out);
 // Index of the dense output tile shape bm x bn at wg_per_cu workgroups per
 // compute unit for an M x N output, or -1 if it is not one of the dense
 // shapes or does not divide M x N.

@@ -110,6 +110,11 @@ def lib():
         L.mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_gemm_tiled.restype = ci
         L.mx_gemm_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, ci, ci, ci, vp]
+        L.mx_gemm_splitk.restype = ci
+        L.mx_gemm_splitk.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, ci, ci, ci, ci, vp, i64,
+                                     vp]
+        L.mx_gemm_plan.restype = ci
+        L.mx_gemm_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]
         L.mx_gemm_accumulate.restype = ci
         L.mx_gemm_accumulate.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, ci, vp, ci, i64, vp]
         L.mx_fused_mlp_fwd.restype = ci
@@ -312,6 +317,46 @@ def gemm_tiled(a, b, M: int, N: int, K: int, fmt: int, c, tile, bias=None, bias_
                              int(tile[2]) if len(tile) > 2 else (0 if tuple(tile) == (0, 0) else 1),
                              _stream(stream))
     _check(st, "mx_gemm_tiled")
+
+
+def gemm_plan(M: int, N: int, K: int, fmt: int):
+    """mx_gemm_plan: ((tile_m, tile_n, wg_per_cu), split_k, workspace bytes)
+    of a dense GEMM on this device."""
+    plan = (ctypes.c_int * 4)()
+    ws = ctypes.c_int64(0)
+    _check(lib().mx_gemm_plan(M, N, K, fmt, plan, ctypes.byref(ws)), "mx_gemm_plan")
+    return (plan[0], plan[1], plan[2]), plan[3], ws.value
+
+
+def gemm_splitk(a, b, M: int, N: int, K: int, fmt: int, c, tile, split_k: int, workspace, bias=None,
+                bias_dtype: int = BF16, c_dtype: int = BF16, ldc: int | None = None, stream=None,
+                workspace_bytes: int | None = None):
+    """mx_gemm_splitk: mx_gemm with the tiling tile = (tile_m, tile_n,
+    workgroups per compute unit) and K cut into split_k parts, summed in order
+    from the caller's workspace (split_k * M * N binary32 values; None when
+    split_k is 1; workspace_bytes defaults to the tensor's size)."""
+    _need_packed(a, M, K, fmt, "gemm_splitk A")
+    _need_packed(b, N, K, fmt, "gemm_splitk B")
+    _need(c, (4 if c_dtype == F32 else 2) * M * (N if ldc is None else ldc), "gemm_splitk C")
+    _need(bias, (4 if bias_dtype == F32 else 2) * N, "gemm_splitk bias")
+    ws_bytes = workspace_bytes if workspace_bytes is not None else _nbytes(workspace)
+    st = lib().mx_gemm_splitk(_ptr(a[0]), _ptr(a[1]), _ptr(b[0]), _ptr(b[1]), M, N, K, fmt, _ptr(bias), bias_dtype,
+                              _ptr(c), c_dtype, N if ldc is None else ldc, int(tile[0]), int(tile[1]), int(tile[2]),
+                              int(split_k), _ptr(workspace), ws_bytes or 0, _stream(stream))
+    _check(st, "mx_gemm_splitk")
+
+
+def gemm_planned(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16,
+                 c_dtype: int = BF16, ldc: int | None = None, stream=None, workspace=None):
+    """The GEMM under mx_gemm_plan's plan: mx_gemm_splitk with the planned
+    tiling and split, taking the workspace it needs from `workspace` (a
+    device tensor of at least that many bytes) or, if None, a new device
+    tensor."""
+    tile, split_k, ws_bytes = gemm_plan(M, N, K, fmt)
+    if split_k > 1 and workspace is None:
+        workspace = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    gemm_splitk(a, b, M, N, K, fmt, c, tile, split_k, workspace if split_k > 1 else None, bias, bias_dtype,
+                c_dtype, ldc, stream)
 
 
 def gemm_accumulate(a, b, M: int, N: int, K: int, fmt: int, c, bias=None, bias_dtype: int = BF16,

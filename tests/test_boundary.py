@@ -278,6 +278,59 @@ def test_gemm_tiled_rejects_shapes_it_cannot_serve():
             assert st == DEVICE
 
 
+def gs(split_k, ws=P6, ws_bytes=None, tile=(0, 0, 0), M=768, N=768, K=1536):
+    nb = split_k * M * N * 4 if ws_bytes is None else ws_bytes
+    return mx.lib().mx_gemm_splitk(P, P2, P3, P4, M, N, K, mx.E2M1, None, mx.BF16, P5, mx.BF16, N, tile[0], tile[1],
+                                   tile[2], split_k, ws, nb, None)
+
+
+def test_gemm_splitk_rejects_what_it_cannot_serve():
+    ok = (OK, DEVICE)
+    assert gs(2) in ok and gs(3) in ok and gs(4) in ok and gs(12) in ok  # K = 1536 = 128 * 12
+    assert gs(1, ws=None, ws_bytes=0) in ok       # no split: no workspace
+    assert gs(0) == SHAPE and gs(17) == SHAPE     # 1 .. MX_SPLIT_K_MAX
+    assert gs(5) == SHAPE and gs(16) == SHAPE     # K not a multiple of 128 * split_k
+    assert gs(2, ws=None) == NULL                 # a split needs the workspace
+    assert gs(2, ws=P6 + 8) == ALIGN
+    assert gs(2, ws_bytes=2 * 768 * 768 * 4 - 1) == SHAPE
+    assert gs(2, tile=(128, 128, 1)) == SHAPE     # not a tile shape
+    assert gs(2, tile=(192, 256, 1), M=512) == SHAPE
+    assert gs(2, tile=(128, 256, 2)) in ok
+    if not mx.lib().mx_device_supported(0):
+        assert gs(2) == DEVICE
+
+
+def test_gemm_plan_without_a_tuned_entry_is_the_rule():
+    # a shape no tuned entry names gets mx_gemm's rule and no split: the
+    # tile with the fewest rounds x tile area on this device's compute units
+    tile, split, ws = mx.gemm_plan(4096 + 256 * 7, 2304, 2816, mx.E2M3)
+    assert split == 1 and ws == 0 and tile[2] == 1
+    assert tile in ((256, 256, 1), (256, 192, 1), (192, 256, 1), (192, 192, 1), (256, 128, 1))
+    L = mx.lib()
+    plan = (ctypes.c_int * 4)()
+    assert L.mx_gemm_plan(512, 512, 500, mx.E2M1, plan, None) == SHAPE
+    assert L.mx_gemm_plan(512, 512, 512, 9, plan, None) == FORMAT
+    assert L.mx_gemm_plan(512, 512, 512, mx.E2M1, None, None) == NULL
+    assert L.mx_gemm_plan(512, 512, 512, mx.E2M1, plan, None) == OK
+
+
+def test_tuned_table_entries_are_servable():
+    # every line of the tuned table names a tiling mx_gemm_tiled accepts and
+    # a split that divides K into 128-element groups
+    src = open(os.path.join(ROOT, "microscaling_block_scaled_mx_amd", "csrc", "mx_tuned.inc")).read()
+    rows = re.findall(r"\{(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*\{(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\}\}", src)
+    shapes = {(256, 256, 1), (256, 192, 1), (192, 256, 1), (192, 192, 1), (256, 128, 1), (256, 128, 2), (128, 256, 2),
+              (192, 192, 2)}
+    seen = set()
+    for r in rows:
+        cus, fmt, M, N, K, tm, tn, wg, split = (int(v) for v in r)
+        assert cus > 0 and fmt in (mx.E2M1, mx.E2M3, mx.E4M3)
+        assert (tm, tn, wg) in shapes and M % tm == 0 and N % tn == 0
+        assert 1 <= split <= 16 and K % (128 * split) == 0
+        assert (cus, fmt, M, N, K) not in seen
+        seen.add((cus, fmt, M, N, K))
+
+
 def test_binding_refuses_host_tensors_and_strided_views():
     # buffers of sufficient size that the kernels could not read correctly:
     # a host tensor (its address is not device memory) and a strided view

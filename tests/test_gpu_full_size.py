@@ -169,6 +169,29 @@ def test_linear_mxfp4_flux_sweep_full_size(mxl, orc, i):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_tuned_splitk_plan_at_512_tokens(mxl, orc, fmt):
+    # the adaLN dgrad at 512 tokens (M = 512, N = 3072, K = 18432): the tuned
+    # table splits K (few output tiles, long K); through mx_gemm_plan and
+    # mx_gemm_splitk as bench.py times it, sampled outputs against the oracle
+    M, N, K = 512, 3072, 18432
+    mode = mxl.RCEIL if fmt == mxl.E4M3 else mxl.FLOOR
+    had = fmt == mxl.E2M3
+    tile, split, ws_bytes = mxl.gemm_plan(M, N, K, fmt)
+    assert split > 1 and ws_bytes == split * M * N * 4
+    rng = np.random.default_rng(600 + fmt)
+    A = I.bf16_normal(rng, (M, K), 1.0)
+    B = I.bf16_normal(rng, (N, K), 0.02)
+    pa, pb = mxl.alloc_packed(M, K, fmt), mxl.alloc_packed(N, K, fmt)
+    mxl.quantize(dev(A), M, K, fmt, mode, had, row=pa)
+    mxl.quantize(dev(B), N, K, fmt, mode, had, row=pb)
+    C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    mxl.gemm_planned(pa, pb, M, N, K, fmt, C)
+    m, n = pick(rng, M), pick(rng, N)
+    ref = gemm_grid(orc, orc_rows(orc, A, m, fmt, mode, had), orc_rows(orc, B, n, fmt, mode, had), K, fmt)
+    assert_close(host(C)[np.ix_(m, n)], ref, f"split-K {split} C = A B^T")
+
+
 # ------------------------------------------------------------------ fused MXFP6 MLP, M = 8192
 def test_fused_mlp_mxfp6_flux_full_size(mxl, orc):
     from oracle import oracle as O

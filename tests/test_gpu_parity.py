@@ -285,6 +285,72 @@ def test_gemm_parity_every_tile_shape(mxl, orc, fmt, mode, had, tile):
     assert np.array_equal(c16, I.f32_to_bf16_bits(c32))
 
 
+def f32_bits_of_bf16(h):
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("fmt,mode,had", [(1, 0, False), (2, 0, True), (3, 1, False)])
+@pytest.mark.parametrize("split_k,tile", [(2, (256, 256, 1)), (3, (256, 192, 1)), (4, (192, 192, 2)),
+                                          (6, (256, 128, 1)), (12, (0, 0, 0))])
+def test_gemm_splitk_parity(mxl, orc, fmt, mode, had, split_k, tile):
+    # mx_gemm_splitk: part s is the GEMM of K slice s (against the oracle on
+    # that slice), and C is the parts summed in order, plus the bias, rounded
+    # once -- checked bit for bit from the parts the call left in the workspace
+    M, N, K = 768, 768, 1536
+    rng = np.random.default_rng(1200 + 20 * fmt + split_k)
+    A = I.bf16_normal(rng, (M, K), 1.0)
+    B = I.bf16_normal(rng, (N, K), 0.02)
+    b = I.bf16_normal(rng, (N,), 0.01)
+    pa = orc.quantize(A, M, K, fmt, mode, had)
+    pb = orc.quantize(B, N, K, fmt, mode, had)
+    ref = orc.gemm(pa["row_codes"], pa["row_scales"], pb["row_codes"], pb["row_scales"], M, N, K, fmt, bias=b)
+    bits = mxl.BITS[fmt]
+    a = (dev(tiled(pa["row_codes"], bits)), dev(blocked(pa["row_scales"])))
+    bb = (dev(tiled(pb["row_codes"], bits)), dev(blocked(pb["row_scales"])))
+    ws = torch.full((split_k * M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    c16 = bf16_empty(M, N)
+    mxl.gemm_splitk(a, bb, M, N, K, fmt, c32, tile, split_k, ws, bias=dev(b), c_dtype=mxl.F32)
+    parts = host(ws).reshape(split_k, M, N).copy()
+    got32 = host(c32).copy()
+    mxl.gemm_splitk(a, bb, M, N, K, fmt, c16, tile, split_k, ws, bias=dev(b), c_dtype=mxl.BF16)
+    mxl.gemm_splitk(a, bb, M, N, K, fmt, c32, tile, split_k, ws, bias=dev(b), c_dtype=mxl.F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c32).view(np.uint32), got32.view(np.uint32))  # repeatable to the bit
+    assert gemm_rel_err(got32, ref) <= REL
+    acc = parts[0].copy()
+    for s in range(1, split_k):
+        acc = (acc + parts[s]).astype(np.float32)
+    want32 = (acc + f32_bits_of_bf16(b)[None, :]).astype(np.float32)
+    assert np.array_equal(got32.view(np.uint32), want32.view(np.uint32))
+    assert np.array_equal(host(c16), I.f32_to_bf16_bits(want32))
+    ks = K // split_k
+    for s in range(split_k):
+        k0, k1 = s * ks, (s + 1) * ks
+        cut = lambda p: (p["row_codes"][:, k0 * bits // 8:k1 * bits // 8], p["row_scales"][:, k0 // 32:k1 // 32])
+        (ac, asc), (bc, bsc) = cut(pa), cut(pb)
+        assert gemm_rel_err(parts[s], orc.gemm(ac, asc, bc, bsc, M, N, ks, fmt)) <= REL, s
+
+
+def test_gemm_splitk_writes_only_its_output_columns(mxl, orc):
+    # a row pitch beyond N: the reduction writes columns [0, N) of each row
+    # and leaves the rest of the pitch alone
+    M, N, K, ldc = 512, 512, 1024, 512 + 136
+    rng = np.random.default_rng(77)
+    pa = orc.quantize(I.bf16_normal(rng, (M, K), 1.0), M, K, 1, 0, False)
+    pb = orc.quantize(I.bf16_normal(rng, (N, K), 0.02), N, K, 1, 0, False)
+    a = (dev(tiled(pa["row_codes"], 4)), dev(blocked(pa["row_scales"])))
+    bb = (dev(tiled(pb["row_codes"], 4)), dev(blocked(pb["row_scales"])))
+    c = torch.full((M, ldc), 0x7BCD, dtype=torch.int16, device="cuda")
+    ref16 = bf16_empty(M, N)
+    ws = torch.empty((4 * M * N,), dtype=torch.float32, device="cuda")
+    mxl.gemm_splitk(a, bb, M, N, K, 1, c, (256, 256, 1), 4, ws, ldc=ldc)
+    mxl.gemm_splitk(a, bb, M, N, K, 1, ref16, (256, 256, 1), 4, ws)
+    got = host(c)
+    assert np.array_equal(got[:, :N], host(ref16))
+    assert (got[:, N:].view(np.uint16) == 0x7BCD).all()
+
+
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_gemm_exact_products_bitwise(mxl, orc, fmt):
     # one shared scale per operand and codes whose products are multiples of
