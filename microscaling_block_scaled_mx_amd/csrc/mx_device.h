@@ -335,40 +335,51 @@ __device__ __forceinline__ void quant_store_sr(const float (&v)[32], uint8_t* g,
 
 // ------------------------------------------------------------------ prologue math
 // Own exp (binary32), the library's contract: Cody-Waite reduction
-// n = rint(x * LOG2E), r = (x - n*LN2_HI) - n*LN2_LO with LN2_HI = ln 2 cut
-// to 16 significant bits, then the degree-7 Taylor polynomial (1/k! rounded
-// to binary32) in Horner order, scaled by 2^n.  x < -87 -> +0 (results stay
-// normal), x > 89 -> +inf, NaN -> NaN.
-__device__ __forceinline__ float mx_exp(float x) {
+// n = rint(x * LOG2E), r = fma(-n, LN2_HI, x) (exact product: LN2_HI is ln 2
+// cut to 16 significant bits), r = fma(-n, LN2_LO, r), then the degree-7
+// Taylor polynomial (1/k! rounded to binary32) in Horner order, one fused
+// multiply-add per step, scaled by 2^n.  x < -87 -> +0 (results stay
+// normal), x > 89 -> +inf, NaN -> NaN.  mx_exp_core is the arithmetic
+// without the range checks.
+__device__ __forceinline__ float mx_exp_core(float x) {
   const float LOG2E = 0x1.715476p+0f;   // fl32(1/ln 2)
   const float LN2_HI = 0x1.62e4p-1f;     // 0.693145751953125
   const float LN2_LO = 0x1.7f7d1cp-20f;  // fl32(ln 2 - LN2_HI)
   const float P2 = 0x1.0p-1f, P3 = 0x1.555556p-3f, P4 = 0x1.555556p-5f;
   const float P5 = 0x1.111112p-7f, P6 = 0x1.6c16c2p-10f, P7 = 0x1.a01a02p-13f;
-  float n = __builtin_rintf(x * LOG2E);
-  float r = x - n * LN2_HI;
-  r = r - n * LN2_LO;
+  const float n = __builtin_rintf(x * LOG2E);
+  float r = __builtin_fmaf(-n, LN2_HI, x);
+  r = __builtin_fmaf(-n, LN2_LO, r);
   float p = P7;
-  p = P6 + r * p;
-  p = P5 + r * p;
-  p = P4 + r * p;
-  p = P3 + r * p;
-  p = P2 + r * p;
-  p = 1.0f + r * p;
-  p = 1.0f + r * p;
-  float res = __builtin_ldexpf(p, (int)n);
+  p = __builtin_fmaf(r, p, P6);
+  p = __builtin_fmaf(r, p, P5);
+  p = __builtin_fmaf(r, p, P4);
+  p = __builtin_fmaf(r, p, P3);
+  p = __builtin_fmaf(r, p, P2);
+  p = __builtin_fmaf(r, p, 1.0f);
+  p = __builtin_fmaf(r, p, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+__device__ __forceinline__ float mx_exp(float x) {
+  float res = mx_exp_core(x);
   res = (x > 89.0f) ? __builtin_inff() : res;
   res = (x < -87.0f) ? 0.0f : res;
   return (x != x) ? x : res;
 }
+// mx_exp for x >= 0 or NaN (x < -87 cannot occur, so its check is left out).
+__device__ __forceinline__ float mx_exp_nonneg(float x) {
+  float res = mx_exp_core(x);
+  res = (x > 89.0f) ? __builtin_inff() : res;
+  return (x != x) ? x : res;
+}
 
-// tanh-GELU pieces.  u = K0*(x + K1*((x*x)*x)); q = 2/(exp(2|u|)+1);
+// tanh-GELU pieces.  u = K0*fma(K1, (x*x)*x, x); q = 2/(exp(2|u|)+1);
 // 1 + tanh(u) = q (u < 0) or 2 - q (u >= 0); 1 - tanh(u)^2 = q*(2-q).
 // K0 = fl32(sqrt(2/pi)), K1 = fl32(0.044715).
 __device__ __forceinline__ float gelu_u(float x) {
   const float K0 = 0x1.988454p-1f, K1 = 0x1.6e4e26p-5f;
   float x3 = (x * x) * x;
-  float inner = x + K1 * x3;
+  float inner = __builtin_fmaf(K1, x3, x);
   return K0 * inner;
 }
 // n / d for n = 1 or 2 and d >= 1, rounded to nearest even: the hardware
@@ -392,7 +403,7 @@ __device__ __forceinline__ float div_small(float n, float d) {
 }
 
 __device__ __forceinline__ float gelu_q(float u) {
-  float e = mx_exp(2.0f * __builtin_fabsf(u));
+  float e = mx_exp_nonneg(2.0f * __builtin_fabsf(u));
   return div_small(2.0f, e + 1.0f);
 }
 
@@ -404,7 +415,7 @@ __device__ __forceinline__ float gelu_bf16(float x) {
   return round_bf16((0.5f * x) * opt);
 }
 
-// dh = bf16(da * (0.5*(1+tanh u) + (0.5*x) * ((q*(2-q)) * (K0*(1 + (3*K1)*(x*x))))))
+// dh = bf16(da * (0.5*(1+tanh u) + (0.5*x) * ((q*(2-q)) * (K0*fma(3*K1, x*x, 1)))))
 // with the second term taken as 0 when q*(2-q) == 0.
 __device__ __forceinline__ float dgelu_bf16(float da, float x) {
   const float K0 = 0x1.988454p-1f, K1x3 = 0x1.12ba9cp-3f;  // fl32(3 * fl32(0.044715))
@@ -413,7 +424,7 @@ __device__ __forceinline__ float dgelu_bf16(float da, float x) {
   float opt = (u < 0.0f) ? q : (2.0f - q);
   float w = q * (2.0f - q);
   float first = 0.5f * opt;
-  float second = (0.5f * x) * (w * (K0 * (1.0f + K1x3 * (x * x))));
+  float second = (0.5f * x) * (w * (K0 * __builtin_fmaf(K1x3, x * x, 1.0f)));
   second = (w == 0.0f) ? 0.0f : second;
   return round_bf16(da * (first + second));
 }

@@ -180,7 +180,8 @@ unsigned orc_scale_rceil(float amax) {
 /* implementation; to make both sides bit-identical, exp is our own:      */
 /* Cody-Waite range reduction with a two-part ln2 and a degree-7 Taylor  */
 /* polynomial (coefficients 1/k!, rounded to binary32), Horner order.     */
-/* Every step is one binary32 operation.                                  */
+/* Every step is one binary32 operation: a product, a sum, or a fused     */
+/* multiply-add (one rounding of a*b + c, C99 fmaf), as named below.      */
 /* ------------------------------------------------------------------ */
 
 /* Constants of the exp contract, each derived here from its definition:
@@ -199,11 +200,14 @@ static float c_ln2_lo(void) {
 }
 
 /* exp(x) in binary32:
- *   x NaN -> NaN; x > 88.5 -> checked below; results below 2^-126 flush to +0
- *   (x < -87.0 gives 0; the activations only ever need exp of large negative
+ *   x NaN -> NaN; x > 89 -> +inf; x < -87 -> +0 (the results in between
+ *   stay normal; the activations only ever need exp of large negative
  *   arguments inside 1/(1+exp(.)), where 0 and a subnormal give the same).
- *   n = rint(x * LOG2E); r = (x - n*LN2_HI) - n*LN2_LO;
- *   p = 1 + r*(1 + r*(1/2 + r*(1/6 + r*(1/24 + r*(1/120 + r*(1/720 + r/5040))))));
+ *   n = rint(x * LOG2E);
+ *   r = fma(-n, LN2_HI, x)  (n*LN2_HI is exact, so this is x - n*LN2_HI);
+ *   r = fma(-n, LN2_LO, r);
+ *   p = 1/5040; then p = fma(r, p, c) for c = 1/720, 1/120, 1/24, 1/6, 1/2,
+ *   1, 1 in turn (Horner order, one rounding per step);
  *   result = p * 2^n (exact power-of-two scaling), +inf when it overflows. */
 float orc_exp(float x) {
   if (isnan(x)) return x;
@@ -214,16 +218,16 @@ float orc_exp(float x) {
   const float k5 = (float)(1.0 / 120.0), k6 = (float)(1.0 / 720.0), k7 = (float)(1.0 / 5040.0);
   float t = x * L2E;
   float n = rintf(t);
-  float r = x - n * LH;
-  r = r - n * LL;
+  float r = fmaf(-n, LH, x);
+  r = fmaf(-n, LL, r);
   float p = k7;
-  p = k6 + r * p;
-  p = k5 + r * p;
-  p = k4 + r * p;
-  p = k3 + r * p;
-  p = k2 + r * p;
-  p = 1.0f + r * p;
-  p = 1.0f + r * p;
+  p = fmaf(r, p, k6);
+  p = fmaf(r, p, k5);
+  p = fmaf(r, p, k4);
+  p = fmaf(r, p, k3);
+  p = fmaf(r, p, k2);
+  p = fmaf(r, p, 1.0f);
+  p = fmaf(r, p, 1.0f);
   double res = ldexp((double)p, (int)n); /* exact: p has 24 bits */
   if (res > 3.4028234663852886e38) return INFINITY;
   return (float)res;
@@ -249,11 +253,11 @@ float orc_one_plus_tanh(float u) {
 static float c_k0(void) { return (float)sqrt(2.0 / 3.14159265358979323846264338327950288); }
 static float c_k1(void) { return (float)0.044715; }
 
-/* u = K0 * (x + K1*((x*x)*x)) */
+/* u = K0 * fma(K1, (x*x)*x, x) */
 static float gelu_u(float x) {
   const float K0 = c_k0(), K1 = c_k1();
   float x3 = (x * x) * x;
-  float inner = x + K1 * x3;
+  float inner = fmaf(K1, x3, x);
   return K0 * inner;
 }
 
@@ -265,7 +269,7 @@ uint16_t orc_gelu_bf16(uint16_t hb) {
 }
 
 /* Derivative of the tanh-GELU above, times the incoming gradient:
- *   dg = 0.5*(1+tanh u) + (0.5*x) * ((q*(2-q)) * (K0 * (1 + (3*K1)*(x*x))))
+ *   dg = 0.5*(1+tanh u) + (0.5*x) * ((q*(2-q)) * (K0 * fma(3*K1, x*x, 1)))
  *   dh = bf16(da * dg)
  * When q*(2-q) is exactly 0 the second term is taken as 0 (it avoids 0*inf
  * for huge |x|). */
@@ -280,7 +284,7 @@ uint16_t orc_dgelu_bf16(uint16_t dab, uint16_t hb) {
   float first = 0.5f * opt;
   float second;
   if (w == 0.0f) second = 0.0f;
-  else second = (0.5f * x) * (w * (K0 * (1.0f + K1x3 * (x * x))));
+  else second = (0.5f * x) * (w * (K0 * fmaf(K1x3, x * x, 1.0f)));
   float dg = first + second;
   return orc_f32_to_bf16(da * dg);
 }
