@@ -184,7 +184,13 @@ __device__ __forceinline__ uint32_t quant_block(const float (&v)[32], uint32_t (
       a[i] = x[2 * i];
       b[i] = x[2 * i + 1];
     }
-    const i6v q = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, sc);
+    // The conversion's 6-dword result must not share registers with its
+    // 32 source dwords or its scale: with the result placed two registers
+    // below the sources (an allocation the compiler can choose), most codes
+    // of the block came out wrong on gfx950.  The early-clobber output
+    // keeps the result apart from every input.
+    i6v q;
+    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(q) : "v"(a), "v"(b), "v"(sc));
 #pragma unroll
     for (int d = 0; d < 6; ++d) w[d] = (uint32_t)q[d];
   }
