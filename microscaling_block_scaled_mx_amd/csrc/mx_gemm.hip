@@ -231,6 +231,15 @@ __device__ __forceinline__ void lds_dma4_s(const void* base, uint32_t off, uint3
 #endif
 }
 
+// A pointer the compiler must take as produced here: it stays in scalar
+// registers (or is spilled) instead of being loaded again where it is used.
+template <typename T>
+__device__ __forceinline__ void held_in_sgprs(T*& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+s"(v));
+#endif
+}
+
 // Materialize a kernel argument in scalar registers at this point.  The
 // epilogue's arguments are pinned before the main loop: a scalar load still
 // in flight there shares the LDS wait counter, and the compiler then turns
@@ -441,7 +450,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   // address arithmetic is left in the main loop.
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale slots of a wavefront are one operand's");
   const uint8_t* s_base[CF::kSJ];
-  int64_t s_step[CF::kSJ];  // bytes between consecutive K groups
+  uint32_t s_step[CF::kSJ];  // bytes between consecutive K groups
   uint32_t s_off[CF::kSJ];
 #pragma unroll
   for (int j = 0; j < CF::kSJ; ++j) {
@@ -451,8 +460,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
     const int64_t ar = MODE == kRaggedM && m0 + (r < BM ? r : 0) >= m_end ? m_end - 1 : m0 + (r < BM ? r : 0);
     s_base[j] = is_b ? p.b_scales + b_soff : p.a_scales;
     s_off[j] = (uint32_t)(is_b ? (b_row(r - BM) - b_row0) * 4 : ar * 4);
-    s_step[j] = (is_b ? b_rows : a_rows) * 4;
+    s_step[j] = (uint32_t)((is_b ? b_rows : a_rows) * 4);
   }
+  // bytes between consecutive K groups of the A / B codes; every offset
+  // into an operand fits 32 bits (operands < 2 GiB), so a stage's base is
+  // one 32-bit product and one 64-bit add
+  const uint32_t a_gb = (uint32_t)(a_rows * kGB), b_gb = (uint32_t)(b_rows * kGB);
+  // the operand bases, held in scalar registers for the whole loop: taken
+  // through an empty asm, the compiler cannot re-derive them by loading the
+  // kernel argument again (a scalar load in the loop shares the LDS wait
+  // counter, and its wait would also wait for every LDS read in flight)
+  const uint8_t* a_codes = p.a_codes;
+  const uint8_t* b_codes = p.b_codes;
+  held_in_sgprs(a_codes);
+  held_in_sgprs(b_codes);
   const int wave_u = wave_uniform(wave);
   const uint32_t smem_lds = wave_uniform((int)lds_addr(smem));  // LDS byte address of smem
 
@@ -462,22 +483,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
   // load instruction.
 #define MX_PIECE(k, buf, q)                                                                               \
   do {                                                                                                   \
-    const int64_t k0_ = kbeg + (int64_t)(k) * BK;                                                        \
+    const uint32_t k0_ = (uint32_t)kbeg + (uint32_t)(k) * BK;                                            \
+    const uint32_t g_ = k0_ >> 7, w_ = (k0_ & 127) * kBits / 8;                                          \
     const uint32_t st_ = smem_lds;                                                                       \
     if ((q) < CF::kAIters) {                                                                             \
       const int i_ = (q) < CF::kAIters ? (q) : 0;                                                        \
       const bool junk_ = CF::kARem && i_ == CF::kAIters - 1 && wave_u * 64 >= CF::kARem;                 \
-      lds_dma16_s(p.a_codes + (k0_ / 128) * a_rows * kGB + (k0_ % 128) * kBits / 8, a_off[i_],          \
+      lds_dma16_s(a_codes + (g_ * a_gb + w_), a_off[i_],                                                \
                   st_ + (junk_ ? CF::kJOff : CF::aoff(buf) + (i_ * kThreads + wave_u * 64) * 16));            \
     } else if ((q) < CF::kAIters + CF::kBIters) {                                                        \
       const int i_ = (q) >= CF::kAIters && (q) < CF::kAIters + CF::kBIters ? (q) - CF::kAIters : 0;      \
       const bool junk_ = CF::kBRem && i_ == CF::kBIters - 1 && wave_u * 64 >= CF::kBRem;                 \
-      lds_dma16_s(p.b_codes + (k0_ / 128) * b_rows * kGB + (k0_ % 128) * kBits / 8, b_off[i_],          \
+      lds_dma16_s(b_codes + (g_ * b_gb + w_), b_off[i_],                                                \
                   st_ + (junk_ ? CF::kJOff : CF::boff(buf) + (i_ * kThreads + wave_u * 64) * 16));            \
     } else {                                                                                             \
       const int e_ = (q) >= CF::kAIters + CF::kBIters ? (q) - CF::kAIters - CF::kBIters : 0;             \
       const int d_ = e_ / CF::kSJ, j_ = e_ % CF::kSJ;                                                    \
-      lds_dma4_s(s_base[j_] + (k0_ / 128 + d_) * s_step[j_], s_off[j_],                                 \
+      lds_dma4_s(s_base[j_] + (g_ + d_) * s_step[j_], s_off[j_],                                        \
                st_ + CF::soff(buf) + (d_ * 512 + j_ * kThreads + wave_u * 64) * 4);                     \
     }                                                                                                    \
   } while (0)
