@@ -445,6 +445,37 @@ def test_gemm_many_linear_trio_matches_gemm(mxl):
         assert torch.equal(c1, c2)
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_gemm_many_equal_tile_trio_matches_gemm_and_oracle(mxl, orc, fmt):
+    # three GEMMs of one output shape and different K in one launch (equal
+    # tile counts, a multiple of 8, like a linear step's trio at square
+    # shapes): every output equals the separate mx_gemm result bit for bit,
+    # and the last matches the oracle
+    rng = np.random.default_rng(700 + fmt)
+    M, N = 1024, 512
+    items, refs, ops = [], [], []
+    for K in (256, 768, 512):
+        A, B = I.bf16_normal(rng, (M, K)), I.bf16_normal(rng, (N, K), 0.05)
+        pa, pb = mxl.alloc_packed(M, K, fmt), mxl.alloc_packed(N, K, fmt)
+        mode = 1 if fmt == 3 else 0
+        mxl.quantize(dev(A), M, K, fmt, mode, False, row=pa)
+        mxl.quantize(dev(B), N, K, fmt, mode, False, row=pb)
+        C1 = torch.full((M, N), 0x5A5A, dtype=torch.int16, device="cuda")
+        C2 = torch.full((M, N), 0x5A5A, dtype=torch.int16, device="cuda")
+        items.append(dict(a=pa, b=pb, M=M, N=N, K=K, c=C1))
+        mxl.gemm(pa, pb, M, N, K, fmt, C2)
+        refs.append(C2)
+        ops.append((A, B, K, mode))
+    mxl.gemm_many(items, fmt)
+    for it, C2 in zip(items, refs):
+        assert torch.equal(it["c"], C2), it["K"]
+    A, B, K, mode = ops[2]
+    qa = orc.quantize(A, M, K, fmt, mode, False, row=True)
+    qb = orc.quantize(B, N, K, fmt, mode, False, row=True)
+    want = orc.gemm(qa["row_codes"], qa["row_scales"], qb["row_codes"], qb["row_scales"], M, N, K, fmt)
+    assert bf16_close(host(items[2]["c"]), want)
+
+
 def test_gemm_determinism(mxl, orc):
     rng = np.random.default_rng(3)
     M, N, K = 512, 512, 1024
