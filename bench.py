@@ -405,7 +405,7 @@ def cpu_baseline_per_config():
 
 
 # ------------------------------------------------------------------ other workloads
-def bench_cfg1(mx, T, iters=20):
+def bench_linear256(mx, T, iters=20):
     """The 256^3 MXFP4 case: packs of A and B (one launch) and the GEMM with an
     fp32 C.  Device time per step from graph replays (a latency-bound case:
     one 256x256 tile, reported in microseconds)."""
@@ -431,8 +431,8 @@ def bench_cfg1(mx, T, iters=20):
             "gemm_us": graph_time(gemm, replays=8)}
 
 
-def bench_cfg3(mx, T, iters=5):
-    """Fused MXFP6 MLP (config 3): forward + backward per step, timed as
+def bench_fused_mlp(mx, T, iters=5):
+    """Fused MXFP6 MLP (M = 8192, 3072 -> 12288 -> 3072): forward + backward per step, timed as
     replays of a HIP graph of two steps over two copies of the inputs (X,
     W1, b1, W2, dY: 250 MB per copy, so a step does not find its inputs in
     the 256 MB Infinity Cache), after warm-up steps."""
@@ -473,7 +473,7 @@ def bench_cfg3(mx, T, iters=5):
             "tflops": fl / (per_step * 1e-6) / 1e12, "frac_of_fp6_peak": fl / (per_step * 1e-6) / 1e12 / PEAK_TFLOPS["fp6"]}
 
 
-def bench_cfg4(mx, T, iters=3):
+def bench_flux_sweep(mx, T, iters=3):
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     out = {"workload": "MXFP4 Flux-12B block linears at M=16384, fwd+dgrad+wgrad", "linears": {}}
@@ -527,23 +527,23 @@ def grouped_step(mx, t, R, D, F, G, fmt, mode, T=None, side=None):
     import torch
     run = (lambda name, fn, *a, **kw: T.run(name, fn, *a, **kw)) if T is not None else \
         (lambda name, fn, *a, **kw: fn(*a, **kw))
-    pack_w1 = lambda: run("c5_pack", mx.quantize, t["W1"], 2 * F, D, fmt, mode, row=t["W1r"], col=t["W1c"], batch=G)
-    pack_w2 = lambda: run("c5_pack", mx.quantize, t["W2"], D, F, fmt, mode, row=t["W2r"], col=t["W2c"], batch=G)
-    pack_x = lambda: run("c5_pack", mx.quantize, t["X"], R, D, fmt, mode, row=t["Xr"], col=t["Xc"])
-    pack_dy = lambda: run("c5_pack", mx.quantize, t["dY"], R, D, fmt, mode, row=t["dYr"], col=t["dYc"])
-    fc1 = lambda: run("c5_fc1_swiglu", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["Xr"], t["W1r"], t["H"],
+    pack_w1 = lambda: run("pack", mx.quantize, t["W1"], 2 * F, D, fmt, mode, row=t["W1r"], col=t["W1c"], batch=G)
+    pack_w2 = lambda: run("pack", mx.quantize, t["W2"], D, F, fmt, mode, row=t["W2r"], col=t["W2c"], batch=G)
+    pack_x = lambda: run("pack", mx.quantize, t["X"], R, D, fmt, mode, row=t["Xr"], col=t["Xc"])
+    pack_dy = lambda: run("pack", mx.quantize, t["dY"], R, D, fmt, mode, row=t["dYr"], col=t["dYc"])
+    fc1 = lambda: run("fc1_swiglu", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["Xr"], t["W1r"], t["H"],
                       epilogue=mx.EPI_SWIGLU, N=2 * F, K=D, out_row=t["zr"], out_col=t["zc"], fmt=fmt,
                       scale_mode=mode)
-    fc2 = lambda: run("c5_fc2", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["zr"], t["W2r"], t["Y"], N=D, K=F,
+    fc2 = lambda: run("fc2", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["zr"], t["W2r"], t["Y"], N=D, K=F,
                       fmt=fmt, scale_mode=mode)
-    fc2_dgrad = lambda: run("c5_fc2_dgrad_dswiglu", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["dYr"],
+    fc2_dgrad = lambda: run("fc2_dgrad_dswiglu", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["dYr"],
                             t["W2c"], None, epilogue=mx.EPI_DSWIGLU, N=F, K=D, aux=t["H"], out_row=t["dHr"],
                             out_col=t["dHc"], fmt=fmt, scale_mode=mode)
-    fc1_dgrad = lambda: run("c5_fc1_dgrad", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["dHr"], t["W1c"],
+    fc1_dgrad = lambda: run("fc1_dgrad", mx.grouped_gemm, mx.RAGGED_M, G, R, t["off"], t["dHr"], t["W1c"],
                             t["dX"], N=D, K=2 * F, fmt=fmt, scale_mode=mode)
-    wgrad2 = lambda: run("c5_wgrad2", mx.grouped_gemm, mx.RAGGED_K, G, R, t["off"], t["dYc"], t["zc"], t["dW2"],
+    wgrad2 = lambda: run("wgrad2", mx.grouped_gemm, mx.RAGGED_K, G, R, t["off"], t["dYc"], t["zc"], t["dW2"],
                          M=D, N=F, fmt=fmt, scale_mode=mode)
-    wgrad1 = lambda: run("c5_wgrad1", mx.grouped_gemm, mx.RAGGED_K, G, R, t["off"], t["dHc"], t["Xc"], t["dW1"],
+    wgrad1 = lambda: run("wgrad1", mx.grouped_gemm, mx.RAGGED_K, G, R, t["off"], t["dHc"], t["Xc"], t["dW1"],
                          M=2 * F, N=D, fmt=fmt, scale_mode=mode)
     if side is None:
         for f in (pack_x, pack_w1, pack_w2, fc1, fc2, pack_dy, fc2_dgrad, fc1_dgrad, wgrad2, wgrad1):
@@ -576,7 +576,7 @@ def grouped_step(mx, t, R, D, F, G, fmt, mode, T=None, side=None):
     main.wait_stream(side)
 
 
-def bench_cfg5(mx, T, iters=5):
+def bench_grouped_mlp(mx, T, iters=5):
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
     R, D, F, G = 32768, 2048, 768, 8
@@ -588,7 +588,7 @@ def bench_cfg5(mx, T, iters=5):
     k = T.summary()
     sec = time_steps(lambda i: grouped_step(mx, t, R, D, F, G, fmt, mode, side=side), iters, 2, Timer())
     fl = 2.0 * R * D * F * (2 + 1 + 1 + 2 + 1 + 2)
-    gemm_us = sum(v for n, v in k.items() if n != "c5_pack")
+    gemm_us = sum(v for n, v in k.items() if n != "pack")
     out = {"workload": "MXFP8 grouped SwiGLU MLP G=8 D=2048 F=768 R=32768 (one empty expert), fwd+bwd",
            "counts": [int(c) for c in counts], "ms_per_step": sec * 1e3, "step_tflops": fl / sec / 1e12,
            "schedule": "two streams: weight / dY packs and the ragged-K weight gradients beside the main chain",
@@ -806,7 +806,7 @@ def only(mx, spec, steps, warmup, T):
     its average time."""
     import torch
     from microscaling_block_scaled_mx_amd import inputs as I
-    workloads = {"linear256": bench_cfg1, "mlp": bench_cfg3, "sweep": bench_cfg4, "grouped": bench_cfg5,
+    workloads = {"linear256": bench_linear256, "mlp": bench_fused_mlp, "sweep": bench_flux_sweep, "grouped": bench_grouped_mlp,
                  "main_grad": bench_main_grad, "sr_pack": bench_sr_pack, "tuned": bench_tuned_plans}
     if spec in workloads:  # one of the other workloads, as in the full run
         print(json.dumps({"only": spec, **workloads[spec](mx, T)}), flush=True)
@@ -994,8 +994,8 @@ def main():
             line["cpu_baseline"]["per_workload"] = cpu_baseline_per_config()
     if args.extra == "all":
         extra = {}
-        for name, fn in (("mxfp4_256", bench_cfg1), ("fused_mlp_mxfp6", bench_cfg3), ("mxfp4_flux_sweep", bench_cfg4),
-                         ("grouped_mxfp8", bench_cfg5), ("wgrad_main_grad", bench_main_grad),
+        for name, fn in (("mxfp4_256", bench_linear256), ("fused_mlp_mxfp6", bench_fused_mlp), ("mxfp4_flux_sweep", bench_flux_sweep),
+                         ("grouped_mxfp8", bench_grouped_mlp), ("wgrad_main_grad", bench_main_grad),
                          ("mxfp4_sr_pack", bench_sr_pack), ("tuned_splitk_512_tokens", bench_tuned_plans)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = fn(mx, T)
