@@ -27,7 +27,7 @@ import torch
 
 from microscaling_block_scaled_mx_amd import inputs as I
 from packed_layout import unblocked, untiled
-from parity_checks import REL, bf16_close, bf16_rel_err
+from parity_checks import bf16_close, bf16_rel_err
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:

@@ -14,7 +14,7 @@ import torch
 
 from microscaling_block_scaled_mx_amd import inputs as I
 from packed_layout import blocked, blocked_shape, tiled, tiled_shape, unblocked, untiled
-from parity_checks import REL, assert_packs_equal, bf16_close, bf16_rel_err, gemm_rel_err
+from parity_checks import REL, assert_packs_equal, bf16_close, gemm_rel_err
 
 pytestmark = pytest.mark.gpu
 
