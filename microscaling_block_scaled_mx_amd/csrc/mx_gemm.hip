@@ -847,9 +847,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
             }
         }
       };
-      if constexpr (accumulate) {
-        stage_bf16(std::true_type{});
-      } else {
+      // without a bias the sums are rounded as they are (one uniform branch)
+      auto stage_sums = [&](auto with_bias) __attribute__((always_inline)) {
+        constexpr bool kBias = decltype(with_bias)::value;
 #pragma unroll
         for (int i = 0; i < CF::kMI; ++i)
 #pragma unroll
@@ -858,10 +858,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bx, int by, i
             for (int e4 = 0; e4 < 4; ++e4) {
               const int r = 32 * i + lrow, cl = 32 * j + 8 * e4 + 4 * g;
               const v16f& a = acc[i][j];
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = kBias ? a[4 * e4 + q] + bv[j][4 * e4 + q] : a[4 * e4 + q];
               *reinterpret_cast<uint2*>(wt + r * CF::kCPitch + cl * 2) =
-                  make_uint2(pack_bf16x2(a[4 * e4 + 0] + bv[j][4 * e4 + 0], a[4 * e4 + 1] + bv[j][4 * e4 + 1]),
-                             pack_bf16x2(a[4 * e4 + 2] + bv[j][4 * e4 + 2], a[4 * e4 + 3] + bv[j][4 * e4 + 3]));
+                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
+      };
+      if constexpr (accumulate) {
+        stage_bf16(std::true_type{});
+      } else if (p.bias != nullptr) {
+        stage_sums(std::true_type{});
+      } else {
+        stage_sums(std::false_type{});
       }
       __syncthreads();
       uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + c_off;
