@@ -45,7 +45,7 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6,
                 "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h", "mx_tuned.inc"),
-                "sources_sha1": "5320a1d303bfca9270e1031d8ad1a3f0b28630bc"}
+                "sources_sha1": "22cd5f73c797a42cb8f00ca2bdd56cd65d8aa017"}
 # VALU wavefront-instructions per launch of the fused pack (rocprofv3
 # SQ_INSTS_VALU), valid while the pack sources are those it was counted with
 PACK_VALU = {"instructions_per_launch": 1.028e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),

@@ -375,9 +375,11 @@ int mx_gemm_splitk(const void* a_codes, const void* a_scales, const void* b_code
  * weight-gradient GEMMs, which are independent once the operands are packed
  * ([P1] description): one launch lets the compute units that finish one
  * GEMM's tiles start the next GEMM's instead of idling until every tile of
- * the launch is done.  Items whose tile shapes are all one shape, or are
- * 256x192 and 192x192, share one launch; other mixes take one launch per
- * shape.
+ * the launch is done.  Items of one tile shape share a launch, and so do
+ * items of two shapes that run the same number of wavefronts at the same
+ * residency (256x192, 192x256, 192x192 and 256x128 at one workgroup per
+ * compute unit, pairwise; 256x128 with 128x256 or 192x192 at two); other
+ * shapes take launches of their own.
  *
  *  items        host array of n items; each item's fields have the meaning
  *               and rules of the mx_gemm arguments of the same names.  No

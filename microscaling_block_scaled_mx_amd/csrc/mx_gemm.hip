@@ -1318,27 +1318,55 @@ hipError_t launch_many_single(const GemmMany& m, int sh, hipStream_t stream) {
   }
 }
 
-// One launch when every GEMM takes the same tile shape, or the shapes are
-// 256 x 192 and 192 x 192 (a linear layer's forward / data-gradient and
-// weight-gradient GEMMs at the Flux shapes); otherwise one launch per shape.
+// Two tile shapes can share a launch when they run the same number of
+// wavefronts at the same residency: the 4-wavefront shapes at one workgroup
+// per CU (256x192, 192x256, 192x192, 256x128) pairwise, and those at two
+// (256x128, 128x256, 192x192) pairwise except 128x256 with 192x192 (their
+// union spills at half the register file).  256x256 runs 8 wavefronts
+// alone.
+constexpr bool pairable(int a, int b) {
+  return a != b && a != 0 && b != 0 && kDenseShapes[a][2] == kDenseShapes[b][2] && !(a == 6 && b == 7) &&
+         !(a == 7 && b == 6);
+}
+template <int FMT>
+hipError_t launch_many_pair(const GemmMany& m, int a, int b, hipStream_t stream) {
+  switch (a * kNumDense + b) {  // a < b
+    case 1 * kNumDense + 2: return launch_many_k<FMT, 1, 2>(m, stream);
+    case 1 * kNumDense + 3: return launch_many_k<FMT, 1, 3>(m, stream);
+    case 1 * kNumDense + 4: return launch_many_k<FMT, 1, 4>(m, stream);
+    case 2 * kNumDense + 3: return launch_many_k<FMT, 2, 3>(m, stream);
+    case 2 * kNumDense + 4: return launch_many_k<FMT, 2, 4>(m, stream);
+    case 3 * kNumDense + 4: return launch_many_k<FMT, 3, 4>(m, stream);
+    case 5 * kNumDense + 6: return launch_many_k<FMT, 5, 6>(m, stream);
+    case 5 * kNumDense + 7: return launch_many_k<FMT, 5, 7>(m, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The GEMMs grouped into launches: the shapes in use taken in table order,
+// each with the first later shape it can share a launch with (a linear
+// layer's forward / data-gradient 256x192 and weight-gradient 192x192 at
+// the Flux shapes are one such pair); items keep their order in a launch.
 template <int FMT>
 hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
   bool used[kNumDense] = {};
   for (int i = 0; i < all.n; ++i) used[all.shape[i]] = true;
-  int nused = 0;
-  for (int k = 0; k < kNumDense; ++k) nused += used[k];
-  if (nused == 2 && used[1] && used[3]) return launch_many_k<FMT, 1, 3>(all, stream);
-  for (int k = 0; k < kNumDense; ++k) {
-    if (!used[k]) continue;
+  for (int a = 0; a < kNumDense; ++a) {
+    if (!used[a]) continue;
+    used[a] = false;
+    int b = -1;
+    for (int k = a + 1; k < kNumDense && b < 0; ++k)
+      if (used[k] && pairable(a, k)) b = k;
+    if (b >= 0) used[b] = false;
     GemmMany m;
     memset(&m, 0, sizeof m);
     for (int i = 0; i < all.n; ++i)
-      if (all.shape[i] == k) {
+      if (all.shape[i] == a || all.shape[i] == b) {
         m.p[m.n] = all.p[i];
-        m.shape[m.n] = k;
+        m.shape[m.n] = all.shape[i];
         ++m.n;
       }
-    const hipError_t e = launch_many_single<FMT>(m, k, stream);
+    const hipError_t e = b >= 0 ? launch_many_pair<FMT>(m, a, b, stream) : launch_many_single<FMT>(m, a, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -445,6 +445,26 @@ def test_gemm_many_linear_trio_matches_gemm(mxl):
         assert torch.equal(c1, c2)
 
 
+def test_gemm_many_shape_pairs_match_gemm(mxl):
+    # GEMMs with 4096x3072 and 3072x4096 outputs (tiles 256x192 and 192x256,
+    # which share one launch) and a 3072x3072 one (its own tiling, in a
+    # launch of its own): each output equals mx_gemm's bit for bit
+    fmt, K = 2, 512
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    rnd = lambda *s: torch.randint(0, 256, s, dtype=torch.uint8, device="cuda", generator=gen)
+    sc = lambda *s: torch.randint(118, 130, s, dtype=torch.uint8, device="cuda", generator=gen)
+    P = lambda r, k: (rnd(*mxl.alloc_packed(r, k, fmt)[0].shape), sc(*mxl.alloc_packed(r, k, fmt)[1].shape))
+    shapes = [(4096, 3072), (3072, 4096), (3072, 3072)]
+    ops = [(P(m, K), P(n, K), m, n) for m, n in shapes]
+    outs = [torch.full((m, n), 0x5A5A, dtype=torch.int16, device="cuda") for m, n in shapes]
+    refs = [torch.full((m, n), 0x5A5A, dtype=torch.int16, device="cuda") for m, n in shapes]
+    mxl.gemm_many([dict(a=a, b=b, M=m, N=n, K=K, c=c) for (a, b, m, n), c in zip(ops, outs)], fmt)
+    for (a, b, m, n), c in zip(ops, refs):
+        mxl.gemm(a, b, m, n, K, fmt, c)
+    for c1, c2 in zip(outs, refs):
+        assert torch.equal(c1, c2)
+
+
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_gemm_many_equal_tile_trio_matches_gemm_and_oracle(mxl, orc, fmt):
     # three GEMMs of one output shape and different K in one launch (equal
