@@ -1126,21 +1126,6 @@ hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 // Dense tile shape (index into kDenseShapes): the one whose rounds of one
 // tile per compute unit cost the least output area (rounds x BM x BN),
 // larger tiles first on ties -- e.g. 4096 x 3072 takes 256 tiles of
@@ -1373,6 +1358,20 @@ hipError_t launch_many_fmt(const GemmMany& all, hipStream_t stream) {
 }
 
 }  // namespace
+
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 int dense_tile_index(int bm, int bn, int wg_per_cu, int64_t M, int64_t N) {
   for (int i = 0; i < kNumDense; ++i)

@@ -47,6 +47,7 @@ struct PackParams {
   uint8_t* col_scales;  // blocked layout, rows C, K = R
   float* partials;      // [R/32][C] or nullptr
   uint64_t sr_seed;     // stochastic-rounding kernels only: Philox key
+  int64_t batch;        // batch entries (set by launch_pack)
 };
 
 // Up to kPackManyMax tensors packed in one launch: item i owns workgroups
@@ -57,6 +58,9 @@ struct PackMany {
   int64_t first[kPackManyMax + 1];
   int n;
 };
+
+// Compute units of the current device (cached per device).
+int cu_count();
 
 bool pack_supported(int fmt, int mode, int had, int pro);
 hipError_t launch_pack(const PackParams& p, int fmt, int mode, int had, int pro, int64_t batch,

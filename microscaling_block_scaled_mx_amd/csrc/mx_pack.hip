@@ -143,6 +143,62 @@ __device__ __forceinline__ Chunk8 apply_prologue(const PackParams& p, const Raw<
   }
 }
 
+// ------------------------------------------------------------------ GELU table
+// The GELU prologue's result is a function of one bf16 code, so a
+// workgroup evaluates gelu_bf16 once per code of a window of magnitudes,
+// [2^-16, 32) (exponent fields kLo .. kLo + kFields - 1), into an LDS table
+// and looks the codes up: slot = (code & 0x7fff) - kA0 + (code >> 15) *
+// kSlots.  Slot kN of each sign is a sentinel for codes outside the
+// window (smaller, larger, infinite, NaN); a chunk holding one is
+// recomputed from its inputs with gelu_bf16 after the lookups.  The other
+// prologues keep their in-register arithmetic: their results also depend on
+// the other inputs, and looking up only the one-code factor did not pay.
+struct GeluTable {
+  static constexpr uint32_t kLo = 111, kFields = 21;
+  static constexpr uint32_t kA0 = kLo << 7, kN = kFields << 7, kSlots = kN + 1;
+  static constexpr int kEntries = 2 * kSlots;
+  static constexpr int kBytes = (kEntries * 2 + 15) & ~15;
+  // workgroups per compute unit that the LDS allows (the kernel's launch
+  // bounds hold its registers to that)
+  static constexpr int kPerCU = (160 * 1024) / (kTileBytes + kBytes);
+};
+template <int PRO>
+constexpr int kTableBytes = PRO == kGelu ? GeluTable::kBytes : 0;
+
+// Fill the table (all 256 threads).
+__device__ __forceinline__ void build_gelu_table(uint16_t* tab) {
+  for (int i = threadIdx.x; i < GeluTable::kEntries; i += 256) {
+    const uint32_t sgn = i >= (int)GeluTable::kSlots ? 1u : 0u;
+    const uint32_t off = (uint32_t)i - sgn * GeluTable::kSlots;
+    // the sentinel takes any code: its value is never used
+    const uint32_t code = (sgn << 15) | (GeluTable::kA0 + (off < GeluTable::kN ? off : 0u));
+    tab[i] = (uint16_t)(__float_as_uint(gelu_bf16(bf16_to_f32(code))) >> 16);
+  }
+}
+
+// Slot of bf16 code `code` (low 16 bits); `out` gains 1 if it lies outside
+// the window.
+__device__ __forceinline__ uint32_t gelu_slot(uint32_t code, uint32_t& out) {
+  uint32_t off = (code & 0x7fffu) - GeluTable::kA0;  // below the window wraps past kN
+  off = off < GeluTable::kN ? off : GeluTable::kN;
+  out |= (off == GeluTable::kN) ? 1u : 0u;
+  return off + (code >> 15) * GeluTable::kSlots;
+}
+
+// GELU of one chunk by lookups; `out` gains 1 if a code lies outside the
+// window.
+__device__ __forceinline__ Chunk8 gelu_lookup(const uint4 in, const uint16_t* tab, uint32_t& out) {
+  const Chunk8 x = as_chunk(in);
+  Chunk8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = tab[gelu_slot(x.w[i] & 0xffffu, out)];
+    const uint32_t hi = tab[gelu_slot(x.w[i] >> 16, out)];
+    r.w[i] = lo | (hi << 16);
+  }
+  return r;
+}
+
 // One workgroup packs one 128 x 128 tile (column tile bx, row tile by) of
 // batch entry z.
 template <int FMT, int MODE, int HAD, int PRO, int SR = 0>
@@ -166,6 +222,10 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
   // block of row row_t + 16 i is i / 2 (row_t < 16)
   const int lds_t = row_t * kPitch + ch_t * 16;
   constexpr auto lds_step = [](int i) { return i * 16 * kPitch + (i >> 1) * kBlockSkew; };
+  // GELU: the prologue by lookups in the table at tile + kTileBytes; bit i
+  // of redo is set if chunk i holds a code outside the table window
+  [[maybe_unused]] const uint16_t* gtab = reinterpret_cast<const uint16_t*>(tile + kTileBytes);
+  [[maybe_unused]] uint32_t redo = 0;
   if (r0 + kTileR <= p.R && c0 + kTileC <= p.C) {
     // whole tile inside the tensor (uniform branch): one address per input,
     // stepped by 16 row pitches per load, and no masks
@@ -177,7 +237,14 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const Chunk8 v = apply_prologue<PRO>(p, raw[i], c_t);
+      Chunk8 v;
+      if constexpr (PRO == kGelu) {
+        uint32_t out = 0;
+        v = gelu_lookup(raw[i].in[0], gtab, out);
+        redo |= out << i;
+      } else {
+        v = apply_prologue<PRO>(p, raw[i], c_t);
+      }
       *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
     }
   } else {
@@ -191,11 +258,33 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
       const int64_t r = r0 + row_t + 16 * i;
       Chunk8 v;
       if (r < p.R && c_t < p.C) {
-        v = apply_prologue<PRO>(p, raw[i], c_t);
+        if constexpr (PRO == kGelu) {
+          uint32_t out = 0;
+          v = gelu_lookup(raw[i].in[0], gtab, out);
+          redo |= out << i;
+        } else {
+          v = apply_prologue<PRO>(p, raw[i], c_t);
+        }
       } else {
         v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u;
       }
       *reinterpret_cast<uint4*>(tile + lds_t + lds_step(i)) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+    }
+  }
+  if constexpr (PRO == kGelu) {
+    // chunks with codes outside the window: every element again from its
+    // input (rare for activations of ordinary magnitude)
+    if (redo != 0) {
+      const uint16_t* x = xb + (r0 + row_t) * p.C + c_t;
+#pragma unroll 1
+      for (int i = 0; i < kLoads; ++i) {
+        if ((redo >> i) & 1u) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(tile + lds_t + lds_step(i));
+#pragma unroll 1
+          for (int e = 0; e < 8; ++e)
+            dst[e] = (uint16_t)(__float_as_uint(gelu_bf16(bf16_to_f32(x[16 * i * p.C + e]))) >> 16);
+        }
+      }
     }
   }
   __syncthreads();
@@ -275,26 +364,71 @@ __device__ __forceinline__ void pack_tile(const PackParams& p, int64_t bx, int64
   }
 }
 
-template <int FMT, int MODE, int HAD, int PRO, int SR = 0>
-__global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
-  pack_tile<FMT, MODE, HAD, PRO, SR>(p, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+// GELU: each workgroup fills the table once, then packs tiles w,
+// w + gridDim.x, ... (the launch gives it as many workgroups as fit at
+// once); `at` maps a tile index to its (params, bx, by, z).
+template <int FMT, int MODE, int HAD, class TileAt>
+__device__ __forceinline__ void pack_gelu_tiles(uint32_t tiles, uint8_t* tile, const TileAt& at) {
+  build_gelu_table(reinterpret_cast<uint16_t*>(tile + kTileBytes));
+  __syncthreads();
+  for (uint32_t w = blockIdx.x; w < tiles; w += gridDim.x) {
+    at(w, [&](const PackParams& p, uint32_t bx, uint32_t by, uint32_t z) {
+      pack_tile<FMT, MODE, HAD, kGelu>(p, bx, by, z, tile);
+    });
+    __syncthreads();  // the next tile's writes wait for this tile's column pass
+  }
 }
 
-// Several tensors in one launch: workgroup w packs tile w - first[i] of
-// item i, with first[i] <= w < first[i + 1]; an item's tiles are ordered
+// Tile w of a tensor of tx column tiles and ty row tiles per batch entry:
 // column tile fastest, then row tile, then batch entry.
+template <class F>
+__device__ __forceinline__ void tile_of(const PackParams& p, uint32_t w, F&& f) {
+  const uint32_t tx = (uint32_t)((p.C + kTileC - 1) / kTileC), ty = (uint32_t)((p.R + kTileR - 1) / kTileR);
+  const uint32_t row_tile = w / tx;
+  f(p, w - row_tile * tx, row_tile % ty, row_tile / ty);
+}
+
+template <int FMT, int MODE, int HAD, int PRO, int SR = 0>
+__global__ __launch_bounds__(256, PRO == kGelu ? GeluTable::kPerCU : 1) void pack_kernel(PackParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes + kTableBytes<PRO>];
+  if constexpr (PRO == kGelu) {
+    const uint32_t tiles = (uint32_t)(((p.C + kTileC - 1) / kTileC) * ((p.R + kTileR - 1) / kTileR) * p.batch);
+    pack_gelu_tiles<FMT, MODE, HAD>(tiles, tile, [&](uint32_t w, auto&& f) { tile_of(p, w, f); });
+  } else {
+    pack_tile<FMT, MODE, HAD, PRO, SR>(p, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+  }
+}
+
+// Several tensors in one launch: tile w of the launch is tile w - first[i]
+// of item i, with first[i] <= w < first[i + 1]; an item's tiles are ordered
+// column tile fastest, then row tile, then batch entry.  Workgroup w packs
+// tile w (GELU: tiles w, w + gridDim.x, ...).
 template <int FMT, int MODE, int HAD, int PRO>
-__global__ __launch_bounds__(256) void pack_many_kernel(PackMany m) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
-  const int64_t w = blockIdx.x;
-  int i = 0;
-  while (i + 1 < m.n && w >= m.first[i + 1]) ++i;
-  // tile counts of one launch fit 32 bits (the grid is one-dimensional)
-  const uint32_t local = (uint32_t)(w - m.first[i]);
-  const uint32_t tx = (uint32_t)((m.p[i].C + kTileC - 1) / kTileC), ty = (uint32_t)((m.p[i].R + kTileR - 1) / kTileR);
-  const uint32_t row_tile = local / tx;
-  pack_tile<FMT, MODE, HAD, PRO>(m.p[i], local - row_tile * tx, row_tile % ty, row_tile / ty, tile);
+__global__ __launch_bounds__(256, PRO == kGelu ? GeluTable::kPerCU : 1) void pack_many_kernel(PackMany m) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes + kTableBytes<PRO>];
+  if constexpr (PRO == kGelu) {
+    pack_gelu_tiles<FMT, MODE, HAD>((uint32_t)m.first[m.n], tile, [&](uint32_t w, auto&& f) {
+      int i = 0;
+      while (i + 1 < m.n && w >= m.first[i + 1]) ++i;
+      tile_of(m.p[i], (uint32_t)(w - m.first[i]), f);
+    });
+  } else {
+    const int64_t w = blockIdx.x;
+    int i = 0;
+    while (i + 1 < m.n && w >= m.first[i + 1]) ++i;
+    // tile counts of one launch fit 32 bits (the grid is one-dimensional)
+    const uint32_t local = (uint32_t)(w - m.first[i]);
+    const uint32_t tx = (uint32_t)((m.p[i].C + kTileC - 1) / kTileC), ty = (uint32_t)((m.p[i].R + kTileR - 1) / kTileR);
+    const uint32_t row_tile = local / tx;
+    pack_tile<FMT, MODE, HAD, PRO>(m.p[i], local - row_tile * tx, row_tile % ty, row_tile / ty, tile);
+  }
+}
+
+// Workgroups of a GELU launch: as many as fit on the compute units at once,
+// at most one per tile.
+int64_t gelu_grid(int64_t tiles) {
+  const int64_t slots = (int64_t)GeluTable::kPerCU * cu_count();
+  return tiles < slots ? tiles : slots;
 }
 
 // db[c] = sum over blocks b (increasing) of partials[b][c], from +0.  One
@@ -378,7 +512,13 @@ hipError_t launch_pack(const PackParams& p, int fmt, int mode, int had, int pro,
   PackFn fn = pick<PackKernels>(fmt, mode, had, pro);
   if (!fn) return hipErrorInvalidValue;
   dim3 grid((unsigned)((p.C + kTileC - 1) / kTileC), (unsigned)((p.R + kTileR - 1) / kTileR), (unsigned)batch);
-  hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, p);
+  if (pro == kGelu) {
+    PackParams q = p;
+    q.batch = batch;
+    hipLaunchKernelGGL(fn, dim3((unsigned)gelu_grid((int64_t)grid.x * grid.y * grid.z)), dim3(256), 0, stream, q);
+  } else {
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -387,7 +527,7 @@ hipError_t launch_pack_many(const PackMany& m, int fmt, int mode, int had, int p
   if (!fn || m.n < 1 || m.n > kPackManyMax) return hipErrorInvalidValue;
   const int64_t tiles = m.first[m.n];
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(256), 0, stream, m);
+  hipLaunchKernelGGL(fn, dim3((unsigned)(pro == kGelu ? gelu_grid(tiles) : tiles)), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 

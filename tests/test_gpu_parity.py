@@ -141,6 +141,43 @@ def test_quantize_whole_and_ragged_tiles(mxl, orc, fmt, mode, had, pro):
     assert_f32_bitwise(got["colsum"], want["colsum"])
 
 
+@pytest.mark.parametrize("pro", [1, 2, 3, 4])
+def test_prologue_pack_several_tiles_per_workgroup(mxl, orc, pro):
+    # 2 x 9 x 48 = 864 tiles (a ragged last row tile in each batch entry),
+    # batched.  GELU launches fewer workgroups than tiles: each builds its
+    # lookup table once and loops over tiles.  Inputs outside the table's
+    # window (tiny, huge, infinite, NaN) are scattered over the tensor, so
+    # the chunks recomputed without the table fall in many tiles; the other
+    # prologues see the same inputs.
+    rng = np.random.default_rng(1700 + pro)
+    B, R, C = 2, 1056, 6144
+
+    def act(shape):
+        v = I.bf16_normal(rng, shape, 2.0)
+        n = v.size // 500
+        idx = rng.integers(0, v.size, n)
+        pool = np.array([0x3380, 0xB400, 0x0001, 0x8000, 0x4300, 0xC2F0, 0x4780, 0x7F80, 0xFF80, 0x7FC0],
+                        dtype=np.uint16)  # 6e-8, -1.2e-7, subnormal, -0, 128, -120, 65536, +-Inf, NaN
+        v.reshape(-1)[idx] = pool[rng.integers(0, len(pool), n)]
+        return v
+
+    if pro == 3:    # x = H [R][2C]
+        x, aux = act((B, R, 2 * C)), None
+    elif pro == 4:  # x = dz [R][C/2], aux = H [R][C]
+        x, aux = I.bf16_normal(rng, (B, R, C // 2), 1.0), act((B, R, C))
+    elif pro == 2:  # x = da, aux = h
+        x, aux = I.bf16_normal(rng, (B, R, C), 1.0), act((B, R, C))
+    else:
+        x, aux = act((B, R, C)), None
+    got = gpu_quantize(mxl, x, aux, R, C, 2, 0, True, pro, colsum=True, batch=B)
+    for b in range(B):
+        want = orc.quantize(x[b], R, C, 2, 0, True, pro=pro, aux=None if aux is None else aux[b], row=True,
+                            col=True, colsum=True)
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+            assert np.array_equal(got[k][b], want[k]), (b, k)
+        assert_f32_bitwise(got["colsum_partials"][b], want["colsum_partials"])
+
+
 @pytest.mark.parametrize("fmt,mode", [(3, 1), (1, 0), (2, 0)])
 def test_quantize_parity_swiglu_dswiglu(mxl, orc, fmt, mode):
     rng = np.random.default_rng(7 + fmt)
