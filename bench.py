@@ -45,18 +45,18 @@ METRIC = "MX GEMM TFLOP/s and % of MXFP4/6/8 MFMA peak (Flux-12B shapes); quanti
 # sources are those the counters were taken with
 GEMM_TRAFFIC = {"bytes_per_launch": 236.8e6,
                 "sources": ("mx_gemm.hip", "mx_device.h", "mx_kernels.h", "mx_tuned.inc"),
-                "sources_sha1": "22cd5f73c797a42cb8f00ca2bdd56cd65d8aa017"}
+                "sources_sha1": "53ce50b65db16e6a151cb803a2fc01e9948211ee"}
 # VALU wavefront-instructions per launch of the fused pack (rocprofv3
 # SQ_INSTS_VALU), valid while the pack sources are those it was counted with
 PACK_VALU = {"instructions_per_launch": 1.028e7, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-             "sources_sha1": "76b0548cc761a9cedc3bfe6739a992ca3b7557b0"}
+             "sources_sha1": "2945333d2cfbd4699be5771f3ec74b31d38e2639"}
 # peak VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, two wave64 instructions per
 # four cycles on each SIMD (gfx950 issues two VALU instructions of different
 # wavefronts together), i.e. the chip's 157.3 TFLOP/s of fp32 vector FMA
 # counted in wave64 instructions (G wavefront-instructions per second)
 VALU_PEAK_GIPS = 256 * 4 * 2.4 * 2 / 4
 PACK_TRAFFIC = {"bytes_per_launch": 123.5e6, "sources": ("mx_pack.hip", "mx_device.h", "mx_kernels.h"),
-                "sources_sha1": "76b0548cc761a9cedc3bfe6739a992ca3b7557b0"}
+                "sources_sha1": "2945333d2cfbd4699be5771f3ec74b31d38e2639"}
 
 
 def measured_traffic(rec):
