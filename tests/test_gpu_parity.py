@@ -664,6 +664,34 @@ def test_grouped_parity_small(mxl, orc, fmt, mode):
     assert bf16_close(dW2, bwd["dW2_64"])
 
 
+@pytest.mark.parametrize("fmt,mode", [(3, 1), (2, 0)])
+def test_grouped_epilogue_sigmoid_slow_path(mxl, orc, fmt, mode):
+    # gate values of +-2048 (rows of 8.0 against a gate column of ones):
+    # exp(2048) overflows, so 1 + exp(-g) is infinite and the SwiGLU and
+    # dSwiGLU epilogues recompute those chunks with the exact division; the
+    # whole chain must still match the oracle
+    R, D, F, G = 512, 256, 256, 4
+    counts, offsets, X, W1, W2, dY = I.grouped_mlp(503, R, D, F, G)  # expert 3 empty
+    one, eight = np.uint16(0x3F80), np.uint16(0x4100)
+    X[5, :], X[7, :] = eight, eight | np.uint16(0x8000)
+    X[300, :] = eight | np.uint16(0x8000)
+    W1[:, 3, :] = one
+    t = run_grouped(mxl, offsets, X, W1, W2, dY, R, D, F, G, fmt=fmt, mode=mode)
+    BITS = mxl.BITS[fmt]
+    H = host(t["H"])
+    assert np.any(H[:, 3] == 0xC500) and np.any(H[:, 3] == 0x4500)  # gates of -2048 and +2048 reached
+    fwd = orc.grouped_fwd_ref(X, W1, W2, offsets, R, D, F, H_in=H, fmt=fmt, mode=mode)
+    assert np.array_equal(untiled(host(t["zr"][0]), F, BITS), fwd["z"]["row_codes"])
+    assert np.array_equal(unblocked(host(t["zr"][1]), F // 32), fwd["z"]["row_scales"])
+    assert np.array_equal(untiled(host(t["zc"][0]), R, BITS), fwd["z"]["col_codes"])
+    dz = host(t["dz"])
+    bwd = orc.grouped_bwd_ref(dY, fwd, offsets, R, D, F, dz_in=dz, H_in=H)
+    assert np.array_equal(untiled(host(t["dHr"][0]), 2 * F, BITS), bwd["dH"]["row_codes"])
+    assert np.array_equal(unblocked(host(t["dHr"][1]), (2 * F) // 32), bwd["dH"]["row_scales"])
+    assert np.array_equal(untiled(host(t["dHc"][0]), R, BITS), bwd["dH"]["col_codes"])
+    assert np.array_equal(unblocked(host(t["dHc"][1]), R // 32), bwd["dH"]["col_scales"])
+
+
 def test_grouped_inactive_tail_untouched(mxl, orc):
     # offsets[-1] < R: rows past the last group end are neither read nor written
     R, D, F, G = 1024, 256, 128, 2
