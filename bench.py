@@ -467,10 +467,21 @@ def bench_fused_mlp(mx, T, iters=5):
     fwd_us = graph_time(fwd, reps=2, replays=iters)
     bwd_us = graph_time(bwd, reps=2, replays=iters)
     fl = 6 * 2.0 * M * D * F
+    # the step's floor: its six GEMMs at the MXFP6 peak plus its packs'
+    # algorithmic bytes at HBM speed (dual packs of X, W1, W2, dY; the GELU
+    # pack of a from h; the dGELU pack of dh from da and h with its 32-row
+    # partials; the column-sum finish reading the partials)
+    dual = 2 + 2 * PACK_OUT[6]
+    pack_bytes = (dual * (M * D + F * D + D * F + M * D) + dual * M * F + (dual + 2 + 0.125) * M * F
+                  + 0.125 * M * F)
+    floor_us = fl / (PEAK_TFLOPS["fp6"] * 1e6) + pack_bytes / (HBM_GBS * 1e3)
     return {"workload": "fused MXFP6 MLP M=8192 3072->12288->3072 tanh-GELU fwd+bwd (+db1)",
             "launch": "hip_graph (2 steps over 2 input copies per replay)",
             "ms_per_step": per_step / 1e3, "fwd_ms": fwd_us / 1e3, "bwd_ms": bwd_us / 1e3,
-            "tflops": fl / (per_step * 1e-6) / 1e12, "frac_of_fp6_peak": fl / (per_step * 1e-6) / 1e12 / PEAK_TFLOPS["fp6"]}
+            "tflops": fl / (per_step * 1e-6) / 1e12, "frac_of_fp6_peak": fl / (per_step * 1e-6) / 1e12 / PEAK_TFLOPS["fp6"],
+            "floor_ms": {"gemms_at_peak": fl / (PEAK_TFLOPS["fp6"] * 1e6) / 1e3,
+                         "packs_at_hbm": pack_bytes / (HBM_GBS * 1e3) / 1e3, "total": floor_us / 1e3},
+            "frac_of_floor": floor_us / per_step}
 
 
 def bench_flux_sweep(mx, T, iters=3):
@@ -595,6 +606,14 @@ def bench_grouped_mlp(mx, T, iters=5):
            "ms_per_step_one_stream": sec_serial * 1e3,
            "gemm_tflops": fl / (gemm_us * 1e-6) / 1e12, "kernels_us": k}
     out["frac_of_fp8_peak"] = out["gemm_tflops"] / PEAK_TFLOPS["fp8"]
+    # the step's floor: its GEMMs at the MXFP8 peak plus the standalone dual
+    # packs' algorithmic bytes (X, W1, W2, dY) at HBM speed (the epilogues'
+    # bytes move inside the GEMM launches)
+    pack_bytes = (2 + 2 * PACK_OUT[8]) * (R * D + G * 2 * F * D + G * D * F + R * D)
+    floor_us = fl / (PEAK_TFLOPS["fp8"] * 1e6) + pack_bytes / (HBM_GBS * 1e3)
+    out["floor_ms"] = {"gemms_at_peak": fl / (PEAK_TFLOPS["fp8"] * 1e6) / 1e3,
+                       "packs_at_hbm": pack_bytes / (HBM_GBS * 1e3) / 1e3, "total": floor_us / 1e3}
+    out["frac_of_floor"] = floor_us / (sec * 1e6)
     return out
 
 
