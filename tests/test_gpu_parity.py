@@ -241,6 +241,42 @@ def test_quantize_many_matches_quantize_and_oracle(mxl, orc, fmt, mode, had, pro
     assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
 
 
+def test_quantize_many_gelu_workgroups_loop_across_items(mxl, orc):
+    # a GELU launch of 512 + 2 x 216 = 944 tiles over three items: more
+    # tiles than the launch has workgroups, so workgroups walk tiles of
+    # different items (and batch entries) with one table each; every byte
+    # equals the separate calls', and the ragged batched item matches the
+    # oracle
+    rng = np.random.default_rng(1800)
+    items = [(2048, 4096, 1), (1056, 3072, 2)]
+    xs = [I.bf16_normal(rng, (R, C), 2.0) if b == 1 else I.bf16_normal(rng, (b, R, C), 2.0) for R, C, b in items]
+    xs[1][1, 1000, 64:72] = np.array([0x3380, 0x7F80, 0xFF80, 0x7FC0, 0x4780, 0xC2F0, 0x0001, 0x8000], np.uint16)
+    bits = mxl.BITS[2]
+
+    def bufs(R, C, b):
+        bb = None if b == 1 else b
+        return [torch.full(tiled_shape(R, C, bits, bb), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(blocked_shape(R, C, bb), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(tiled_shape(C, R, bits, bb), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.full(blocked_shape(C, R, bb), 0xA5, dtype=torch.uint8, device="cuda")]
+
+    many = [bufs(*it) for it in items]
+    one = [bufs(*it) for it in items]
+    xd = [dev(x) for x in xs]
+    mxl.quantize_many([dict(x=xd[i], R=R, C=C, batch=b, row=(many[i][0], many[i][1]), col=(many[i][2], many[i][3]))
+                       for i, (R, C, b) in enumerate(items)], 2, 0, True, 1)
+    for i, (R, C, b) in enumerate(items):
+        mxl.quantize(xd[i], R, C, 2, 0, True, 1, row=(one[i][0], one[i][1]), col=(one[i][2], one[i][3]), batch=b)
+    for i in range(len(items)):
+        for k in range(4):
+            assert torch.equal(many[i][k], one[i][k]), (items[i], k)
+    R, C, _ = items[1]
+    want = orc.quantize(xs[1][1], R, C, 2, 0, True, pro=1, row=True, col=True)
+    got = {"row_codes": untiled(host(many[1][0])[1], C, bits), "row_scales": unblocked(host(many[1][1])[1], C // 32),
+           "col_codes": untiled(host(many[1][2])[1], R, bits), "col_scales": unblocked(host(many[1][3])[1], R // 32)}
+    assert_packs_equal(got, want, ["row_codes", "row_scales", "col_codes", "col_scales"])
+
+
 def test_binding_refuses_strided_device_views(mxl):
     # a transposed or column-sliced view has the wrong row pitch for the
     # kernels' dense row-major reads and writes: refused before the call
